@@ -1,0 +1,219 @@
+"""Python binding of libdlfusion, the fused Conv/MatMul -> BatchNorm -> activation
+operator for MI355X (gfx950).
+
+This module only marshals arguments to the C ABI declared in
+``include/dlfusion.h`` (same function names).  Every step of the operator runs
+in the library's HIP kernels or its host fold; there is no Python or CPU
+fallback: importing fails loudly when ``libdlfusion.so`` has not been built.
+
+Device buffers are passed as contiguous torch tensors (their ``data_ptr()``)
+or as raw integer addresses; host buffers of the fold functions are numpy
+arrays.  ``stream=None`` means torch's current stream on the current device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdlfusion.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---------------------------------------------------------------------------
+# Enums and descriptors (mirror include/dlfusion.h)
+# ---------------------------------------------------------------------------
+DLF_OK, DLF_ERR_INVALID_ARG, DLF_ERR_UNSUPPORTED, DLF_ERR_HIP, DLF_ERR_ALIAS = 0, -1, -2, -3, -4
+DLF_F32, DLF_BF16, DLF_FP8_E4M3 = 0, 1, 2
+DLF_ACT_NONE, DLF_ACT_RELU, DLF_ACT_GELU_TANH = 0, 1, 2
+
+DTYPES = {"f32": DLF_F32, "bf16": DLF_BF16, "fp8": DLF_FP8_E4M3}
+ACTS = {"none": DLF_ACT_NONE, "relu": DLF_ACT_RELU, "gelu_tanh": DLF_ACT_GELU_TANH}
+
+
+class dlf_conv_desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("h", ctypes.c_int64), ("w", ctypes.c_int64),
+                ("c_in", ctypes.c_int64), ("c_out", ctypes.c_int64), ("kh", ctypes.c_int64),
+                ("kw", ctypes.c_int64), ("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32),
+                ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32), ("dtype", ctypes.c_int),
+                ("act", ctypes.c_int)]
+
+
+class dlf_gemm_desc(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("act", ctypes.c_int),
+                ("out_inv_scale", ctypes.c_float)]
+
+
+def conv_desc(n, h, w, c_in, c_out, kh=3, kw=3, stride=1, pad=1, dtype="bf16", act="relu"):
+    return dlf_conv_desc(n, h, w, c_in, c_out, kh, kw, stride, stride, pad, pad,
+                         DTYPES.get(dtype, dtype), ACTS.get(act, act))
+
+
+def gemm_desc(m, n, k, in_dtype="bf16", out_dtype="bf16", act="none", out_inv_scale=1.0):
+    return dlf_gemm_desc(m, n, k, DTYPES.get(in_dtype, in_dtype), DTYPES.get(out_dtype, out_dtype),
+                         ACTS.get(act, act), out_inv_scale)
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32p = ctypes.POINTER(ctypes.c_float)
+_SIGS = {
+    "dlf_fold_bn": [_i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_int, _vp, _vp],
+    "dlf_bn_scale_shift": [_i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_double, _vp, _vp],
+    "dlf_conv_fused": [ctypes.POINTER(dlf_conv_desc), _vp, _vp, _vp, _vp, _vp, _vp],
+    "dlf_gemm_fused": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "dlf_conv_plain": [ctypes.POINTER(dlf_conv_desc), _vp, _vp, _vp, _vp, _vp],
+    "dlf_gemm_plain": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, ctypes.c_float, _vp, _vp],
+    "dlf_bn_apply": [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp],
+    "dlf_scale_shift_apply": [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp],
+    "dlf_add": [_i64, ctypes.c_int, _vp, _vp, _vp, _vp],
+    "dlf_act_apply": [_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp],
+    "dlf_quant_apply": [_i64, _vp, ctypes.c_float, _vp, _vp],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = ctypes.c_int
+    _fn.argtypes = _args
+_lib.dlf_status_string.restype = ctypes.c_char_p
+_lib.dlf_status_string.argtypes = [ctypes.c_int]
+_lib.dlf_last_error.restype = ctypes.c_char_p
+_lib.dlf_last_error.argtypes = []
+
+
+class DlfError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        self.detail = dlf_last_error()
+        super().__init__(f"{func}: {dlf_status_string(status)}: {self.detail}")
+
+
+def dlf_status_string(status: int) -> str:
+    return _lib.dlf_status_string(int(status)).decode()
+
+
+def dlf_last_error() -> str:
+    return _lib.dlf_last_error().decode()
+
+
+def _check(status: int, func: str):
+    if status != DLF_OK:
+        raise DlfError(status, func)
+
+
+def _dev(t):
+    """Device pointer of a contiguous torch tensor, a raw int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _host(a, dtype=None):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(a, dtype=dtype) if dtype is not None else np.ascontiguousarray(a)
+    return arr, arr.ctypes.data
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Host-side fold
+# ---------------------------------------------------------------------------
+def dlf_fold_bn(w, conv_bias, gamma, beta, mean, var, eps, w_out_dtype="bf16"):
+    """Fold BN into conv weights (host, binary64, one RNE rounding).  w is fp32
+    [cout, ...] (OHWI); returns (w_out [same shape] as float32 or uint16 bf16 bits,
+    bias_out float32 [cout])."""
+    w_arr, w_p = _host(w, np.float32)
+    cout = w_arr.shape[0] if w_arr.ndim else 0
+    k = w_arr.size // cout if cout else 0
+    dt = DTYPES.get(w_out_dtype, w_out_dtype)
+    out = np.empty(w_arr.shape, dtype=np.float32 if dt == DLF_F32 else np.uint16)
+    bias_out = np.empty(cout, dtype=np.float32)
+    keep = [_host(v, np.float32) for v in (conv_bias, gamma, beta, mean, var)]
+    st = _lib.dlf_fold_bn(cout, k, w_p, *[p for _, p in keep], float(eps), dt, out.ctypes.data,
+                          bias_out.ctypes.data)
+    _check(st, "dlf_fold_bn")
+    return out, bias_out
+
+
+def dlf_bn_scale_shift(conv_bias, gamma, beta, mean, var, eps, pre_scale=1.0):
+    """Per-channel (alpha, beta') with BN(acc * pre_scale + b) = acc * alpha + beta' (host)."""
+    g, _ = _host(gamma, np.float32)
+    cout = g.size
+    scale = np.empty(cout, dtype=np.float32)
+    shift = np.empty(cout, dtype=np.float32)
+    keep = [_host(v, np.float32) for v in (conv_bias, gamma, beta, mean, var)]
+    st = _lib.dlf_bn_scale_shift(cout, *[p for _, p in keep], float(eps), float(pre_scale),
+                                 scale.ctypes.data, shift.ctypes.data)
+    _check(st, "dlf_bn_scale_shift")
+    return scale, shift
+
+
+# ---------------------------------------------------------------------------
+# Device entry points (asynchronous on `stream`)
+# ---------------------------------------------------------------------------
+def dlf_conv_fused(desc, x, w, bias, residual, y, stream=None):
+    _check(_lib.dlf_conv_fused(ctypes.byref(desc), _dev(x), _dev(w), _dev(bias), _dev(residual), _dev(y),
+                               _stream(stream)), "dlf_conv_fused")
+
+
+def dlf_gemm_fused(desc, a, b, col_scale, col_shift, residual, c, stream=None):
+    _check(_lib.dlf_gemm_fused(ctypes.byref(desc), _dev(a), _dev(b), _dev(col_scale), _dev(col_shift),
+                               _dev(residual), _dev(c), _stream(stream)), "dlf_gemm_fused")
+
+
+def dlf_conv_plain(desc, x, w, conv_bias, y, stream=None):
+    _check(_lib.dlf_conv_plain(ctypes.byref(desc), _dev(x), _dev(w), _dev(conv_bias), _dev(y), _stream(stream)),
+           "dlf_conv_plain")
+
+
+def dlf_gemm_plain(desc, a, b, dequant, y, stream=None):
+    _check(_lib.dlf_gemm_plain(ctypes.byref(desc), _dev(a), _dev(b), float(dequant), _dev(y), _stream(stream)),
+           "dlf_gemm_plain")
+
+
+def dlf_bn_apply(rows, c, dt, y, gamma, beta, mean, var, eps, z, stream=None):
+    _check(_lib.dlf_bn_apply(rows, c, DTYPES.get(dt, dt), _dev(y), _dev(gamma), _dev(beta), _dev(mean), _dev(var),
+                             float(eps), _dev(z), _stream(stream)), "dlf_bn_apply")
+
+
+def dlf_scale_shift_apply(rows, c, dt, y, scale, shift, z, stream=None):
+    _check(_lib.dlf_scale_shift_apply(rows, c, DTYPES.get(dt, dt), _dev(y), _dev(scale), _dev(shift), _dev(z),
+                                      _stream(stream)), "dlf_scale_shift_apply")
+
+
+def dlf_add(count, dt, a, b, out, stream=None):
+    _check(_lib.dlf_add(count, DTYPES.get(dt, dt), _dev(a), _dev(b), _dev(out), _stream(stream)), "dlf_add")
+
+
+def dlf_act_apply(count, dt, act, x, out, stream=None):
+    _check(_lib.dlf_act_apply(count, DTYPES.get(dt, dt), ACTS.get(act, act), _dev(x), _dev(out),
+                              _stream(stream)), "dlf_act_apply")
+
+
+def dlf_quant_apply(count, x, inv_scale, codes, stream=None):
+    _check(_lib.dlf_quant_apply(count, _dev(x), float(inv_scale), _dev(codes), _stream(stream)),
+           "dlf_quant_apply")
+
+
+def raw():
+    """The ctypes library handle (for status-code tests that bypass the raising wrappers)."""
+    return _lib

@@ -1,0 +1,75 @@
+// Device-side building blocks shared by the HIP kernels of libdlfusion:
+// vector types for the gfx950 MFMA builtins, bf16 conversion, the epilogue
+// activations and the e4m3 output quantiser.
+//
+// Epilogue order and activation numbering follow the conv epilogue of
+// "OpenPPL算子融合深度解析" §4.3 (bias, then residual, then activation
+// 0 none / 1 ReLU / 2 GELU-tanh, applied to the accumulator before the one
+// store); the quantiser is the static-scale FP8 store of
+// "FlashRT 跨层融合深度解析" §3 with the clamp a quantised ReLU needs
+// ("OpenPPL算子融合深度解析" §6.4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlf {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+enum : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
+enum : int { kOutBf16 = 0, kOutFp8 = 1, kOutF32 = 2 };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// GELU, tanh form: 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+__device__ __forceinline__ float gelu_tanh(float v) {
+    const float k0 = 0.797884560802865355879892f;   // sqrt(2/pi)
+    const float inner = k0 * (v + 0.044715f * v * v * v);
+    return 0.5f * v * (1.0f + tanhf(inner));
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v) {
+    if constexpr (ACT == kActRelu) {
+        return v > 0.0f ? v : 0.0f;
+    } else if constexpr (ACT == kActGelu) {
+        return gelu_tanh(v);
+    } else {
+        return v;
+    }
+}
+
+// Static e4m3 quantisation: code = Q(fp32(v * inv_scale)).  The product is one
+// IEEE fp32 multiply (never contracted into a neighbouring add), clamped to the
+// largest finite e4m3 magnitude 448, then converted by the hardware's OCP e4m3
+// conversion (round to nearest even).
+__device__ __forceinline__ uint32_t quant_e4m3(float v, float inv_scale) {
+    float p = __fmul_rn(v, inv_scale);
+    p = fminf(fmaxf(p, -448.0f), 448.0f);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false)) & 0xFFu;
+}
+
+// Four codes packed little-endian into one 32-bit word.
+__device__ __forceinline__ uint32_t quant_e4m3_x4(float a, float b, float c, float d, float inv_scale) {
+    float pa = fminf(fmaxf(__fmul_rn(a, inv_scale), -448.0f), 448.0f);
+    float pb = fminf(fmaxf(__fmul_rn(b, inv_scale), -448.0f), 448.0f);
+    float pc = fminf(fmaxf(__fmul_rn(c, inv_scale), -448.0f), 448.0f);
+    float pd = fminf(fmaxf(__fmul_rn(d, inv_scale), -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(pa, pb, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(pc, pd, w, true);
+    return static_cast<uint32_t>(w);
+}
+
+}  // namespace dlf

@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Nothing here is exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlf {
+
+// Arguments of the MFMA GEMM / implicit-GEMM kernel.  C[m][n] = sum_k A[m][k] B[n][k]
+// followed by the register epilogue.  For a convolution, A is gathered on the fly
+// from the NHWC input (row m = (img, ho, wo), k = (r*KW + s)*Cin + ci).
+struct MmaArgs {
+    const void* a;          // dense: A [M][K]; conv: x [N][H][W][Cin]
+    const void* b;          // B [N][K] (OHWI-flattened weights)
+    const float* scale;     // [N] per-column multiplier or nullptr (= 1)
+    const float* shift;     // [N] per-column bias / shift or nullptr (= 0)
+    const uint16_t* res;    // bf16 residual [M][N] or nullptr
+    void* c;                // output [M][N]
+    int64_t M;
+    int N, K;
+    float out_inv_scale;    // fp8 output: fp32(1/s_y)
+    float dequant;          // fp32 output of the plain fp8 GEMM: s_x * s_w
+    // convolution geometry (A gather); unused by the dense kernel
+    int H, W, Cin, Ho, Wo, KW, SH, SW, PH, PW;
+};
+
+// Output tile shapes of the MFMA kernel (rows x columns of C per workgroup).
+enum MmaTile : int {
+    kTile256x256 = 0,   // 2x2 waves of 128x128
+    kTile128x128 = 1,   // 2x2 waves of 64x64
+    kTile256x64 = 2,    // 4x1 waves of 64x64
+    kTile64x64 = 3,     // 2x2 waves of 32x32
+    kTile128x64 = 4,    // 2x2 waves of 64x32
+    kTileCount = 5
+};
+int mma_tile_rows(int tile);
+int mma_tile_cols(int tile);
+
+// out: kOutBf16 / kOutFp8 / kOutF32; act: kActNone / kActRelu / kActGelu.
+hipError_t launch_mma_bf16(const MmaArgs& args, bool conv, int act, int tile, hipStream_t stream);
+hipError_t launch_mma_fp8(const MmaArgs& args, int act, int out, int tile, hipStream_t stream);
+
+// fp32 direct convolution with the same epilogue (bias -> residual -> act).
+struct ConvF32Args {
+    const float* x;
+    const float* w;
+    const float* bias;      // nullable
+    const float* res;       // nullable
+    float* y;
+    int64_t M;              // n * ho * wo
+    int Cout, K;
+    int H, W, Cin, Ho, Wo, KW, SH, SW, PH, PW;
+};
+hipError_t launch_conv_f32(const ConvF32Args& args, int act, hipStream_t stream);
+
+// Elementwise passes of the unfused chain.  dt: 0 fp32, 1 bf16.
+hipError_t launch_bn_apply(int64_t rows, int64_t c, int dt, const void* y, const float* gamma,
+                           const float* beta, const float* mean, const float* var, float eps,
+                           void* z, hipStream_t stream);
+hipError_t launch_scale_shift(int64_t rows, int64_t c, int dt, const void* y, const float* scale,
+                              const float* shift, void* z, hipStream_t stream);
+hipError_t launch_add(int64_t count, int dt, const void* a, const void* b, void* out,
+                      hipStream_t stream);
+hipError_t launch_act(int64_t count, int dt, int act, const void* in, void* out, hipStream_t stream);
+hipError_t launch_quant(int64_t count, const float* in, float inv_scale, uint8_t* codes,
+                        hipStream_t stream);
+
+}  // namespace dlf

@@ -1,0 +1,246 @@
+/*
+ * dlfusion.h - C ABI of the fused Conv/MatMul -> BatchNorm -> activation
+ * operator for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for one layer,
+ *     out = act( conv(x, W') + b' [+ residual] )           (bf16 / fp32)
+ *     out = Q( relu( acc(xq, Wq) * alpha + beta' ) / s_y )  (fp8 e4m3)
+ * in a single kernel whose epilogue runs on the accumulator registers, so the
+ * pre-activation tensors never reach HBM.  BatchNorm is folded into the
+ * weights on the host beforehand (dlf_fold_bn, dlf_bn_scale_shift).  An
+ * unfused chain of separate kernels (dlf_conv_plain ... dlf_quant_apply) is
+ * kept only for comparing HBM traffic and timings against the fused kernel.
+ *
+ * Sources (web pages; the section named is where each definition appears):
+ *  [OPPL] "OpenPPL算子融合深度解析：从图优化到推理性能提升" (OpenPPL operator
+ *         fusion deep dive), codechina.net.
+ *  [INFR] discosf.com inference-fusion practice article (page titled
+ *         "企业官网建设流程全解析").
+ *  [CANN] aitangshan.cn graph-autofusion (CANN) article.
+ *  [RFC]  "RFC：自动融合: 扩展统一 Pattern Matcher 覆盖量化融合与 GMM/MM+激活",
+ *         MindIE-SD issue 298.
+ *  [FRT]  "FlashRT 跨层融合深度解析", sheratonhq.com.
+ *
+ * Conventions shared by every entry point
+ *  - Plain C types only.  Device pointers are HIP device memory owned by the
+ *    caller; the library allocates no device memory and keeps no pointer after
+ *    it returns.  Host pointers (fold functions) are plain host memory.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Device work is enqueued asynchronously on it; nothing synchronises.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Every argument is validated on the host before any HIP call; a failed
+ *    check returns a negative dlf_status and launches nothing.  The reason is
+ *    kept in a thread-local string returned by dlf_last_error().
+ *  - DLF_ERR_UNSUPPORTED means "this combination has no fused kernel": the
+ *    caller runs the unfused chain instead.  Nothing is ever approximated
+ *    silently ([OPPL] §4.2 falls back to separate ops when a fused form does
+ *    not apply; [RFC] §3.7 falls back to the original graph on a mismatch).
+ *  - Device pointers must be 16-byte aligned (vector loads); bf16 inputs need
+ *    their contiguous dimension (c_in, or k) to be a multiple of 8, fp8 inputs
+ *    a multiple of 16.  Zero-sized outputs are valid and launch nothing.
+ *  - The output must not overlap any input (DLF_ERR_ALIAS): every input
+ *    element is read by many output tiles.
+ *  - Thread safety: no global mutable state besides the thread-local error.
+ */
+#ifndef DLFUSION_H
+#define DLFUSION_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DLF_OK = 0,
+    DLF_ERR_INVALID_ARG = -1,   /* null / negative / non-finite / misaligned argument */
+    DLF_ERR_UNSUPPORTED = -2,   /* no fused kernel for this combination: run the unfused chain */
+    DLF_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
+    DLF_ERR_ALIAS = -4          /* the output overlaps an input */
+} dlf_status;
+
+typedef enum {
+    DLF_F32 = 0,                /* IEEE binary32 */
+    DLF_BF16 = 1,               /* bfloat16, stored as uint16 bit patterns */
+    DLF_FP8_E4M3 = 2            /* OCP e4m3fn codes (uint8): max 448, no inf, S.1111.111 = NaN */
+} dlf_dtype;
+
+/* Activation of the epilogue; numbering as the epilogue's activation field in
+ * [OPPL] §4.3 (0 none, 1 ReLU, 2 GELU).  GELU is the tanh form
+ * 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))). */
+typedef enum {
+    DLF_ACT_NONE = 0,
+    DLF_ACT_RELU = 1,
+    DLF_ACT_GELU_TANH = 2
+} dlf_act;
+
+/* A 2-D convolution layer.  x is NHWC [n][h][w][c_in]; weights are OHWI
+ * [c_out][kh][kw][c_in] (the GEMM view: B = [c_out][K], K = kh*kw*c_in,
+ * k = (r*kw + s)*c_in + ci); y (and residual) are NHWC [n][ho][wo][c_out] with
+ * ho = (h + 2 pad_h - kh)/stride_h + 1, wo likewise.  Zero padding, dilation 1,
+ * one group.  [INFR] §3.3 gives the kernel arguments (C_in, C_out, H, W, KH,
+ * KW, stride, pad) and the zero-padding rule; [OPPL] §3.4 motivates NHWC. */
+typedef struct {
+    int64_t n, h, w, c_in, c_out, kh, kw;
+    int32_t stride_h, stride_w, pad_h, pad_w;
+    dlf_dtype dtype;            /* storage type of x, w, residual and y */
+    dlf_act act;
+} dlf_conv_desc;
+
+/* A matrix product C[m][n] = A[m][k] . B[n][k]^T (a 1x1 convolution over m
+ * tokens; B in the [out][in] layout of a linear layer). */
+typedef struct {
+    int64_t m, n, k;
+    dlf_dtype in_dtype;         /* type of A and B */
+    dlf_dtype out_dtype;        /* type of C (and residual) */
+    dlf_act act;
+    float out_inv_scale;        /* fp8 output only: fp32(1/s_y) of the static output scale */
+} dlf_gemm_desc;
+
+/* ---------------------------------------------------------------------- */
+/* Host-side folding (once per layer, at load time)                        */
+/* ---------------------------------------------------------------------- */
+
+/* Fold an inference BatchNorm into the preceding convolution's weights and
+ * bias ([OPPL] §3.1; derivation in [INFR] §2.1):
+ *     s[c]   = gamma[c] / sqrt(var[c] + eps)
+ *     W'[c,:] = W[c,:] * s[c]
+ *     b'[c]  = (b[c] - mean[c]) * s[c] + beta[c],   b = 0 when conv_bias is NULL
+ * A bias is always produced, so a conv without one gains one ([OPPL] §3.1).
+ * eps is used exactly as given; nothing is approximated ([OPPL] §3.1, [INFR]
+ * §2.1 and §4.1 on what a dropped eps does to low-variance channels).  The
+ * bias is computed from the original W and b, never from W' ([INFR] §2.1).
+ * All arithmetic is binary64; each W' is rounded once (round to nearest
+ * even) to w_out_dtype, avoiding the double rounding of [OPPL] §6.2.
+ *   w        host, [cout][k] fp32 (OHWI flattened, k = kh*kw*c_in)
+ *   conv_bias host, [cout] fp32 or NULL
+ *   gamma, beta, mean, var  host, [cout] fp32
+ *   eps      finite, >= 0; var[c] + eps must be > 0 for every channel
+ *   w_out_dtype  DLF_F32 or DLF_BF16 (else DLF_ERR_UNSUPPORTED)
+ *   w_out    host, [cout][k] in w_out_dtype (uint16 bit patterns for bf16)
+ *   bias_out host, [cout] fp32, always written
+ * Synchronous; touches no GPU.  May be called with cout == 0 or k == 0. */
+dlf_status dlf_fold_bn(int64_t cout, int64_t k, const float *w, const float *conv_bias,
+                       const float *gamma, const float *beta, const float *mean,
+                       const float *var, double eps, dlf_dtype w_out_dtype,
+                       void *w_out, float *bias_out);
+
+/* Per-channel scale and shift of a BatchNorm kept out of the weights, for the
+ * fp8 path, where a per-channel factor inside the weights would change their
+ * per-tensor amax and thus their scale ([RFC] §3.4 takes the input and weight
+ * scales from the graph; [FRT] §3 folds norm parameters at load time):
+ *     s[c] = gamma[c] / sqrt(var[c] + eps)
+ *     scale_out[c] = fp32( pre_scale * s[c] )                 (alpha)
+ *     shift_out[c] = fp32( (b[c] - mean[c]) * s[c] + beta[c] )  (beta')
+ * so that  BN(acc * pre_scale + b) = acc * alpha + beta'.  pre_scale is the
+ * product of the static input and weight scales s_x * s_w (1 for none).
+ * Binary64 throughout, one rounding per output.  Host memory, synchronous. */
+dlf_status dlf_bn_scale_shift(int64_t cout, const float *conv_bias, const float *gamma,
+                              const float *beta, const float *mean, const float *var,
+                              double eps, double pre_scale, float *scale_out,
+                              float *shift_out);
+
+/* ---------------------------------------------------------------------- */
+/* Fused kernels (the hot path)                                            */
+/* ---------------------------------------------------------------------- */
+
+/* Fused convolution with a register epilogue ([OPPL] §4.3: conv main loop as
+ * an implicit GEMM plus an epilogue applied in the order bias -> residual ->
+ * activation before the single store; [OPPL] §2.1 and §3.3):
+ *     y = act( conv(x, w) + bias[c] + residual )
+ * w and bias are the folded W' and b' from dlf_fold_bn.  Accumulation is fp32
+ * ([OPPL] §4.2 and §6.2, [INFR] §4.1); the output is rounded once (RNE).
+ * Each element of y is written to device memory exactly once.
+ *   d        host descriptor; dtype DLF_F32 (fp32 FMA kernel) or DLF_BF16
+ *            (bf16 MFMA implicit GEMM, c_in % 8 == 0); DLF_FP8_E4M3 ->
+ *            DLF_ERR_UNSUPPORTED
+ *   x, w     device, layouts as in dlf_conv_desc, type d->dtype
+ *   bias     device [c_out] fp32, or NULL (no bias)
+ *   residual device, same shape and type as y, or NULL ([OPPL] §4.2: only a
+ *            dense same-shape tensor is absorbed)
+ *   y        device output
+ *   stream   hipStream_t or NULL */
+dlf_status dlf_conv_fused(const dlf_conv_desc *d, const void *x, const void *w,
+                          const float *bias, const void *residual, void *y, void *stream);
+
+/* Fused matrix product with the same register epilogue, per output column n:
+ *     v = acc * col_scale[n] + col_shift[n]  [+ residual]; v = act(v)
+ *     bf16 out:  C = bf16(v)
+ *     fp8 out:   C = Q( fp32(v * out_inv_scale) )  (static per-tensor scale)
+ * Q rounds to the nearest e4m3 value, ties to even, and saturates at +-448
+ * (the quantisation-aware clamp of [OPPL] §6.4; the static-scale fp8 epilogue
+ * of [FRT] §3 and §6; quantised MatMul + activation of [RFC] §3.4).
+ * Supported: in_dtype BF16 -> out BF16 (any act, optional bf16 residual);
+ *            in_dtype FP8_E4M3 -> out FP8_E4M3 or BF16 (act NONE or RELU,
+ *            no residual).  Everything else -> DLF_ERR_UNSUPPORTED.
+ *   a        device [m][k]; b device [n][k] (k % 8 == 0 bf16, % 16 == 0 fp8)
+ *   col_scale device [n] fp32 or NULL (= 1); col_shift device [n] fp32 or
+ *            NULL (= 0): the bias, or the folded BN scale/shift (alpha, beta')
+ *   residual device [m][n] in out_dtype (bf16 only) or NULL
+ *   c        device [m][n] in out_dtype */
+dlf_status dlf_gemm_fused(const dlf_gemm_desc *d, const void *a, const void *b,
+                          const float *col_scale, const float *col_shift,
+                          const void *residual, void *c, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Unfused comparison chain: one kernel per op, every intermediate goes     */
+/* through device memory ([OPPL] §2.1, §3.3; [CANN] MatMul->BiasAdd->ReLU   */
+/* costs three HBM round trips where the fused form costs one).             */
+/* ---------------------------------------------------------------------- */
+
+/* y = conv(x, w) + conv_bias (no BN, no activation), rounded once to d->dtype.
+ * Same layouts, dtypes and checks as dlf_conv_fused; d->act must be NONE. */
+dlf_status dlf_conv_plain(const dlf_conv_desc *d, const void *x, const void *w,
+                          const float *conv_bias, void *y, void *stream);
+
+/* y = A . B^T, no epilogue.  bf16 in -> d->out_dtype BF16 (rounded once);
+ * fp8 in -> d->out_dtype F32 with y = fp32(acc * dequant), dequant = s_x*s_w.
+ * d->act must be NONE. */
+dlf_status dlf_gemm_plain(const dlf_gemm_desc *d, const void *a, const void *b,
+                          float dequant, void *y, void *stream);
+
+/* Inference BatchNorm as its own pass over [rows][c] (channel innermost):
+ *     z = gamma (y - mean) / sqrt(var + eps) + beta        ([OPPL] §3.1)
+ * computed in fp32; dt is DLF_F32 or DLF_BF16 for both y and z; BN params are
+ * device [c] fp32. */
+dlf_status dlf_bn_apply(int64_t rows, int64_t c, dlf_dtype dt, const void *y,
+                        const float *gamma, const float *beta, const float *mean,
+                        const float *var, double eps, void *z, void *stream);
+
+/* z = y * scale[ch] + shift[ch] over [rows][c]; scale NULL means 1 (a
+ * BiasAdd).  dt DLF_F32 or DLF_BF16; scale/shift device fp32 [c]. */
+dlf_status dlf_scale_shift_apply(int64_t rows, int64_t c, dlf_dtype dt, const void *y,
+                                 const float *scale, const float *shift, void *z,
+                                 void *stream);
+
+/* out = a + b elementwise (the residual Add as its own kernel, [OPPL] §3.3).
+ * dt DLF_F32 or DLF_BF16. */
+dlf_status dlf_add(int64_t count, dlf_dtype dt, const void *a, const void *b, void *out,
+                   void *stream);
+
+/* out = act(in) elementwise; dt DLF_F32 or DLF_BF16.  in == out is allowed
+ * (the only entry point that may work in place). */
+dlf_status dlf_act_apply(int64_t count, dlf_dtype dt, dlf_act act, const void *in, void *out,
+                         void *stream);
+
+/* codes = Q( fp32(in * inv_scale) ): the same e4m3 quantiser the fused fp8
+ * epilogue uses, as its own pass (static per-tensor scale, [FRT] §3). */
+dlf_status dlf_quant_apply(int64_t count, const float *in, float inv_scale, uint8_t *codes,
+                           void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Status                                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Static name of a status code. */
+const char *dlf_status_string(dlf_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next library call on this thread. */
+const char *dlf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLFUSION_H */

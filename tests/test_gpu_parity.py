@@ -1,0 +1,408 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (the floored relative metric of oracle.rel_error):
+  fp32 1e-4, bf16 2e-2; fp8 outputs within one e4m3 code of the oracle's code;
+  the quantiser bit-exact on identical fp32 inputs.
+Every output buffer carries a guard band after its end that must stay untouched.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+GUARD = 4096
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dl_fusion_amd  # noqa: F401  (loud failure if the library is missing)
+    torch.cuda.set_device(0)
+    yield
+    os.environ.pop("DLF_TILE", None)
+
+
+def dlf():
+    import dl_fusion_amd
+    return dl_fusion_amd
+
+
+def layers():
+    from dl_fusion_amd import layers as L
+    return L
+
+
+def case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def guarded(shape, dtype):
+    """A contiguous output tensor followed by a canary-filled guard band."""
+    n = int(np.prod(shape))
+    buf = torch.empty(n + GUARD, dtype=dtype, device="cuda")
+    if dtype == torch.uint8:
+        buf.fill_(0xA5)
+    elif dtype == torch.bfloat16:
+        buf.view(torch.int16).fill_(0x7FA5)
+    else:
+        buf.view(torch.int32).fill_(0x7FA5A5A5)
+    return buf, buf[:n].view(shape)
+
+
+def guard_intact(buf, n):
+    tail = buf[n:]
+    if buf.dtype == torch.uint8:
+        return bool((tail == 0xA5).all())
+    if buf.dtype == torch.bfloat16:
+        return bool((tail.view(torch.int16) == 0x7FA5).all())
+    return bool((tail.view(torch.int32) == 0x7FA5A5A5).all())
+
+
+def host(t, dtype):
+    return layers().to_host(t, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Convolutions
+# ---------------------------------------------------------------------------
+def check_conv(wl, tiles=(None,), unfused=True):
+    inp = workloads.generate(wl)
+    ref = oracle.conv_bn_act(inp)
+    L = layers().make_layer(inp, with_unfused=unfused)
+    tdt = L.y.dtype
+    for tile in tiles:
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"conv_fused {wl} tile={tile}")
+        buf, y = guarded(L.out_shape, tdt)
+        L.forward(y=y)
+        torch.cuda.synchronize()
+        got = oracle.widen(host(y, wl.dtype), wl.dtype)
+        err = oracle.rel_error(got, ref)
+        assert err <= TOL[wl.dtype], (wl, tile, err)
+        assert guard_intact(buf, y.numel()), "store beyond the output"
+        if wl.act == "relu":
+            assert np.all(got >= 0)
+    os.environ.pop("DLF_TILE", None)
+    if unfused:
+        case(f"conv_unfused {wl}")
+        yu = L.forward_unfused()
+        torch.cuda.synchronize()
+        err = oracle.rel_error(oracle.widen(host(yu, wl.dtype), wl.dtype), ref)
+        assert err <= TOL[wl.dtype], ("unfused", wl, err)
+
+
+def test_config0_fp32_conv_bn_relu_full():
+    check_conv(workloads.workload(0))
+
+
+def test_config1_bf16_conv_bn_relu_full():
+    check_conv(workloads.workload(1))
+
+
+def test_config2_bf16_conv_bn_residual_relu_full():
+    check_conv(workloads.workload(2))
+
+
+def test_config2_with_conv_bias_variant():
+    check_conv(workloads.workload(2, n=4, conv_bias=True), unfused=False)
+
+
+RAGGED_BF16 = [
+    dict(n=2, h=9, w=7, cin=8, cout=40, kh=3, kw=3, stride=1, pad=1, act="relu", residual=False),
+    dict(n=1, h=13, w=11, cin=24, cout=72, kh=3, kw=3, stride=2, pad=1, act="gelu_tanh", residual=True),
+    dict(n=3, h=6, w=6, cin=64, cout=64, kh=1, kw=1, stride=1, pad=0, act="none", residual=False),
+    dict(n=1, h=10, w=10, cin=16, cout=96, kh=5, kw=5, stride=1, pad=2, act="relu", residual=True),
+    dict(n=2, h=7, w=9, cin=136, cout=33, kh=3, kw=3, stride=1, pad=1, act="relu", residual=False),
+    dict(n=5, h=15, w=15, cin=32, cout=129, kh=3, kw=3, stride=1, pad=0, act="gelu_tanh", residual=False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(RAGGED_BF16)))
+def test_bf16_conv_ragged_shapes_every_tile(i):
+    wl = workloads.workload(1, conv_bias=bool(i % 2), **RAGGED_BF16[i])
+    check_conv(wl, tiles=(None, 0, 1, 2, 3, 4), unfused=(i < 3))
+
+
+RAGGED_F32 = [
+    dict(n=2, h=9, w=7, cin=3, cout=5, kh=3, kw=3, stride=2, pad=1, act="relu", residual=False),
+    dict(n=1, h=5, w=5, cin=16, cout=70, kh=1, kw=1, stride=1, pad=0, act="gelu_tanh", residual=True),
+    dict(n=3, h=11, w=6, cin=7, cout=33, kh=5, kw=3, stride=1, pad=2, act="none", residual=False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(RAGGED_F32)))
+def test_f32_conv_ragged_shapes(i):
+    wl = workloads.workload(0, conv_bias=bool(i % 2), **RAGGED_F32[i])
+    check_conv(wl)
+
+
+def test_conv_empty_and_degenerate():
+    d = dlf()
+    case("conv empty batch")
+    x = torch.empty(0, device="cuda", dtype=torch.bfloat16)
+    d.dlf_conv_fused(d.conv_desc(0, 8, 8, 16, 16), x, x, None, None, x)
+    case("conv eps=1e-2 no-bias stress at tiny size")
+    check_conv(workloads.workload(2, n=1, h=3, w=3, cin=8, cout=32))
+
+
+# ---------------------------------------------------------------------------
+# bf16 GEMM + bias + activation
+# ---------------------------------------------------------------------------
+def gemm_reference(inp, rows, residual=None):
+    wl = inp["workload"]
+    x = oracle.widen(inp["x"], "bf16")[rows]
+    y = oracle.matmul_nt(x, oracle.widen(inp["w"], "bf16"))
+    if inp.get("bias") is not None:
+        y = oracle.bias_add(y, inp["bias"])
+    if residual is not None:
+        y = oracle.add(y, oracle.widen(residual, "bf16")[rows])
+    return oracle.activation(y, wl.act)
+
+
+def sample_rows(m, tile=256, extra=40, seed=0):
+    rng = np.random.default_rng(seed)
+    edges = {0, 1, m - 1, m - 2}
+    for t in range(tile, m, tile):
+        edges.update({t - 1, t})
+    edges = sorted(r for r in edges if 0 <= r < m)[:24]
+    return np.array(sorted(set(edges) | set(rng.choice(m, min(extra, m), replace=False).tolist())))
+
+
+def test_config3_bf16_gemm_bias_gelu_full_size_sampled():
+    wl = workloads.workload(3)
+    inp = workloads.generate(wl)
+    L = layers().make_layer(inp)
+    case(f"gemm_fused {wl}")
+    buf, y = guarded((wl.m, wl.n), torch.bfloat16)
+    L.forward(y=y)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, y.numel())
+    rows = sample_rows(wl.m)
+    got_all = oracle.widen(host(y, "bf16"), "bf16")
+    assert np.all(np.isfinite(got_all)) and got_all.min() >= -0.1701   # GELU(tanh) minimum ~ -0.170
+    ref = gemm_reference(inp, rows)
+    err = oracle.rel_error(got_all[rows], ref)
+    assert err <= TOL["bf16"], err
+    case("gemm_unfused config 3")
+    yu = L.forward_unfused()
+    torch.cuda.synchronize()
+    err_u = oracle.rel_error(oracle.widen(host(yu, "bf16"), "bf16")[rows], ref)
+    assert err_u <= TOL["bf16"], err_u
+
+
+RAGGED_GEMM = [
+    dict(m=300, n=200, k=136, act="gelu_tanh", bias=True),
+    dict(m=1, n=17, k=8, act="relu", bias=True),
+    dict(m=513, n=257, k=520, act="none", bias=False),
+    dict(m=64, n=48, k=0, act="gelu_tanh", bias=True),
+    dict(m=777, n=1000, k=1024, act="relu", bias=True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(RAGGED_GEMM)))
+def test_bf16_gemm_ragged_shapes_every_tile(i):
+    wl = workloads.workload(3, **RAGGED_GEMM[i])
+    inp = workloads.generate(wl)
+    res = None
+    if i % 2 == 0:
+        res = workloads.bf16_bits(np.random.default_rng(i).standard_normal((wl.m, wl.n)).astype(np.float32))
+    rows = np.arange(wl.m)
+    ref = gemm_reference(inp, rows, res)
+    L = layers().make_layer(inp)
+    res_d = layers().to_device(res, "bf16") if res is not None else None
+    for tile in (None, 0, 1, 2, 3, 4):
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"gemm_fused {wl} tile={tile} residual={res is not None}")
+        buf, y = guarded((wl.m, wl.n), torch.bfloat16)
+        L.forward(y=y, residual=res_d)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, y.numel())
+        err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+        assert err <= TOL["bf16"], (wl, tile, err)
+    os.environ.pop("DLF_TILE", None)
+    if res is None:
+        case(f"gemm_unfused {wl}")
+        yu = L.forward_unfused()
+        torch.cuda.synchronize()
+        assert oracle.rel_error(oracle.widen(host(yu, "bf16"), "bf16"), ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# fp8 GEMM + scale/shift + ReLU + static e4m3 quantisation
+# ---------------------------------------------------------------------------
+def fp8_reference(inp, rows):
+    sub = dict(inp)
+    codes, u = oracle.fp8_gemm_bn_relu_quant(sub, rows=rows)
+    return codes, u
+
+
+def assert_codes_within_one(got, ref):
+    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert np.all(got <= 0x7E) and np.all(ref <= 0x7E)
+    assert d.max() <= 1, (d.max(), np.argwhere(d > 1)[:5])
+    return float(np.mean(d == 0))
+
+
+def test_config4_fp8_gemm_bn_relu_quant_full_size_sampled():
+    wl = workloads.workload(4)
+    inp = workloads.generate(wl)
+    L = layers().make_layer(inp)
+    case(f"fp8_fused {wl}")
+    buf, y = guarded((wl.m, wl.n), torch.uint8)
+    L.forward(y=y)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, y.numel())
+    got_all = host(y, "fp8")
+    assert np.all(got_all <= 0x7E)          # non-negative finite codes only (post-ReLU, saturating)
+    rows = sample_rows(wl.m)
+    ref, _ = fp8_reference(inp, rows)
+    exact = assert_codes_within_one(got_all[rows], ref)
+    assert exact > 0.9, exact
+    case("fp8_unfused config 4")
+    yu = L.forward_unfused()
+    torch.cuda.synchronize()
+    assert_codes_within_one(host(yu, "fp8")[rows], ref)
+
+
+RAGGED_FP8 = [
+    dict(m=300, n=200, k=144),
+    dict(m=77, n=33, k=16),
+    dict(m=513, n=260, k=1040),
+    dict(m=1000, n=1100, k=4096),
+]
+
+
+@pytest.mark.parametrize("i", range(len(RAGGED_FP8)))
+def test_fp8_gemm_ragged_shapes_every_tile(i):
+    wl = workloads.workload(4, **RAGGED_FP8[i])
+    inp = workloads.generate(wl)
+    rows = np.arange(wl.m)
+    ref, u = fp8_reference(inp, rows)
+    L = layers().make_layer(inp)
+    for tile in (None, 0, 1, 2, 3, 4):
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"fp8_fused {wl} tile={tile}")
+        buf, y = guarded((wl.m, wl.n), torch.uint8)
+        L.forward(y=y)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, y.numel())
+        assert_codes_within_one(host(y, "fp8"), ref)
+    os.environ.pop("DLF_TILE", None)
+    case(f"fp8 -> bf16 out {wl}")
+    d = dlf()
+    yb = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device="cuda")
+    d.dlf_gemm_fused(d.gemm_desc(wl.m, wl.n, wl.k, "fp8", "bf16", "relu"), L.x, L.w, L.alpha, L.shift, None, yb)
+    torch.cuda.synchronize()
+    assert oracle.rel_error(oracle.widen(host(yb, "bf16"), "bf16"), u) <= TOL["bf16"]
+    case(f"fp8_unfused {wl}")
+    yu = L.forward_unfused()
+    torch.cuda.synchronize()
+    assert_codes_within_one(host(yu, "fp8"), ref)
+
+
+def test_fp8_saturation_variant():
+    """Half the static output scale: the largest outputs must saturate to 448 (0x7E)."""
+    wl = workloads.workload(4, m=256, n=256, k=512, out_scale=0.5)
+    inp = workloads.generate(wl)
+    ref, u = fp8_reference(inp, np.arange(wl.m))
+    assert np.any(ref == 0x7E)
+    L = layers().make_layer(inp, with_unfused=False)
+    case(f"fp8_fused saturation {wl}")
+    y = L.forward()
+    torch.cuda.synchronize()
+    got = host(y, "fp8")
+    assert_codes_within_one(got, ref)
+    assert np.all(got[u / inp["s_y"] >= 464.0] == 0x7E)
+
+
+# ---------------------------------------------------------------------------
+# The e4m3 quantiser: bit-exact against the oracle on identical fp32 inputs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("inv", [1.0, 0.125, float(np.float32(1 / 3.7)), float(np.float32(1 / 11.3))])
+def test_quantiser_bit_exact_exhaustive(inv):
+    """Every fp32 pattern whose scaled value falls in [2^-12, 512) (about 21 binades x 2^23),
+    plus samples of the saturating, underflowing and negative ranges."""
+    d = dlf()
+    lo = np.float32(2.0 ** -12 / inv).view(np.uint32)
+    hi = np.float32(512.0 / inv).view(np.uint32)
+    step = 1 << 24
+    codes = torch.empty(step, dtype=torch.uint8, device="cuda")
+    case(f"quant exhaustive inv={inv} patterns={int(hi) - int(lo)}")
+    for start in range(int(lo), int(hi), step):
+        n = min(step, int(hi) - start)
+        bits = torch.arange(start, start + n, dtype=torch.int64, device="cuda").to(torch.int32)
+        v = bits.view(torch.float32)
+        d.dlf_quant_apply(n, v, inv, codes[:n])
+        got = codes[:n].cpu().numpy()
+        ref = oracle.quant_f32(v.cpu().numpy(), inv)
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, (start, v.cpu().numpy()[bad[:4]], got[bad[:4]], ref[bad[:4]])
+    rng = np.random.default_rng(1)
+    extra = np.concatenate([
+        rng.uniform(0, 2.0 ** -12 / inv, 100000), rng.uniform(448 / inv, 1e6 / inv, 100000),
+        -rng.uniform(0, 600 / inv, 200000), [0.0, -0.0, 448 / inv, 464 / inv, 3e38],
+    ]).astype(np.float32)
+    vt = torch.from_numpy(extra).cuda()
+    out = torch.empty(extra.size, dtype=torch.uint8, device="cuda")
+    d.dlf_quant_apply(extra.size, vt, inv, out)
+    np.testing.assert_array_equal(out.cpu().numpy(), oracle.quant_f32(extra, inv))
+
+
+# ---------------------------------------------------------------------------
+# Elementwise passes of the unfused chain (odd sizes exercise the scalar tails)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_unfused_eltwise_passes(dt):
+    d = dlf()
+    rng = np.random.default_rng(5)
+    rows, c = 1001, 24
+    y32 = rng.standard_normal((rows, c)).astype(np.float32)
+    r32 = rng.standard_normal((rows, c)).astype(np.float32)
+    store = (lambda a: a) if dt == "f32" else workloads.bf16_bits
+    y_s, r_s = store(y32), store(r32)
+    L = layers()
+    y, r = L.to_device(y_s, dt), L.to_device(r_s, dt)
+    g, b, mu = rng.uniform(0.5, 1.5, c), rng.normal(0, 0.1, c), rng.normal(0, 0.1, c)
+    var = rng.uniform(1e-3, 1, c)
+    P = [torch.from_numpy(np.asarray(a, np.float32)).cuda() for a in (g, b, mu, var)]
+    out = torch.empty_like(y)
+    tol = TOL[dt]
+    yw, rw = oracle.widen(y_s, dt), oracle.widen(r_s, dt)
+    P32 = [np.asarray(a, np.float32) for a in (g, b, mu, var)]
+    case(f"bn_apply {dt}")
+    d.dlf_bn_apply(rows, c, dt, y, *P, 1e-5, out)
+    torch.cuda.synchronize()
+    assert oracle.rel_error(oracle.widen(host(out, dt), dt), oracle.batchnorm(yw, *P32, 1e-5)) <= tol
+    case(f"scale_shift {dt}")
+    d.dlf_scale_shift_apply(rows, c, dt, y, P[0], P[1], out)
+    torch.cuda.synchronize()
+    ref = yw * P32[0].astype(np.float64) + P32[1].astype(np.float64)
+    assert oracle.rel_error(oracle.widen(host(out, dt), dt), ref) <= tol
+    case(f"add {dt}")
+    d.dlf_add(rows * c - 3, dt, y, r, out)
+    torch.cuda.synchronize()
+    got = oracle.widen(host(out, dt), dt).ravel()[:rows * c - 3]
+    assert oracle.rel_error(got, oracle.add(yw, rw).ravel()[:rows * c - 3]) <= tol
+    for act in ("relu", "gelu_tanh"):
+        case(f"act {act} {dt}")
+        d.dlf_act_apply(rows * c - 5, dt, act, y, out)
+        torch.cuda.synchronize()
+        got = oracle.widen(host(out, dt), dt).ravel()[:rows * c - 5]
+        assert oracle.rel_error(got, oracle.activation(yw, act).ravel()[:rows * c - 5]) <= tol
