@@ -361,4 +361,11 @@ def test_fp8_pipeline_codes_are_post_relu_and_in_range():
 def test_metric_floor():
     o = np.array([0.0, 1.0, -1.0, 0.0])
     assert oracle.rel_error(o, o) == 0.0
+    # 1-D: one channel, floor = rms(o) = sqrt(0.5)
     assert math.isclose(oracle.rel_error(o + np.array([0.1, 0, 0, 0]), o), 0.1 / math.sqrt(0.5))
+    # 2-D: the floor is the rms of each column (channel)
+    o2 = np.array([[0.0, 10.0], [0.0, -10.0], [1.0, 0.0], [-1.0, 0.0]])
+    g2 = o2 + np.array([[0.5, 0.0], [0, 0], [0, 0], [0, 0]])
+    assert math.isclose(oracle.rel_error(g2, o2), 0.5 / math.sqrt(0.5))
+    g3 = o2 + np.array([[0.0, 0.0], [0, 0], [0, 1.0], [0, 0]])
+    assert math.isclose(oracle.rel_error(g3, o2), 1.0 / math.sqrt(50.0))
