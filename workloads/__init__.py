@@ -186,7 +186,7 @@ def generate(wl) -> dict:
                    var=var, eps=float(wl.eps), residual=res, stressed=stressed)
     elif isinstance(wl, GemmWorkload):
         x = rng.standard_normal((wl.m, wl.k)).astype(np.float32)
-        w = rng.normal(0.0, 1.0 / np.sqrt(wl.k), (wl.n, wl.k)).astype(np.float32)
+        w = rng.normal(0.0, 1.0 / np.sqrt(max(wl.k, 1)), (wl.n, wl.k)).astype(np.float32)
         bias = rng.normal(0.0, 0.02, wl.n).astype(np.float32) if wl.bias else None
         out.update(x=bf16_bits(x), w=bf16_bits(w), bias=bias)
     elif isinstance(wl, Fp8GemmWorkload):
