@@ -97,7 +97,7 @@ class Fp8GemmWorkload:
     n: int
     k: int
     eps: float = 1e-5
-    out_scale: float = 8.0     # static output scale s_y (power of two)
+    out_scale: float = 8.0     # static output scale s_y, fixed ahead of time (a power of two)
     seed: int = 4
 
     @property
