@@ -56,7 +56,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<0..4> forces one
+// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<0..5> forces one
 // (tuning only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x
 // (tile area / relative MFMA efficiency of the tile shape).
 int pick_tile(int64_t M, int64_t N) {
@@ -64,12 +64,12 @@ int pick_tile(int64_t M, int64_t N) {
         const int t = std::atoi(env);
         if (t >= 0 && t < dlf::kTileCount) return t;
     }
-    const int cands[] = {dlf::kTile256x256, dlf::kTile128x128, dlf::kTile256x64, dlf::kTile128x64,
-                         dlf::kTile64x64};
-    const double eff[] = {1.0, 0.8, 0.8, 0.65, 0.5};
+    const int cands[] = {dlf::kTile256x256, dlf::kTile256x128, dlf::kTile128x128, dlf::kTile256x64,
+                         dlf::kTile128x64, dlf::kTile64x64};
+    const double eff[] = {1.0, 0.9, 0.8, 0.8, 0.65, 0.5};
     int best = dlf::kTile64x64;
     double best_cost = 0;
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 6; ++i) {
         const int t = cands[i];
         const int64_t bm = dlf::mma_tile_rows(t), bn = dlf::mma_tile_cols(t);
         if (bn > 64 && N <= bn / 2) continue;   // mostly-empty columns
@@ -164,7 +164,7 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
         a.bias = bias;
         a.res = static_cast<const float*>(residual);
         a.y = static_cast<float*>(y);
-        a.M = g.M;
+        a.M = static_cast<int>(g.M);
         a.Cout = static_cast<int>(d->c_out);
         a.K = static_cast<int>(g.K);
         a.H = static_cast<int>(d->h); a.W = static_cast<int>(d->w); a.Cin = static_cast<int>(d->c_in);

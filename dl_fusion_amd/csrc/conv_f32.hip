@@ -20,44 +20,63 @@ constexpr int kKs = 64;      // K slice
 template <int TC, int ACT>
 __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
     constexpr int PG = 256 / TC;            // pixel groups
-    constexpr int PPT = kPix / PG;          // pixels per lane
+    constexpr int PPT = kPix / PG;          // output pixels per lane
+    constexpr int XS = kPix * kKs / 256;    // im2col entries each lane stages per slice
     __shared__ float ws[kKs][TC + 1];
     __shared__ float xs[kPix][kKs + 1];
 
     const int tid = static_cast<int>(threadIdx.x);
     const int co_l = tid % TC, pg = tid / TC;
-    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPix;
+    const int p0 = static_cast<int>(blockIdx.x) * kPix;   // M <= 2^30 (checked on the host)
     const int c0 = static_cast<int>(blockIdx.y) * TC;
     const int co = c0 + co_l;
+
+    // staging assignment: this lane stages column kq of the slice for pixels kp + 4 i
+    const int kq = tid & (kKs - 1), kp = tid >> 6;
+    int px_base[XS], px_h[XS], px_w[XS];
+    const int hw = p.Ho * p.Wo;
+#pragma unroll
+    for (int i = 0; i < XS; ++i) {
+        const int m = p0 + kp + 4 * i;
+        const int mm = m < p.M ? m : 0;
+        const int img = mm / hw, rem = mm - img * hw;
+        const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
+        const int h0 = ho * p.SH - p.PH;
+        px_w[i] = wo * p.SW - p.PW;
+        px_base[i] = (img * p.H + h0) * p.W + px_w[i];
+        px_h[i] = m < p.M ? h0 : -(1 << 29);   // rows past M never pass the bounds test
+    }
 
     float acc[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) acc[j] = 0.0f;
 
-    const int hw = p.Ho * p.Wo;
     for (int k0 = 0; k0 < p.K; k0 += kKs) {
+        const int gk = k0 + kq;
+        const bool k_ok = gk < p.K;
         // weights slice -> ws[k][channel]
-        for (int e = tid; e < kKs * TC; e += 256) {
-            const int c = e / kKs, k = e % kKs;
-            const int gc = c0 + c, gk = k0 + k;
-            ws[k][c] = (gc < p.Cout && gk < p.K) ? p.w[static_cast<int64_t>(gc) * p.K + gk] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kKs * TC / 256; ++i) {
+            const int c = kp + 4 * i;
+            const int gc = c0 + c;
+            ws[kq][c] = (gc < p.Cout && k_ok) ? p.w[static_cast<int64_t>(gc) * p.K + gk] : 0.0f;
         }
-        // im2col slice -> xs[pixel][k]
-        for (int e = tid; e < kPix * kKs; e += 256) {
-            const int pix = e / kKs, k = e % kKs;
-            const int64_t m = p0 + pix;
-            const int gk = k0 + k;
+        // im2col slice -> xs[pixel][k]: one (tap, ci) decomposition per lane per slice
+        int r = 0, s = 0, ci = 0;
+        if (k_ok) {
+            const int tap = gk / p.Cin;
+            ci = gk - tap * p.Cin;
+            r = tap / p.KW;
+            s = tap - r * p.KW;
+        }
+#pragma unroll
+        for (int i = 0; i < XS; ++i) {
+            const int hi = px_h[i] + r, wi = px_w[i] + s;
             float v = 0.0f;
-            if (m < p.M && gk < p.K) {
-                const int tap = gk / p.Cin, ci = gk - tap * p.Cin;
-                const int r = tap / p.KW, s = tap - r * p.KW;
-                const int img = static_cast<int>(m / hw), rem = static_cast<int>(m % hw);
-                const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
-                const int hi = ho * p.SH - p.PH + r, wi = wo * p.SW - p.PW + s;
-                if (hi >= 0 && hi < p.H && wi >= 0 && wi < p.W)
-                    v = p.x[((static_cast<int64_t>(img) * p.H + hi) * p.W + wi) * p.Cin + ci];
-            }
-            xs[pix][k] = v;
+            if (k_ok && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                static_cast<unsigned>(wi) < static_cast<unsigned>(p.W))
+                v = p.x[static_cast<int64_t>(px_base[i] + r * p.W + s) * p.Cin + ci];
+            xs[kp + 4 * i][kq] = v;
         }
         __syncthreads();
         const int kn = min(kKs, p.K - k0);
@@ -73,9 +92,9 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
     const float b = p.bias ? p.bias[co] : 0.0f;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-        const int64_t m = p0 + pg + PG * j;
+        const int m = p0 + pg + PG * j;
         if (m >= p.M) continue;
-        const int64_t idx = m * p.Cout + co;
+        const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
         float v = acc[j] + b;
         if (p.res) v += p.res[idx];
         p.y[idx] = activate<ACT>(v);

@@ -33,11 +33,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// GELU, tanh form: 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+// GELU, tanh form: 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3).
+// Evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), i.e.
+// gelu(v) = v / (1 + 2^(-2 u log2 e)), with the hardware exp2 and reciprocal
+// (about 1 ulp each).  This form has no cancellation for negative v and gives
+// -0 / v in the saturated tails.
 __device__ __forceinline__ float gelu_tanh(float v) {
-    const float k0 = 0.797884560802865355879892f;   // sqrt(2/pi)
-    const float inner = k0 * (v + 0.044715f * v * v * v);
-    return 0.5f * v * (1.0f + tanhf(inner));
+    const float k = -2.0f * 0.797884560802865355879892f * 1.442695040888963407359924f;  // -2 sqrt(2/pi) log2(e)
+    const float t = v * fmaf(0.044715f * v, v, 1.0f);                                   // v + 0.044715 v^3
+    const float e = __builtin_amdgcn_exp2f(k * t);
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 template <int ACT>

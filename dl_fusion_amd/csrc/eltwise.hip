@@ -77,18 +77,28 @@ __global__ __launch_bounds__(kBlock) void channel_affine_kernel(int64_t count, i
     };
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    // the channel index advances by a constant per grid-stride step: one division per lane
     if (c % 8 == 0) {
         const int64_t nv = count / 8;
+        int64_t ch0 = (8 * t) % c;
+        const int64_t dch = (8 * stride) % c;
         for (int64_t v = t; v < nv; v += stride) {
             Vec8<DT> x;
             x.load(y, 8 * v);
-            const int64_t ch0 = (8 * v) % c;
 #pragma unroll
             for (int j = 0; j < 8; ++j) x.v[j] = f(x.v[j], ch0 + j);
             x.store(z, 8 * v);
+            ch0 += dch;
+            if (ch0 >= c) ch0 -= c;
         }
     } else {
-        for (int64_t i = t; i < count; i += stride) st(z, i, DT, f(ld(y, i, DT), i % c));
+        int64_t ch = t % c;
+        const int64_t dch = stride % c;
+        for (int64_t i = t; i < count; i += stride) {
+            st(z, i, DT, f(ld(y, i, DT), ch));
+            ch += dch;
+            if (ch >= c) ch -= c;
+        }
     }
 }
 

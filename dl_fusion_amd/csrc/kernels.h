@@ -32,7 +32,8 @@ enum MmaTile : int {
     kTile256x64 = 2,    // 4x1 waves of 64x64
     kTile64x64 = 3,     // 2x2 waves of 32x32
     kTile128x64 = 4,    // 2x2 waves of 64x32
-    kTileCount = 5
+    kTile256x128 = 5,   // 2x2 waves of 128x64
+    kTileCount = 6
 };
 int mma_tile_rows(int tile);
 int mma_tile_cols(int tile);
@@ -48,7 +49,7 @@ struct ConvF32Args {
     const float* bias;      // nullable
     const float* res;       // nullable
     float* y;
-    int64_t M;              // n * ho * wo
+    int M;                  // n * ho * wo (<= 2^30, checked on the host)
     int Cout, K;
     int H, W, Cin, Ho, Wo, KW, SH, SW, PH, PW;
 };

@@ -1,25 +1,34 @@
 // MFMA GEMM / implicit-GEMM kernel for gfx950 with a register epilogue.
 //
 // One workgroup (4 waves, 256 lanes) owns a BM x BN tile of C.  The K loop
-// stages 128-byte-wide slices of A and B (64 bf16 or 128 fp8 per row) through
-// LDS with a double buffer: while the MFMAs consume slice k, the next slice is
-// already in flight from global memory into registers and is written to the
-// other LDS buffer afterwards (one barrier per slice).  LDS rows are XOR-
-// swizzled in 16-byte chunks so that both the row-wise stores and the MFMA
-// fragment reads (32 rows x one chunk) are bank-conflict free.
+// streams 64-byte slices of every A and B row (32 bf16 or 64 fp8 values)
+// straight from global memory into a ring of STAGES LDS buffers with
+// global_load_lds_dwordx4 (no register staging), so STAGES-1 slices are in
+// flight while the MFMAs consume the current one.  Each load instruction fills
+// one contiguous kilobyte of LDS (16 rows); the lane -> row/chunk assignment
+// applies an XOR swizzle on the 16-byte chunks so that the MFMA operand reads
+// (32 rows x one chunk per instruction) are free of bank conflicts.  Lanes
+// whose chunk lies outside the operand (M/N/K tails, convolution padding) read
+// a zero page instead, so the LDS image is exactly the zero-padded operand.
 //
-// The contraction uses v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x64_f8f6f4
-// (fp8 e4m3 x e4m3) with fp32 accumulators that stay in registers; the
-// epilogue then applies per-column scale/shift (folded BN or bias), the
-// residual and the activation to those registers and stores each output
-// element once.  That is the conv implicit-GEMM main loop plus epilogue of
-// "OpenPPL算子融合深度解析" §4.3, with the FP8 static-scale store of
+// The contraction is v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x64_f8f6f4
+// (e4m3 x e4m3) with fp32 accumulators that stay in registers.  The MFMA is
+// issued as D = W . X^T, so each lane holds one output row and runs of four
+// consecutive output columns; the epilogue applies the per-column scale/shift
+// (folded BN or bias), the residual and the activation on those registers,
+// rounds once, and stages the tile through LDS so that every output element
+// is written to global memory exactly once by a coalesced 16-byte store.  This
+// is the conv implicit-GEMM main loop plus epilogue of
+// "OpenPPL算子融合深度解析" §4.3, with the static-scale FP8 store of
 // "FlashRT 跨层融合深度解析" §3.
 //
 // For a convolution the A operand is never materialised: row m = (img, ho, wo)
-// and column k = (r*KW + s)*Cin + ci are gathered from the NHWC input while
-// loading, with zero fill outside the image (zero padding as in the direct
-// convolution loop of the discosf.com fusion article §3.3).
+// and column k = (r*KW + s)*Cin + ci are gathered from the NHWC input by the
+// load addresses, with the zero page standing in for taps outside the image
+// (zero padding as in the direct convolution loop of the discosf.com fusion
+// article §3.3).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,22 +36,73 @@ namespace dlf {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;   // one LDS row of a K slice
+constexpr int kRowBytes = 64;      // bytes of each operand row per K slice
+constexpr int kChunks = 4;         // 16-byte chunks per row slice
+constexpr int kRowsPerLoad = 16;   // one load instruction fills 1 KB = 16 rows
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+// Zero-initialised device memory read by lanes whose chunk is padding.
+__device__ __attribute__((aligned(64))) uint8_t g_zero_page[64];
+
+enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2 };
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct TileShape {
-    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 MFMA fragments per wave
-    static constexpr int AR = BM / 32, BR = BN / 32;     // rows each lane loads per slice
+    static constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 fragments per wave
+    static constexpr int LA = BM / kRowsPerLoad / 4;       // A loads per lane per slice
+    static constexpr int LB = BN / kRowsPerLoad / 4;       // B loads per lane per slice
     static constexpr int STAGE = (BM + BN) * kRowBytes;
     static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 fragments");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
+    static_assert(LA >= 1 && LB >= 1, "each wave loads at least one kilobyte per operand");
+    static_assert(STAGES >= 2, "at least double buffered");
 };
 
-// Byte offset of 16-byte chunk `chunk` of LDS row `row` (XOR swizzle over 8 chunks).
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+// Physical 16-byte chunk of logical chunk c in row r.  Rows are 64 bytes (four
+// chunks); the XOR makes 8 consecutive rows hit 8 distinct 16-byte bank groups
+// of a 128-byte window and 16 consecutive rows 16 distinct groups of a 256-byte
+// window, whichever width the LDS serves per cycle.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + (swz_chunk(r, c) << 4); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 left
+// at its maximum, lgkmcnt 11:8).  Waiting for lgkmcnt(0) as well makes sure this wave's
+// LDS reads of the previous slice are complete before the barrier that lets other waves
+// overwrite it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads() (which
+// would drain every outstanding LDS-DMA load); the asm statement keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Scheduling hint for one pipeline step: alternate its MF MFMAs with the R LDS
+// reads of the next step's fragments and the G global->LDS loads of a future
+// slice, so the matrix pipe never waits on an LDS round trip.
+template <int MF, int R, int G>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        if (i < G) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one VMEM load
+    }
+    if constexpr (R > MF) __builtin_amdgcn_sched_group_barrier(0x100, R - MF, 0);
+    if constexpr (G > MF) __builtin_amdgcn_sched_group_barrier(0x020, G - MF, 0);
+}
+
+// One 16-byte global load per lane straight into LDS: lane i's data lands at
+// lds_wave_base + 16 i (the base must be uniform across the wave).
+__device__ __forceinline__ void load_lds16(const void* g, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
 
 // Maps the linear workgroup id to an output tile.  Consecutive workgroup ids are
@@ -70,11 +130,12 @@ template <int ELEM>
 struct Frag;
 
 template <>
-struct Frag<2> {   // bf16: 16-wide K per MFMA, 8 elements (one chunk) per lane
+struct Frag<2> {   // bf16: 16 K per MFMA; a lane supplies 8 values (one chunk)
     using T = bf16x8_t;
-    static constexpr int kSlices = 4;   // 64 K per 128-byte row
-    static __device__ __forceinline__ T load(const uint8_t* s, int row, int kk, int lane) {
-        return *reinterpret_cast<const T*>(s + swz(row, kk * 2 + (lane >> 5)));
+    static constexpr int kSteps = 2;   // MFMA k-steps per 64-byte slice
+    static constexpr int kReads = 1;   // LDS reads per fragment
+    static __device__ __forceinline__ T load(const uint8_t* s, int row, int step, int lane) {
+        return *reinterpret_cast<const T*>(s + lds_off(row, step * 2 + (lane >> 5)));
     }
     static __device__ __forceinline__ f32x16_t mma(const T& a, const T& b, const f32x16_t& c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -82,31 +143,34 @@ struct Frag<2> {   // bf16: 16-wide K per MFMA, 8 elements (one chunk) per lane
 };
 
 template <>
-struct Frag<1> {   // fp8 e4m3: 64-wide K per MFMA, 32 elements (two chunks) per lane
+struct Frag<1> {   // fp8 e4m3: 64 K per MFMA; a lane supplies 32 values (two chunks)
     using T = i32x8_t;
-    static constexpr int kSlices = 2;   // 128 K per 128-byte row
-    static __device__ __forceinline__ T load(const uint8_t* s, int row, int kk, int lane) {
-        const int c0 = kk * 4 + (lane >> 5) * 2;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(s + swz(row, c0));
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(s + swz(row, c0 + 1));
+    static constexpr int kSteps = 1;
+    static constexpr int kReads = 2;
+    static __device__ __forceinline__ T load(const uint8_t* s, int row, int, int lane) {
+        const int c0 = (lane >> 5) * 2;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(s + lds_off(row, c0));
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(s + lds_off(row, c0 + 1));
         T r;
         r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
         r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
         return r;
     }
     static __device__ __forceinline__ f32x16_t mma(const T& a, const T& b, const f32x16_t& c) {
-        // format 0 = e4m3 for both operands; zero scale operands select the unscaled MFMA
+        // operand format 0 = e4m3 for both; zero scale operands select the unscaled MFMA
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
     }
 };
 
-template <int ELEM, class TS, bool CONV, int ACT, int OUT>
+template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const int tiles_m,
                                                           const int tiles_n) {
-    constexpr int CE = 16 / ELEM;            // elements per 16-byte chunk
-    constexpr int KE = kRowBytes / ELEM;     // K elements per slice
+    constexpr int CE = 16 / ELEM;                 // elements per 16-byte chunk
+    constexpr int KE = kRowBytes / ELEM;          // K elements per slice
+    constexpr int S = TS::STAGES;
+    constexpr int LOADS = TS::LA + TS::LB;        // vmcnt units per slice per lane
     using F = Frag<ELEM>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TS::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * TS::STAGE];
 
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6;
@@ -117,186 +181,332 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
     const int n0 = tn * TS::BN;
     const int64_t M = p.M;
     const int N = p.N, K = p.K;
+    const int KT = (K + KE - 1) / KE;
 
-    // ---- loader state: this lane moves chunk lc of rows lr + 32 i ----
-    const int lc = tid & 7, lr = tid >> 3;
+    // ---- load assignment: wave w fills kilobytes [w*LA, (w+1)*LA) of the A slice and
+    //      [w*LB, ...) of the B slice; lane i writes row 16*kb + i/4, physical chunk i%4 ----
     const uint8_t* const a_bytes = static_cast<const uint8_t*>(p.a);
     const uint8_t* const b_bytes = static_cast<const uint8_t*>(p.b);
     const int64_t row_bytes = static_cast<int64_t>(K) * ELEM;
+    const int prow = lane >> 2, pch = lane & 3;
 
-    uint32_t a_ok = 0, b_ok = 0;          // per-row validity bits
-    int a_pix[CONV ? TS::AR : 1], a_h[CONV ? TS::AR : 1], a_w[CONV ? TS::AR : 1];
+    const uint8_t* a_ptr[TS::LA];     // dense: row base + logical chunk offset
+    int a_lchunk[TS::LA];             // logical chunk of this lane's slot
+    bool a_rowok[TS::LA];
+    int a_pix[AMODE != kDense ? TS::LA : 1], a_h[AMODE != kDense ? TS::LA : 1], a_w[AMODE != kDense ? TS::LA : 1];
 #pragma unroll
-    for (int i = 0; i < TS::AR; ++i) {
-        const int64_t m = m0 + lr + 32 * i;
-        if (m < M) a_ok |= 1u << i;
-        if constexpr (CONV) {
-            const int mm = static_cast<int>(m < M ? m : 0);
+    for (int j = 0; j < TS::LA; ++j) {
+        const int r = (wave * TS::LA + j) * kRowsPerLoad + prow;
+        const int64_t m = m0 + r;
+        a_rowok[j] = m < M;
+        a_lchunk[j] = swz_chunk(r, pch);          // the swizzle is an involution
+        if constexpr (AMODE == kDense) {
+            a_ptr[j] = a_bytes + (a_rowok[j] ? m : 0) * row_bytes + a_lchunk[j] * 16;
+        } else {
+            const int mm = static_cast<int>(a_rowok[j] ? m : 0);
             const int hw = p.Ho * p.Wo;
             const int img = mm / hw, rem = mm - img * hw;
             const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
-            a_h[i] = ho * p.SH - p.PH;
-            a_w[i] = wo * p.SW - p.PW;
-            a_pix[i] = (img * p.H + a_h[i]) * p.W + a_w[i];
+            a_h[j] = ho * p.SH - p.PH;
+            a_w[j] = wo * p.SW - p.PW;
+            a_pix[j] = (img * p.H + a_h[j]) * p.W + a_w[j];
+            a_ptr[j] = a_bytes;
         }
     }
+    const uint8_t* b_ptr[TS::LB];
+    int b_lchunk[TS::LB];
 #pragma unroll
-    for (int i = 0; i < TS::BR; ++i)
-        if (n0 + lr + 32 * i < N) b_ok |= 1u << i;
+    for (int j = 0; j < TS::LB; ++j) {
+        const int r = (wave * TS::LB + j) * kRowsPerLoad + prow;
+        const int n = n0 + r;
+        b_lchunk[j] = swz_chunk(r, pch);
+        b_ptr[j] = (n < N) ? b_bytes + static_cast<int64_t>(n) * row_bytes + b_lchunk[j] * 16 : nullptr;
+    }
 
-    const uint8_t* const a_row0 = a_bytes + (m0 + lr) * row_bytes + lc * 16;
-    const uint8_t* const b_row0 = b_bytes + static_cast<int64_t>(n0 + lr) * row_bytes + lc * 16;
-
-    u32x4_t ra[TS::AR], rb[TS::BR];
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-    auto global_load = [&](int kt) {
-        const int kb = kt * KE + lc * CE;     // first K element of this lane's chunk
-        const bool kin = kb < K;
-        if constexpr (CONV) {
-            int r = 0, s = 0, ci = 0;
-            if (kin) {
-                const int tap = kb / p.Cin;
-                ci = kb - tap * p.Cin;
-                r = tap / p.KW;
-                s = tap - r * p.KW;
-            }
+    const void* const zp = g_zero_page;   // kept in registers across the loop
+    auto issue_slice = [&](int kt) {   // kt may exceed the last slice: then all zero page
+        uint8_t* sA = smem + (kt % S) * TS::STAGE;
+        uint8_t* sB = sA + TS::BM * kRowBytes;
+        const int kbase = kt * KE;
+        if constexpr (AMODE == kConvAligned) {
+            // Cin % KE == 0: the whole slice lies in one kernel tap
+            const bool kin = kbase < K;
+            const int kb = kin ? kbase : 0;
+            const int tap = kb / p.Cin;
+            const int ci0 = kb - tap * p.Cin;
+            const int r = tap / p.KW, s = tap - r * p.KW;
 #pragma unroll
-            for (int i = 0; i < TS::AR; ++i) {
-                const int hi = a_h[i] + r, wi = a_w[i] + s;
-                const bool ok = kin && ((a_ok >> i) & 1u) && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+            for (int j = 0; j < TS::LA; ++j) {
+                const int hi = a_h[j] + r, wi = a_w[j] + s;
+                const bool ok = kin && a_rowok[j] && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
                                 static_cast<unsigned>(wi) < static_cast<unsigned>(p.W);
-                const int64_t off = (static_cast<int64_t>(a_pix[i] + r * p.W + s) * p.Cin + ci) * ELEM;
-                ra[i] = ok ? *reinterpret_cast<const u32x4_t*>(a_bytes + off) : zero;
+                const int64_t off =
+                    (static_cast<int64_t>(a_pix[j] + r * p.W + s) * p.Cin + ci0 + a_lchunk[j] * CE) * ELEM;
+                load_lds16(ok ? static_cast<const void*>(a_bytes + off) : zp,
+                           sA + (wave * TS::LA + j) * 1024);
+            }
+        } else if constexpr (AMODE == kConvGeneric) {
+#pragma unroll
+            for (int j = 0; j < TS::LA; ++j) {
+                const int k = kbase + a_lchunk[j] * CE;
+                const bool kin = k < K;
+                const int kc = kin ? k : 0;                     // division stays branch-free
+                const int tap = kc / p.Cin, ci = kc - tap * p.Cin;
+                const int r = tap / p.KW, s = tap - r * p.KW;
+                const int hi = a_h[j] + r, wi = a_w[j] + s;
+                const bool ok = kin && a_rowok[j] && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                                static_cast<unsigned>(wi) < static_cast<unsigned>(p.W);
+                const int64_t off = (static_cast<int64_t>(a_pix[j] + r * p.W + s) * p.Cin + ci) * ELEM;
+                load_lds16(ok ? static_cast<const void*>(a_bytes + off) : zp,
+                           sA + (wave * TS::LA + j) * 1024);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < TS::AR; ++i) {
-                const bool ok = kin && ((a_ok >> i) & 1u);
-                ra[i] = ok ? *reinterpret_cast<const u32x4_t*>(a_row0 + 32 * i * row_bytes + kt * kRowBytes)
-                           : zero;
+            for (int j = 0; j < TS::LA; ++j) {
+                const bool ok = a_rowok[j] && kbase + a_lchunk[j] * CE < K;
+                load_lds16(ok ? static_cast<const void*>(a_ptr[j] + static_cast<int64_t>(kt) * kRowBytes)
+                              : zp,
+                           sA + (wave * TS::LA + j) * 1024);
             }
         }
 #pragma unroll
-        for (int i = 0; i < TS::BR; ++i) {
-            const bool ok = kin && ((b_ok >> i) & 1u);
-            rb[i] = ok ? *reinterpret_cast<const u32x4_t*>(b_row0 + 32 * i * row_bytes + kt * kRowBytes)
-                       : zero;
+        for (int j = 0; j < TS::LB; ++j) {
+            const bool ok = b_ptr[j] != nullptr && kbase + b_lchunk[j] * CE < K;
+            load_lds16(ok ? static_cast<const void*>(b_ptr[j] + static_cast<int64_t>(kt) * kRowBytes)
+                          : zp,
+                       sB + (wave * TS::LB + j) * 1024);
         }
     };
-    auto lds_store = [&](int stage) {
-        uint8_t* sA = smem + stage * TS::STAGE;
-        uint8_t* sB = sA + TS::BM * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < TS::AR; ++i)
-            *reinterpret_cast<u32x4_t*>(sA + swz(lr + 32 * i, lc)) = ra[i];
-#pragma unroll
-        for (int i = 0; i < TS::BR; ++i)
-            *reinterpret_cast<u32x4_t*>(sB + swz(lr + 32 * i, lc)) = rb[i];
-    };
 
-    f32x16_t acc[TS::FM][TS::FN];
+    f32x16_t acc[TS::FN][TS::FM];     // D = W . X^T: acc[j][i] covers columns of fragment j, rows of i
 #pragma unroll
-    for (int i = 0; i < TS::FM; ++i)
+    for (int j = 0; j < TS::FN; ++j)
+#pragma unroll
+        for (int i = 0; i < TS::FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+    // ---- software pipeline, branch-free in the steady state.  Step g runs FM*FN MFMAs on
+    //      the fragments in register buffer g&1 while the next step's fragments are read
+    //      from LDS into the other buffer.  When the next step starts slice kt+1, this wave
+    //      first waits until its own loads of that slice have landed (the S-1 slices issued
+    //      after it may stay in flight), then a barrier proves that every wave has it and
+    //      that every wave is done reading slice kt, whose LDS buffer is refilled with slice
+    //      kt+S right away.  Slices past the end of K are read from the zero page, so every
+    //      transition issues the same number of loads and the wait count is a constant;
+    //      an fp8 K loop is padded to an even number of (zero) slices for the same reason. ----
+    typename F::T xf[2][TS::FM], wf[2][TS::FN];
+    const int x_row = wm * TS::WTM + (lane & 31);   // activation fragment rows in the tile
+    const int w_row = wn * TS::WTN + (lane & 31);   // weight fragment rows in the tile
+    const int KTP = F::kSteps == 1 ? (KT + 1) & ~1 : KT;   // slices walked (even step count)
+    const int steps = KTP * F::kSteps;
+    auto stage_a = [&](int kt) -> const uint8_t* { return smem + (kt % S) * TS::STAGE; };
+    auto read_frags = [&](auto buf_c, int kt, int st) {
+        constexpr int b = decltype(buf_c)::value;
+        const uint8_t* sA = stage_a(kt);
+#pragma unroll
+        for (int i = 0; i < TS::FM; ++i) xf[b][i] = F::load(sA, x_row + 32 * i, st, lane);
+#pragma unroll
+        for (int j = 0; j < TS::FN; ++j) wf[b][j] = F::load(sA + TS::BM * kRowBytes, w_row + 32 * j, st, lane);
+    };
+    auto mma_all = [&](auto buf_c) {
+        constexpr int b = decltype(buf_c)::value;
 #pragma unroll
         for (int j = 0; j < TS::FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int i = 0; i < TS::FM; ++i) acc[j][i] = F::mma(wf[b][j], xf[b][i], acc[j][i]);
+    };
+    constexpr int MF = TS::FM * TS::FN, R = (TS::FM + TS::FN) * F::kReads;
 
-    const int KT = (K + KE - 1) / KE;
-    if (KT > 0) {
-        global_load(0);
-        lds_store(0);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) issue_slice(s2);
+    wait_vmcnt<(S - 1) * LOADS>();
+    barrier();
+    read_frags(std::integral_constant<int, 0>{}, 0, 0);
 
-    const int a_frag_row = wm * TS::WTM + (lane & 31);
-    const int b_frag_row = wn * TS::WTN + (lane & 31);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) global_load(kt + 1);
-        const uint8_t* sA = smem + cur * TS::STAGE;
-        const uint8_t* sB = sA + TS::BM * kRowBytes;
-#pragma unroll
-        for (int kk = 0; kk < F::kSlices; ++kk) {
-            typename F::T af[TS::FM], bfr[TS::FN];
-#pragma unroll
-            for (int i = 0; i < TS::FM; ++i) af[i] = F::load(sA, a_frag_row + 32 * i, kk, lane);
-#pragma unroll
-            for (int j = 0; j < TS::FN; ++j) bfr[j] = F::load(sB, b_frag_row + 32 * j, kk, lane);
-#pragma unroll
-            for (int i = 0; i < TS::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < TS::FN; ++j) acc[i][j] = F::mma(af[i], bfr[j], acc[i][j]);
+    // one pipeline step; C is the register buffer holding this step's fragments
+    auto step = [&](auto cur_c, int g) {
+        constexpr int c = decltype(cur_c)::value;
+        const int kt = g / F::kSteps, st = g - kt * F::kSteps;
+        if (F::kSteps == 2 && st == 0) {
+            // next step is in the same slice: no synchronisation needed
+            read_frags(std::integral_constant<int, c ^ 1>{}, kt, 1);
+            mma_all(cur_c);
+            interleave<MF, R, 0>();
+        } else {
+            wait_vmcnt<(S - 2) * LOADS>();
+            barrier();
+            issue_slice(kt + S);
+            read_frags(std::integral_constant<int, c ^ 1>{}, kt + 1, 0);
+            mma_all(cur_c);
+            interleave<MF, R, LOADS>();
         }
-        if (kt + 1 < KT) lds_store(cur ^ 1);
-        __syncthreads();
+    };
+    for (int g = 0; g < steps; g += 2) {
+        step(std::integral_constant<int, 0>{}, g);
+        step(std::integral_constant<int, 1>{}, g + 1);
     }
 
-    // ---- register epilogue: lane holds column (lane & 31) and 16 rows per fragment:
-    //      row = 8*(e/4) + 4*(lane/32) + e%4 within the 32x32 fragment ----
-    const float* const scale = p.scale;
-    const float* const shift = p.shift;
+    // ---- epilogue.  Lane holds output row  m = m0 + wm*WTM + 32 i + (lane & 31)  and, in
+    //      register group g = e/4, columns  n = n0 + wn*WTN + 32 j + 8 g + 4 (lane/32) + e%4 ----
+    const int lrow = lane & 31, half = lane >> 5;
+    if constexpr (OUT == kOutF32) {
+        // fp32 result of the plain fp8 GEMM: acc * dequant, stored directly (16 B per lane-group)
 #pragma unroll
-    for (int j = 0; j < TS::FN; ++j) {
-        const int col = n0 + wn * TS::WTN + 32 * j + (lane & 31);
-        const bool col_ok = col < N;
-        float sc = 1.0f, sh = 0.0f;
-        if (col_ok) {
-            if (scale) sc = scale[col];
-            if (shift) sh = shift[col];
-        }
+        for (int j = 0; j < TS::FN; ++j)
 #pragma unroll
-        for (int i = 0; i < TS::FM; ++i) {
-            const int64_t rbase = m0 + wm * TS::WTM + 32 * i + 4 * (lane >> 5);
+            for (int i = 0; i < TS::FM; ++i) {
+                const int64_t m = m0 + wm * TS::WTM + 32 * i + lrow;
+                if (m >= M) continue;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = rbase + 8 * (e >> 2) + (e & 3);
-                if (!col_ok || row >= M) continue;
-                const int64_t idx = row * N + col;
-                float v = acc[i][j][e];
-                if constexpr (OUT == kOutF32) {
-                    static_cast<float*>(p.c)[idx] = v * p.dequant;
-                } else {
-                    v = scale ? fmaf(v, sc, sh) : v + sh;
-                    if (p.res) v += bf16_to_f32(p.res[idx]);
-                    v = activate<ACT>(v);
-                    if constexpr (OUT == kOutFp8)
-                        static_cast<uint8_t*>(p.c)[idx] = static_cast<uint8_t>(quant_e4m3(v, p.out_inv_scale));
-                    else
-                        static_cast<uint16_t*>(p.c)[idx] = f32_to_bf16(v);
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * TS::WTN + 32 * j + 8 * g + 4 * half;
+                    float* dst = static_cast<float*>(p.c) + m * N + n;
+                    if (n + 3 < N && (N & 3) == 0) {
+                        f32x4_t v;
+                        for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e] * p.dequant;
+                        *reinterpret_cast<f32x4_t*>(dst) = v;
+                    } else {
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) dst[e] = acc[j][i][4 * g + e] * p.dequant;
+                    }
                 }
+            }
+        return;
+    } else {
+        constexpr int OB = OUT == kOutFp8 ? 1 : 2;            // output bytes per element
+        constexpr int SROW = TS::BN * OB;                     // staging row bytes
+        static_assert(TS::BM * SROW <= S * TS::STAGE, "output tile fits the LDS ring");
+        __syncthreads();   // all waves are done reading operand slices: the LDS is reused for staging
+        const float* const scale = p.scale;
+        const float* const shift = p.shift;
+        const int64_t m_last = M - 1;
+        const int n_last4 = N >= 4 ? N - 4 : 0;
+#pragma unroll
+        for (int j = 0; j < TS::FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * TS::WTN + 32 * j + 8 * g + 4 * half;   // first of 4 columns
+                const int n = n0 + nl;
+                // per-column parameters; columns past N read a clamped (valid) address and
+                // their results are never written out
+                float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if ((N & 3) == 0) {   // n % 4 == 0: the run of four is entirely in or past N
+                    const int nc = min(n, n_last4);
+                    if (scale) {
+                        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(scale + nc);
+                        sc[0] = t[0]; sc[1] = t[1]; sc[2] = t[2]; sc[3] = t[3];
+                    }
+                    if (shift) {
+                        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(shift + nc);
+                        sh[0] = t[0]; sh[1] = t[1]; sh[2] = t[2]; sh[3] = t[3];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int nc = min(n + e, N - 1);
+                        if (scale) sc[e] = scale[nc];
+                        if (shift) sh[e] = shift[nc];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < TS::FM; ++i) {
+                    const int ml = wm * TS::WTM + 32 * i + lrow;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = acc[j][i][4 * g + e];
+                        v[e] = scale ? fmaf(t, sc[e], sh[e]) : t + sh[e];
+                    }
+                    if (p.res != nullptr) {
+                        const int64_t mc = min(m0 + ml, m_last);
+                        if ((N & 3) == 0) {   // 8-byte aligned run of four
+                            const uint2 t = *reinterpret_cast<const uint2*>(p.res + mc * N + min(n, n_last4));
+                            v[0] += __uint_as_float(t.x << 16);
+                            v[1] += __uint_as_float(t.x & 0xFFFF0000u);
+                            v[2] += __uint_as_float(t.y << 16);
+                            v[3] += __uint_as_float(t.y & 0xFFFF0000u);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.res[mc * N + min(n + e, N - 1)]);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                    uint8_t* dst = smem + ml * SROW + nl * OB;
+                    if constexpr (OUT == kOutFp8) {
+                        *reinterpret_cast<uint32_t*>(dst) = quant_e4m3_x4(v[0], v[1], v[2], v[3], p.out_inv_scale);
+                    } else {
+                        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                                            (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+                                            (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // coalesced write-out: 16-byte chunks of the staged tile, row-major
+        constexpr int CPR = SROW / 16;                        // chunks per staged row
+        const bool vec_ok = ((static_cast<int64_t>(N) * OB) & 15) == 0;
+        uint8_t* const cbytes = static_cast<uint8_t*>(p.c);
+        for (int q = tid; q < TS::BM * CPR; q += kThreads) {
+            const int ml = q / CPR, cc = q - ml * CPR;
+            const int64_t m = m0 + ml;
+            const int nl = cc * (16 / OB);
+            const int n = n0 + nl;
+            if (m >= M || n >= N) continue;
+            const uint8_t* src = smem + ml * SROW + cc * 16;
+            uint8_t* dst = cbytes + (m * N + n) * OB;
+            if (vec_ok && n + 16 / OB <= N) {
+                *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+            } else {
+                const int cnt = min(16 / OB, N - n) * OB;
+                for (int b = 0; b < cnt; ++b) dst[b] = src[b];
             }
         }
     }
 }
 
-using T256x256 = TileShape<256, 256, 2, 2>;
-using T128x128 = TileShape<128, 128, 2, 2>;
-using T256x64 = TileShape<256, 64, 4, 1>;
-using T64x64 = TileShape<64, 64, 2, 2>;
-using T128x64 = TileShape<128, 64, 2, 2>;
+using T256x256 = TileShape<256, 256, 2, 2, 4>;
+using T256x128 = TileShape<256, 128, 2, 2, 4>;
+using T128x128 = TileShape<128, 128, 2, 2, 4>;
+using T256x64 = TileShape<256, 64, 4, 1, 4>;
+using T128x64 = TileShape<128, 64, 2, 2, 4>;
+using T64x64 = TileShape<64, 64, 2, 2, 4>;
 
-template <int ELEM, class TS, bool CONV, int ACT, int OUT>
+template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 hipError_t launch_one(const MmaArgs& a, hipStream_t stream) {
     const int64_t tm64 = (a.M + TS::BM - 1) / TS::BM;
     const int tiles_n = (a.N + TS::BN - 1) / TS::BN;
     if (tm64 * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
     const int tiles_m = static_cast<int>(tm64);
     if (tiles_m == 0 || tiles_n == 0) return hipSuccess;
-    hipLaunchKernelGGL((mma_kernel<ELEM, TS, CONV, ACT, OUT>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
+    hipLaunchKernelGGL((mma_kernel<ELEM, TS, AMODE, ACT, OUT>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
                        stream, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-template <int ELEM, bool CONV, int ACT, int OUT>
+template <int ELEM, int AMODE, int ACT, int OUT>
 hipError_t launch_tile(const MmaArgs& a, int tile, hipStream_t s) {
     switch (tile) {
-        case kTile256x256: return launch_one<ELEM, T256x256, CONV, ACT, OUT>(a, s);
-        case kTile128x128: return launch_one<ELEM, T128x128, CONV, ACT, OUT>(a, s);
-        case kTile256x64: return launch_one<ELEM, T256x64, CONV, ACT, OUT>(a, s);
-        case kTile64x64: return launch_one<ELEM, T64x64, CONV, ACT, OUT>(a, s);
-        case kTile128x64: return launch_one<ELEM, T128x64, CONV, ACT, OUT>(a, s);
+        case kTile256x256: return launch_one<ELEM, T256x256, AMODE, ACT, OUT>(a, s);
+        case kTile256x128: return launch_one<ELEM, T256x128, AMODE, ACT, OUT>(a, s);
+        case kTile128x128: return launch_one<ELEM, T128x128, AMODE, ACT, OUT>(a, s);
+        case kTile256x64: return launch_one<ELEM, T256x64, AMODE, ACT, OUT>(a, s);
+        case kTile128x64: return launch_one<ELEM, T128x64, AMODE, ACT, OUT>(a, s);
+        case kTile64x64: return launch_one<ELEM, T64x64, AMODE, ACT, OUT>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int AMODE>
+hipError_t launch_bf16_act(const MmaArgs& a, int act, int tile, hipStream_t s) {
+    switch (act) {
+        case kActNone: return launch_tile<2, AMODE, kActNone, kOutBf16>(a, tile, s);
+        case kActRelu: return launch_tile<2, AMODE, kActRelu, kOutBf16>(a, tile, s);
+        case kActGelu: return launch_tile<2, AMODE, kActGelu, kOutBf16>(a, tile, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -305,7 +515,7 @@ hipError_t launch_tile(const MmaArgs& a, int tile, hipStream_t s) {
 
 int mma_tile_rows(int tile) {
     switch (tile) {
-        case kTile256x256: case kTile256x64: return 256;
+        case kTile256x256: case kTile256x128: case kTile256x64: return 256;
         case kTile128x128: case kTile128x64: return 128;
         case kTile64x64: return 64;
         default: return 0;
@@ -315,38 +525,28 @@ int mma_tile_rows(int tile) {
 int mma_tile_cols(int tile) {
     switch (tile) {
         case kTile256x256: return 256;
-        case kTile128x128: return 128;
+        case kTile256x128: case kTile128x128: return 128;
         default: return 64;
     }
 }
 
 hipError_t launch_mma_bf16(const MmaArgs& a, bool conv, int act, int tile, hipStream_t s) {
-    if (conv) {
-        switch (act) {
-            case kActNone: return launch_tile<2, true, kActNone, kOutBf16>(a, tile, s);
-            case kActRelu: return launch_tile<2, true, kActRelu, kOutBf16>(a, tile, s);
-            case kActGelu: return launch_tile<2, true, kActGelu, kOutBf16>(a, tile, s);
-        }
-    } else {
-        switch (act) {
-            case kActNone: return launch_tile<2, false, kActNone, kOutBf16>(a, tile, s);
-            case kActRelu: return launch_tile<2, false, kActRelu, kOutBf16>(a, tile, s);
-            case kActGelu: return launch_tile<2, false, kActGelu, kOutBf16>(a, tile, s);
-        }
-    }
-    return hipErrorInvalidValue;
+    if (!conv) return launch_bf16_act<kDense>(a, act, tile, s);
+    // a 64-byte slice (32 bf16) stays inside one kernel tap when Cin % 32 == 0
+    if (a.Cin % 32 == 0) return launch_bf16_act<kConvAligned>(a, act, tile, s);
+    return launch_bf16_act<kConvGeneric>(a, act, tile, s);
 }
 
 hipError_t launch_mma_fp8(const MmaArgs& a, int act, int out, int tile, hipStream_t s) {
-    if (out == kOutF32) return act == kActNone ? launch_tile<1, false, kActNone, kOutF32>(a, tile, s)
+    if (out == kOutF32) return act == kActNone ? launch_tile<1, kDense, kActNone, kOutF32>(a, tile, s)
                                                : hipErrorInvalidValue;
     if (out == kOutFp8) {
-        if (act == kActNone) return launch_tile<1, false, kActNone, kOutFp8>(a, tile, s);
-        if (act == kActRelu) return launch_tile<1, false, kActRelu, kOutFp8>(a, tile, s);
+        if (act == kActNone) return launch_tile<1, kDense, kActNone, kOutFp8>(a, tile, s);
+        if (act == kActRelu) return launch_tile<1, kDense, kActRelu, kOutFp8>(a, tile, s);
     }
     if (out == kOutBf16) {
-        if (act == kActNone) return launch_tile<1, false, kActNone, kOutBf16>(a, tile, s);
-        if (act == kActRelu) return launch_tile<1, false, kActRelu, kOutBf16>(a, tile, s);
+        if (act == kActNone) return launch_tile<1, kDense, kActNone, kOutBf16>(a, tile, s);
+        if (act == kActRelu) return launch_tile<1, kDense, kActRelu, kOutBf16>(a, tile, s);
     }
     return hipErrorInvalidValue;
 }

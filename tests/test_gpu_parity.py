@@ -135,7 +135,7 @@ RAGGED_BF16 = [
 @pytest.mark.parametrize("i", range(len(RAGGED_BF16)))
 def test_bf16_conv_ragged_shapes_every_tile(i):
     wl = workloads.workload(1, conv_bias=bool(i % 2), **RAGGED_BF16[i])
-    check_conv(wl, tiles=(None, 0, 1, 2, 3, 4), unfused=(i < 3))
+    check_conv(wl, tiles=(None, 0, 1, 2, 3, 4, 5), unfused=(i < 3))
 
 
 RAGGED_F32 = [
@@ -225,7 +225,7 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
     ref = gemm_reference(inp, rows, res)
     L = layers().make_layer(inp)
     res_d = layers().to_device(res, "bf16") if res is not None else None
-    for tile in (None, 0, 1, 2, 3, 4):
+    for tile in (None, 0, 1, 2, 3, 4, 5):
         if tile is None:
             os.environ.pop("DLF_TILE", None)
         else:
@@ -297,7 +297,7 @@ def test_fp8_gemm_ragged_shapes_every_tile(i):
     rows = np.arange(wl.m)
     ref, u = fp8_reference(inp, rows)
     L = layers().make_layer(inp)
-    for tile in (None, 0, 1, 2, 3, 4):
+    for tile in (None, 0, 1, 2, 3, 4, 5):
         if tile is None:
             os.environ.pop("DLF_TILE", None)
         else:
