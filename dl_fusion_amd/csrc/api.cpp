@@ -56,7 +56,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<0..5> forces one
+// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<0..15> forces one
 // (tuning only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x
 // (tile area / relative MFMA efficiency of the tile shape).
 int pick_tile(int64_t M, int64_t N) {

@@ -1,109 +1,78 @@
 // fp32 direct convolution with the register epilogue (bias -> residual -> act).
 //
-// Used for fp32 layers (small, latency-bound shapes).  A workgroup computes a
-// tile of 64 output pixels x TC output channels.  The K dimension
-// (k = (r*KW + s)*Cin + ci) is walked in slices of 64: each slice of the
-// weights is staged in LDS transposed to [k][channel] (consecutive lanes read
-// consecutive channels), and the matching im2col slice of the input (64 pixels
-// x 64 k, zero outside the image) is staged as [pixel][k] and read as a
-// broadcast.  Each lane accumulates 64*TC/256 outputs in fp32 and applies the
-// epilogue of "OpenPPL算子融合深度解析" §4.3 before its single store.
+// Used for fp32 layers (small, latency-bound shapes).  Each lane computes one
+// output element (pixel m, channel co); a workgroup covers 256/TC pixels x TC
+// channels, so even a 32x32x32 layer spreads over 128 workgroups.  The
+// workgroup's weights are staged in LDS transposed to [k][channel] in slices of
+// 4096 values (consecutive lanes read consecutive channels), together with the
+// im2col rows of its pixels (zero outside the image), each gathered by
+// independent loads so that a slice costs one memory round trip.  fp32
+// accumulation, then the epilogue of "OpenPPL算子融合深度解析" §4.3 before the
+// single store.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace dlf {
 namespace {
 
-constexpr int kPix = 64;     // output pixels per workgroup
-constexpr int kKs = 64;      // K slice
-
 template <int TC, int ACT>
 __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
-    constexpr int PG = 256 / TC;            // pixel groups
-    constexpr int PPT = kPix / PG;          // output pixels per lane
-    constexpr int XS = kPix * kKs / 256;    // im2col entries each lane stages per slice
-    __shared__ float ws[kKs][TC + 1];
-    __shared__ float xs[kPix][kKs + 1];
+    constexpr int PPB = 256 / TC;         // pixels per workgroup
+    constexpr int KS = 4096 / TC;         // K values per slice (16 KB of weights in LDS)
+    __shared__ float ws[KS][TC];
+    __shared__ float xs[PPB][KS + 1];
 
     const int tid = static_cast<int>(threadIdx.x);
-    const int co_l = tid % TC, pg = tid / TC;
-    const int p0 = static_cast<int>(blockIdx.x) * kPix;   // M <= 2^30 (checked on the host)
+    const int co_l = tid % TC, pl = tid / TC;
+    const int m0 = static_cast<int>(blockIdx.x) * PPB;   // M <= 2^30 (checked on the host)
     const int c0 = static_cast<int>(blockIdx.y) * TC;
     const int co = c0 + co_l;
-
-    // staging assignment: this lane stages column kq of the slice for pixels kp + 4 i
-    const int kq = tid & (kKs - 1), kp = tid >> 6;
-    int px_base[XS], px_h[XS], px_w[XS];
     const int hw = p.Ho * p.Wo;
-#pragma unroll
-    for (int i = 0; i < XS; ++i) {
-        const int m = p0 + kp + 4 * i;
-        const int mm = m < p.M ? m : 0;
-        const int img = mm / hw, rem = mm - img * hw;
-        const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
-        const int h0 = ho * p.SH - p.PH;
-        px_w[i] = wo * p.SW - p.PW;
-        px_base[i] = (img * p.H + h0) * p.W + px_w[i];
-        px_h[i] = m < p.M ? h0 : -(1 << 29);   // rows past M never pass the bounds test
-    }
 
-    float acc[PPT];
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) acc[j] = 0.0f;
-
-    for (int k0 = 0; k0 < p.K; k0 += kKs) {
-        const int gk = k0 + kq;
-        const bool k_ok = gk < p.K;
-        // weights slice -> ws[k][channel]
-#pragma unroll
-        for (int i = 0; i < kKs * TC / 256; ++i) {
-            const int c = kp + 4 * i;
-            const int gc = c0 + c;
-            ws[kq][c] = (gc < p.Cout && k_ok) ? p.w[static_cast<int64_t>(gc) * p.K + gk] : 0.0f;
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < p.K; k0 += KS) {
+        // weights slice -> ws[k][channel]; consecutive lanes read consecutive k
+        for (int e = tid; e < KS * TC; e += 256) {
+            const int c = e / KS, kk = e - c * KS;
+            const int gc = c0 + c, gk = k0 + kk;
+            ws[kk][c] = (gc < p.Cout && gk < p.K) ? p.w[static_cast<int64_t>(gc) * p.K + gk] : 0.0f;
         }
-        // im2col slice -> xs[pixel][k]: one (tap, ci) decomposition per lane per slice
-        int r = 0, s = 0, ci = 0;
-        if (k_ok) {
-            const int tap = gk / p.Cin;
-            ci = gk - tap * p.Cin;
-            r = tap / p.KW;
-            s = tap - r * p.KW;
-        }
-#pragma unroll
-        for (int i = 0; i < XS; ++i) {
-            const int hi = px_h[i] + r, wi = px_w[i] + s;
+        // im2col rows of this workgroup's pixels -> xs[pixel][k]; every load is independent
+        for (int e = tid; e < PPB * KS; e += 256) {
+            const int q = e / KS, kk = e - q * KS;
+            const int m = m0 + q, gk = k0 + kk;
             float v = 0.0f;
-            if (k_ok && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
-                static_cast<unsigned>(wi) < static_cast<unsigned>(p.W))
-                v = p.x[static_cast<int64_t>(px_base[i] + r * p.W + s) * p.Cin + ci];
-            xs[kp + 4 * i][kq] = v;
+            if (m < p.M && gk < p.K) {
+                const int img = m / hw, rem = m - img * hw;
+                const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
+                const int tap = gk / p.Cin, ci = gk - tap * p.Cin;
+                const int r = tap / p.KW, s = tap - r * p.KW;
+                const int hi = ho * p.SH - p.PH + r, wi = wo * p.SW - p.PW + s;
+                if (static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                    static_cast<unsigned>(wi) < static_cast<unsigned>(p.W))
+                    v = p.x[((static_cast<int64_t>(img) * p.H + hi) * p.W + wi) * p.Cin + ci];
+            }
+            xs[q][kk] = v;
         }
         __syncthreads();
-        const int kn = min(kKs, p.K - k0);
-        for (int k = 0; k < kn; ++k) {
-            const float wv = ws[k][co_l];
-#pragma unroll
-            for (int j = 0; j < PPT; ++j) acc[j] = fmaf(xs[pg + PG * j][k], wv, acc[j]);
-        }
+        const int kn = min(KS, p.K - k0);
+#pragma unroll 8
+        for (int kk = 0; kk < kn; ++kk) acc = fmaf(xs[pl][kk], ws[kk][co_l], acc);
         __syncthreads();
     }
 
-    if (co >= p.Cout) return;
-    const float b = p.bias ? p.bias[co] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-        const int m = p0 + pg + PG * j;
-        if (m >= p.M) continue;
-        const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
-        float v = acc[j] + b;
-        if (p.res) v += p.res[idx];
-        p.y[idx] = activate<ACT>(v);
-    }
+    const int m = m0 + pl;
+    if (m >= p.M || co >= p.Cout) return;
+    const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
+    float v = acc + (p.bias ? p.bias[co] : 0.0f);
+    if (p.res) v += p.res[idx];
+    p.y[idx] = activate<ACT>(v);
 }
 
 template <int TC>
 hipError_t launch_tc(const ConvF32Args& a, int act, hipStream_t s) {
-    const int64_t gx = (a.M + kPix - 1) / kPix;
+    constexpr int PPB = 256 / TC;
+    const int64_t gx = (a.M + PPB - 1) / PPB;
     const int gy = (a.Cout + TC - 1) / TC;
     if (gx == 0 || gy == 0) return hipSuccess;
     if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;

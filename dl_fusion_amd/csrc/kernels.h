@@ -33,7 +33,18 @@ enum MmaTile : int {
     kTile64x64 = 3,     // 2x2 waves of 32x32
     kTile128x64 = 4,    // 2x2 waves of 64x32
     kTile256x128 = 5,   // 2x2 waves of 128x64
-    kTileCount = 6
+    // dense-GEMM variants for tuning: eight waves (two per SIMD) or three stages
+    kTile256x256w8 = 6,   // 2x4 waves of 128x64
+    kTile256x256w8t = 7,  // 4x2 waves of 64x128
+    kTile256x256s3 = 8,   // 2x2 waves of 128x128, three stages
+    kTile256x128s3 = 9,   // 2x2 waves of 128x64, three stages
+    kTile256x128w8 = 10,  // 4x2 waves of 64x64
+    kTile256x256w8b2 = 11,   // 4x2 waves of 64x128, one barrier per two K slices
+    kTile256x256w8ab2 = 12,  // 2x4 waves of 128x64, one barrier per two K slices
+    kTile256x256w8s5 = 13,   // 4x2 waves of 64x128, five stages
+    kTile256x256w8r = 14,    // 4x2 waves of 64x128, operands staged through registers
+    kTile256x256w8ar = 15,   // 2x4 waves of 128x64, operands staged through registers
+    kTileCount = 23   // 16..22: schedule variants of the eight-wave tiles (tuning)
 };
 int mma_tile_rows(int tile);
 int mma_tile_cols(int tile);

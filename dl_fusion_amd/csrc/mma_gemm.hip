@@ -35,7 +35,6 @@
 namespace dlf {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kRowBytes = 64;      // bytes of each operand row per K slice
 constexpr int kChunks = 4;         // 16-byte chunks per row slice
 constexpr int kRowsPerLoad = 16;   // one load instruction fills 1 KB = 16 rows
@@ -45,25 +44,38 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64];
 
 enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2 };
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1, bool REG_ = false,
+          int SCHED_ = 0>
 struct TileShape {
+    // SCHED 0: MFMAs interleaved one by one with LDS reads / loads; 1: compiler's own
+    // order; 2: loads and reads first, then the MFMA cluster; 3: as 0 with the wave's
+    // priority raised while it issues MFMAs
+    static constexpr int SCHED = SCHED_;
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+    static constexpr int SPB = SPB_;                       // K slices consumed per barrier
+    // REG: operand slices travel global -> registers -> LDS (global_load_dwordx4 +
+    // ds_write_b128) instead of the LDS-DMA path; the LDS image is identical
+    static constexpr bool REG = REG_;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 fragments per wave
-    static constexpr int LA = BM / kRowsPerLoad / 4;       // A loads per lane per slice
-    static constexpr int LB = BN / kRowsPerLoad / 4;       // B loads per lane per slice
+    static constexpr int NW = WAVES_M * WAVES_N;           // waves per workgroup
+    static constexpr int NT = 64 * NW;                     // lanes per workgroup
+    static constexpr int LA = BM / kRowsPerLoad / NW;      // A loads per lane per slice
+    static constexpr int LB = BN / kRowsPerLoad / NW;      // B loads per lane per slice
     static constexpr int STAGE = (BM + BN) * kRowBytes;
-    static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+    static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup (one or two per SIMD)");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
     static_assert(LA >= 1 && LB >= 1, "each wave loads at least one kilobyte per operand");
-    static_assert(STAGES >= 2, "at least double buffered");
+    static_assert(STAGES >= 2 * SPB, "the ring holds the slices being read and the ones landing");
+    static_assert(!REG || (STAGES == 3 && SPB == 1), "register path: three LDS stages, one slice per barrier");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r.  Rows are 64 bytes (four
-// chunks); the XOR makes 8 consecutive rows hit 8 distinct 16-byte bank groups
-// of a 128-byte window and 16 consecutive rows 16 distinct groups of a 256-byte
-// window, whichever width the LDS serves per cycle.
-__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+// chunks), so rows r, r+4, r+8, r+12 start in the same bank group; XOR-ing the
+// chunk with bits 2..3 of the row spreads the 16 rows that one fragment read
+// serves per cycle over 16 distinct 16-byte bank groups (measured on gfx950 with
+// SQ_LDS_BANK_CONFLICT: zero conflict cycles for both MFMA k-steps).
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + (swz_chunk(r, c) << 4); }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 left
@@ -87,14 +99,16 @@ __device__ __forceinline__ void barrier() {
 // Scheduling hint for one pipeline step: alternate its MF MFMAs with the R LDS
 // reads of the next step's fragments and the G global->LDS loads of a future
 // slice, so the matrix pipe never waits on an LDS round trip.
-template <int MF, int R, int G>
+template <int MF, int R, int G, int W = 0>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        if (i < W) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
         if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
         if (i < G) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one VMEM load
     }
+    if constexpr (W > MF) __builtin_amdgcn_sched_group_barrier(0x200, W - MF, 0);
     if constexpr (R > MF) __builtin_amdgcn_sched_group_barrier(0x100, R - MF, 0);
     if constexpr (G > MF) __builtin_amdgcn_sched_group_barrier(0x020, G - MF, 0);
 }
@@ -163,14 +177,17 @@ struct Frag<1> {   // fp8 e4m3: 64 K per MFMA; a lane supplies 32 values (two ch
 };
 
 template <int ELEM, class TS, int AMODE, int ACT, int OUT>
-__global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const int tiles_m,
+__global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const int tiles_m,
                                                           const int tiles_n) {
     constexpr int CE = 16 / ELEM;                 // elements per 16-byte chunk
     constexpr int KE = kRowBytes / ELEM;          // K elements per slice
     constexpr int S = TS::STAGES;
     constexpr int LOADS = TS::LA + TS::LB;        // vmcnt units per slice per lane
     using F = Frag<ELEM>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * TS::STAGE];
+    // the LDS holds the operand ring during the K loop and the rounded output tile after it
+    constexpr int STAGED = OUT == kOutF32 ? 0 : TS::BM * TS::BN * (OUT == kOutFp8 ? 1 : 2);
+    constexpr int SMEM = S * TS::STAGE > STAGED ? S * TS::STAGE : STAGED;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6;
@@ -224,7 +241,11 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
     }
 
     const void* const zp = g_zero_page;   // kept in registers across the loop
-    auto issue_slice = [&](int kt) {   // kt may exceed the last slice: then all zero page
+    // register staging for the REG path: two sets of this lane's 16-byte pieces of a slice
+    u32x4_t rv[TS::REG ? 2 : 1][TS::LA + TS::LB];
+    // Issues this lane's loads of slice kt (kt may exceed the last slice: then all zero
+    // page).  sink(j, src, lds_dst) receives load slot j (A slots first, then B).
+    auto gen_slice = [&](int kt, auto sink) {
         uint8_t* sA = smem + (kt % S) * TS::STAGE;
         uint8_t* sB = sA + TS::BM * kRowBytes;
         const int kbase = kt * KE;
@@ -242,8 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
                                 static_cast<unsigned>(wi) < static_cast<unsigned>(p.W);
                 const int64_t off =
                     (static_cast<int64_t>(a_pix[j] + r * p.W + s) * p.Cin + ci0 + a_lchunk[j] * CE) * ELEM;
-                load_lds16(ok ? static_cast<const void*>(a_bytes + off) : zp,
-                           sA + (wave * TS::LA + j) * 1024);
+                sink(j, ok ? static_cast<const void*>(a_bytes + off) : zp, sA + (wave * TS::LA + j) * 1024);
             }
         } else if constexpr (AMODE == kConvGeneric) {
 #pragma unroll
@@ -257,25 +277,45 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
                 const bool ok = kin && a_rowok[j] && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
                                 static_cast<unsigned>(wi) < static_cast<unsigned>(p.W);
                 const int64_t off = (static_cast<int64_t>(a_pix[j] + r * p.W + s) * p.Cin + ci) * ELEM;
-                load_lds16(ok ? static_cast<const void*>(a_bytes + off) : zp,
-                           sA + (wave * TS::LA + j) * 1024);
+                sink(j, ok ? static_cast<const void*>(a_bytes + off) : zp, sA + (wave * TS::LA + j) * 1024);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < TS::LA; ++j) {
                 const bool ok = a_rowok[j] && kbase + a_lchunk[j] * CE < K;
-                load_lds16(ok ? static_cast<const void*>(a_ptr[j] + static_cast<int64_t>(kt) * kRowBytes)
-                              : zp,
-                           sA + (wave * TS::LA + j) * 1024);
+                sink(j, ok ? static_cast<const void*>(a_ptr[j] + static_cast<int64_t>(kt) * kRowBytes) : zp,
+                     sA + (wave * TS::LA + j) * 1024);
             }
         }
 #pragma unroll
         for (int j = 0; j < TS::LB; ++j) {
             const bool ok = b_ptr[j] != nullptr && kbase + b_lchunk[j] * CE < K;
-            load_lds16(ok ? static_cast<const void*>(b_ptr[j] + static_cast<int64_t>(kt) * kRowBytes)
-                          : zp,
-                       sB + (wave * TS::LB + j) * 1024);
+            sink(TS::LA + j, ok ? static_cast<const void*>(b_ptr[j] + static_cast<int64_t>(kt) * kRowBytes) : zp,
+                 sB + (wave * TS::LB + j) * 1024);
         }
+    };
+    // LDS-DMA path: every load lands in LDS directly
+    auto issue_slice = [&](int kt) {
+        gen_slice(kt, [&](int, const void* src, uint8_t* dst) { load_lds16(src, dst); });
+    };
+    // register path: loads into register set `set`; the later LDS write puts lane i's piece
+    // at dst + 16 i, the position the LDS-DMA path would have used
+    auto load_slice = [&](auto set_c, int kt) {
+        constexpr int set = decltype(set_c)::value;
+        gen_slice(kt, [&](int j, const void* src, uint8_t*) {
+            rv[set][j] = *static_cast<const u32x4_t*>(src);
+        });
+    };
+    auto write_slice = [&](auto set_c, int kt) {
+        constexpr int set = decltype(set_c)::value;
+        uint8_t* sA = smem + (kt % S) * TS::STAGE;
+        uint8_t* sB = sA + TS::BM * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < TS::LA; ++j)
+            *reinterpret_cast<u32x4_t*>(sA + (wave * TS::LA + j) * 1024 + lane * 16) = rv[set][j];
+#pragma unroll
+        for (int j = 0; j < TS::LB; ++j)
+            *reinterpret_cast<u32x4_t*>(sB + (wave * TS::LB + j) * 1024 + lane * 16) = rv[set][TS::LA + j];
     };
 
     f32x16_t acc[TS::FN][TS::FM];     // D = W . X^T: acc[j][i] covers columns of fragment j, rows of i
@@ -286,19 +326,26 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
 
-    // ---- software pipeline, branch-free in the steady state.  Step g runs FM*FN MFMAs on
-    //      the fragments in register buffer g&1 while the next step's fragments are read
-    //      from LDS into the other buffer.  When the next step starts slice kt+1, this wave
-    //      first waits until its own loads of that slice have landed (the S-1 slices issued
-    //      after it may stay in flight), then a barrier proves that every wave has it and
-    //      that every wave is done reading slice kt, whose LDS buffer is refilled with slice
-    //      kt+S right away.  Slices past the end of K are read from the zero page, so every
-    //      transition issues the same number of loads and the wait count is a constant;
-    //      an fp8 K loop is padded to an even number of (zero) slices for the same reason. ----
+    // ---- software pipeline, branch-free.  Step g runs FM*FN MFMAs on the fragments in
+    //      register buffer g&1 while the next step's fragments are read from LDS into the
+    //      other buffer.  Every SPB slices there is a transition: this wave waits until its
+    //      own loads of the next SPB slices have landed (later slices may stay in flight),
+    //      then a barrier proves that every wave has them and that every wave is done
+    //      reading the SPB slices just consumed, whose LDS buffers are refilled with the
+    //      slices S ahead right away.  Slices past the end of K are read from the zero page,
+    //      so every transition issues the same number of loads and the wait counts are
+    //      constants; the K loop is padded with zero slices to a whole number of unrolled
+    //      iterations for the same reason. ----
+    constexpr int SPB = TS::SPB;
     typename F::T xf[2][TS::FM], wf[2][TS::FN];
     const int x_row = wm * TS::WTM + (lane & 31);   // activation fragment rows in the tile
     const int w_row = wn * TS::WTN + (lane & 31);   // weight fragment rows in the tile
-    const int KTP = F::kSteps == 1 ? (KT + 1) & ~1 : KT;   // slices walked (even step count)
+    constexpr int P = SPB * F::kSteps;               // steps between transitions
+    // steps per loop iteration: even (static fragment buffers); the register path also needs
+    // two slices per iteration (static register sets)
+    constexpr int U = TS::REG ? 2 * F::kSteps : (P >= 2 ? P : 2);
+    constexpr int SLICES_PER_ITER = U / F::kSteps;
+    const int KTP = (KT + SLICES_PER_ITER - 1) / SLICES_PER_ITER * SLICES_PER_ITER;
     const int steps = KTP * F::kSteps;
     auto stage_a = [&](int kt) -> const uint8_t* { return smem + (kt % S) * TS::STAGE; };
     auto read_frags = [&](auto buf_c, int kt, int st) {
@@ -317,34 +364,99 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
             for (int i = 0; i < TS::FM; ++i) acc[j][i] = F::mma(wf[b][j], xf[b][i], acc[j][i]);
     };
     constexpr int MF = TS::FM * TS::FN, R = (TS::FM + TS::FN) * F::kReads;
-
-#pragma unroll
-    for (int s2 = 0; s2 < S; ++s2) issue_slice(s2);
-    wait_vmcnt<(S - 1) * LOADS>();
-    barrier();
-    read_frags(std::integral_constant<int, 0>{}, 0, 0);
-
-    // one pipeline step; C is the register buffer holding this step's fragments
-    auto step = [&](auto cur_c, int g) {
-        constexpr int c = decltype(cur_c)::value;
-        const int kt = g / F::kSteps, st = g - kt * F::kSteps;
-        if (F::kSteps == 2 && st == 0) {
-            // next step is in the same slice: no synchronisation needed
-            read_frags(std::integral_constant<int, c ^ 1>{}, kt, 1);
-            mma_all(cur_c);
-            interleave<MF, R, 0>();
-        } else {
-            wait_vmcnt<(S - 2) * LOADS>();
-            barrier();
-            issue_slice(kt + S);
-            read_frags(std::integral_constant<int, c ^ 1>{}, kt + 1, 0);
-            mma_all(cur_c);
-            interleave<MF, R, LOADS>();
+    auto schedule = [&](auto r_c, auto g_c, auto w_c) {
+        constexpr int RR = decltype(r_c)::value, GG = decltype(g_c)::value, WW = decltype(w_c)::value;
+        if constexpr (TS::SCHED == 0 || TS::SCHED == 3) {
+            interleave<MF, RR, GG, WW>();
+        } else if constexpr (TS::SCHED == 2 || TS::SCHED == 4) {
+            if constexpr (GG > 0) __builtin_amdgcn_sched_group_barrier(0x020, GG, 0);
+            if constexpr (WW > 0) __builtin_amdgcn_sched_group_barrier(0x200, WW, 0);
+            if constexpr (RR > 0) __builtin_amdgcn_sched_group_barrier(0x100, RR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
         }
     };
-    for (int g = 0; g < steps; g += 2) {
+    auto prio_hi = [&]() { if constexpr (TS::SCHED == 3 || TS::SCHED == 4) __builtin_amdgcn_s_setprio(2); };
+    auto prio_lo = [&]() { if constexpr (TS::SCHED == 3 || TS::SCHED == 4) __builtin_amdgcn_s_setprio(0); };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if constexpr (TS::REG) {
+        // slices 0 and 1 go to LDS; slices 2 and 3 stay in flight in the register sets
+        load_slice(I0{}, 0);
+        load_slice(I1{}, 1);
+        wait_vmcnt<LOADS>();
+        write_slice(I0{}, 0);
+        load_slice(I0{}, 2);
+        wait_vmcnt<LOADS>();
+        write_slice(I1{}, 1);
+        load_slice(I1{}, 3);
+        wait_vmcnt<2 * LOADS>();
+    } else {
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) issue_slice(s2);
+        wait_vmcnt<(S - SPB) * LOADS>();
+    }
+    barrier();
+    read_frags(I0{}, 0, 0);
+
+    // step q of an unrolled iteration starting at step g0 (q and everything derived from it
+    // are compile-time constants)
+    auto step = [&](auto q_c, int g0) {
+        constexpr int q = decltype(q_c)::value;
+        constexpr int c = q & 1, n = c ^ 1;
+        constexpr int st = q % F::kSteps;
+        constexpr int slice_in_iter = q / F::kSteps;
+        constexpr bool same_slice = st + 1 < F::kSteps;
+        constexpr bool transition = !same_slice && (slice_in_iter + 1) % SPB == 0;
+        const int kt = g0 / F::kSteps + slice_in_iter;
+        if constexpr (same_slice) {
+            read_frags(std::integral_constant<int, n>{}, kt, st + 1);
+            prio_hi();
+            mma_all(std::integral_constant<int, c>{});
+            prio_lo();
+            schedule(std::integral_constant<int, R>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        } else if constexpr (!transition) {
+            // the next slice landed at the previous transition
+            read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
+            prio_hi();
+            mma_all(std::integral_constant<int, c>{});
+            prio_lo();
+            schedule(std::integral_constant<int, R>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        } else if constexpr (TS::REG) {
+            // slice kt+2 has reached its registers (kt+3 may be in flight) and this wave's
+            // LDS writes of slice kt+1 are done; after the barrier slice kt+1 is visible to
+            // all and stage (kt+2)%3 (slice kt-1) is free
+            wait_vmcnt<LOADS>();
+            barrier();
+            constexpr int set = slice_in_iter & 1;          // register set of slice kt+2 (and kt+4)
+            write_slice(std::integral_constant<int, set>{}, kt + 2);
+            load_slice(std::integral_constant<int, set>{}, kt + 4);
+            read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
+            prio_hi();
+            mma_all(std::integral_constant<int, c>{});
+            prio_lo();
+            schedule(std::integral_constant<int, R>{}, std::integral_constant<int, LOADS>{},
+                     std::integral_constant<int, LOADS>{});
+        } else {
+            wait_vmcnt<(S - 2 * SPB) * LOADS>();
+            barrier();
+#pragma unroll
+            for (int i = 0; i < SPB; ++i) issue_slice(kt + 1 - SPB + S + i);
+            read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
+            prio_hi();
+            mma_all(std::integral_constant<int, c>{});
+            prio_lo();
+            schedule(std::integral_constant<int, R>{}, std::integral_constant<int, SPB * LOADS>{},
+                     std::integral_constant<int, 0>{});
+        }
+    };
+    for (int g = 0; g < steps; g += U) {
         step(std::integral_constant<int, 0>{}, g);
-        step(std::integral_constant<int, 1>{}, g + 1);
+        step(std::integral_constant<int, 1>{}, g);
+        if constexpr (U > 2) {
+            step(std::integral_constant<int, 2>{}, g);
+            step(std::integral_constant<int, 3>{}, g);
+        }
     }
 
     // ---- epilogue.  Lane holds output row  m = m0 + wm*WTM + 32 i + (lane & 31)  and, in
@@ -376,7 +488,10 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
     } else {
         constexpr int OB = OUT == kOutFp8 ? 1 : 2;            // output bytes per element
         constexpr int SROW = TS::BN * OB;                     // staging row bytes
-        static_assert(TS::BM * SROW <= S * TS::STAGE, "output tile fits the LDS ring");
+        constexpr int CPR = SROW / 16;                        // 16-byte chunks per staged row
+        // staged chunk cc of row r lives at chunk cc ^ (r & XM): the 16 rows written by one
+        // store instruction land in distinct bank groups instead of one
+        constexpr int XM = (CPR < 16 ? CPR : 16) - 1;
         __syncthreads();   // all waves are done reading operand slices: the LDS is reused for staging
         const float* const scale = p.scale;
         const float* const shift = p.shift;
@@ -433,7 +548,8 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
-                    uint8_t* dst = smem + ml * SROW + nl * OB;
+                    const int cb = nl * OB;                               // byte column in the row
+                    uint8_t* dst = smem + ml * SROW + ((((cb >> 4) ^ (ml & XM))) << 4) + (cb & 15);
                     if constexpr (OUT == kOutFp8) {
                         *reinterpret_cast<uint32_t*>(dst) = quant_e4m3_x4(v[0], v[1], v[2], v[3], p.out_inv_scale);
                     } else {
@@ -448,16 +564,15 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(const MmaArgs p, const
         }
         __syncthreads();
         // coalesced write-out: 16-byte chunks of the staged tile, row-major
-        constexpr int CPR = SROW / 16;                        // chunks per staged row
         const bool vec_ok = ((static_cast<int64_t>(N) * OB) & 15) == 0;
         uint8_t* const cbytes = static_cast<uint8_t*>(p.c);
-        for (int q = tid; q < TS::BM * CPR; q += kThreads) {
+        for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
             const int ml = q / CPR, cc = q - ml * CPR;
             const int64_t m = m0 + ml;
             const int nl = cc * (16 / OB);
             const int n = n0 + nl;
             if (m >= M || n >= N) continue;
-            const uint8_t* src = smem + ml * SROW + cc * 16;
+            const uint8_t* src = smem + ml * SROW + ((cc ^ (ml & XM)) << 4);
             uint8_t* dst = cbytes + (m * N + n) * OB;
             if (vec_ok && n + 16 / OB <= N) {
                 *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
@@ -475,6 +590,24 @@ using T128x128 = TileShape<128, 128, 2, 2, 4>;
 using T256x64 = TileShape<256, 64, 4, 1, 4>;
 using T128x64 = TileShape<128, 64, 2, 2, 4>;
 using T64x64 = TileShape<64, 64, 2, 2, 4>;
+// tuning variants (dense GEMM only): two waves per SIMD, or fewer stages
+using T256x256w8 = TileShape<256, 256, 2, 4, 4>;    // 8 waves of 128x64
+using T256x256w8t = TileShape<256, 256, 4, 2, 4>;   // 8 waves of 64x128
+using T256x256s3 = TileShape<256, 256, 2, 2, 3>;
+using T256x128s3 = TileShape<256, 128, 2, 2, 3>;
+using T256x128w8 = TileShape<256, 128, 4, 2, 4>;    // 8 waves of 64x64
+using T256x256w8b2 = TileShape<256, 256, 4, 2, 4, 2>;  // 8 waves of 64x128, barrier every 2 slices
+using T256x256w8ab2 = TileShape<256, 256, 2, 4, 4, 2>; // 8 waves of 128x64, barrier every 2 slices
+using T256x256w8s5 = TileShape<256, 256, 4, 2, 5>;     // 8 waves of 64x128, five stages
+using T256x256w8r = TileShape<256, 256, 4, 2, 3, 1, true>;   // 8 waves of 64x128, register path
+using T256x256w8ar = TileShape<256, 256, 2, 4, 3, 1, true>;  // 8 waves of 128x64, register path
+using T256x256w8ab2s1 = TileShape<256, 256, 2, 4, 4, 2, false, 1>;
+using T256x256w8ab2s2 = TileShape<256, 256, 2, 4, 4, 2, false, 2>;
+using T256x256w8ab2s3 = TileShape<256, 256, 2, 4, 4, 2, false, 3>;
+using T256x256w8b2s2 = TileShape<256, 256, 4, 2, 4, 2, false, 2>;
+using T256x256w8as2 = TileShape<256, 256, 2, 4, 4, 1, false, 2>;
+using T256x256w8ab2s4 = TileShape<256, 256, 2, 4, 4, 2, false, 4>;
+using T256x256w8ars2 = TileShape<256, 256, 2, 4, 3, 1, true, 2>;
 
 template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 hipError_t launch_one(const MmaArgs& a, hipStream_t stream) {
@@ -483,7 +616,7 @@ hipError_t launch_one(const MmaArgs& a, hipStream_t stream) {
     if (tm64 * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
     const int tiles_m = static_cast<int>(tm64);
     if (tiles_m == 0 || tiles_n == 0) return hipSuccess;
-    hipLaunchKernelGGL((mma_kernel<ELEM, TS, AMODE, ACT, OUT>), dim3(tiles_m * tiles_n), dim3(kThreads), 0,
+    hipLaunchKernelGGL((mma_kernel<ELEM, TS, AMODE, ACT, OUT>), dim3(tiles_m * tiles_n), dim3(TS::NT), 0,
                        stream, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -497,8 +630,31 @@ hipError_t launch_tile(const MmaArgs& a, int tile, hipStream_t s) {
         case kTile256x64: return launch_one<ELEM, T256x64, AMODE, ACT, OUT>(a, s);
         case kTile128x64: return launch_one<ELEM, T128x64, AMODE, ACT, OUT>(a, s);
         case kTile64x64: return launch_one<ELEM, T64x64, AMODE, ACT, OUT>(a, s);
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    if constexpr (AMODE == kDense) {
+        switch (tile) {
+            case kTile256x256w8r: return launch_one<ELEM, T256x256w8r, AMODE, ACT, OUT>(a, s);
+            case 16: return launch_one<ELEM, T256x256w8ab2s1, AMODE, ACT, OUT>(a, s);
+            case 17: return launch_one<ELEM, T256x256w8ab2s2, AMODE, ACT, OUT>(a, s);
+            case 18: return launch_one<ELEM, T256x256w8ab2s3, AMODE, ACT, OUT>(a, s);
+            case 19: return launch_one<ELEM, T256x256w8b2s2, AMODE, ACT, OUT>(a, s);
+            case 20: return launch_one<ELEM, T256x256w8as2, AMODE, ACT, OUT>(a, s);
+            case 21: return launch_one<ELEM, T256x256w8ab2s4, AMODE, ACT, OUT>(a, s);
+            case 22: return launch_one<ELEM, T256x256w8ars2, AMODE, ACT, OUT>(a, s);
+            case kTile256x256w8ar: return launch_one<ELEM, T256x256w8ar, AMODE, ACT, OUT>(a, s);
+            case kTile256x256w8: return launch_one<ELEM, T256x256w8, AMODE, ACT, OUT>(a, s);
+            case kTile256x256w8t: return launch_one<ELEM, T256x256w8t, AMODE, ACT, OUT>(a, s);
+            case kTile256x256s3: return launch_one<ELEM, T256x256s3, AMODE, ACT, OUT>(a, s);
+            case kTile256x128s3: return launch_one<ELEM, T256x128s3, AMODE, ACT, OUT>(a, s);
+            case kTile256x128w8: return launch_one<ELEM, T256x128w8, AMODE, ACT, OUT>(a, s);
+            case kTile256x256w8b2: return launch_one<ELEM, T256x256w8b2, AMODE, ACT, OUT>(a, s);
+            case kTile256x256w8ab2: return launch_one<ELEM, T256x256w8ab2, AMODE, ACT, OUT>(a, s);
+            case kTile256x256w8s5: return launch_one<ELEM, T256x256w8s5, AMODE, ACT, OUT>(a, s);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int AMODE>
@@ -515,7 +671,10 @@ hipError_t launch_bf16_act(const MmaArgs& a, int act, int tile, hipStream_t s) {
 
 int mma_tile_rows(int tile) {
     switch (tile) {
-        case kTile256x256: case kTile256x128: case kTile256x64: return 256;
+        case kTile256x256: case kTile256x128: case kTile256x64: case kTile256x256w8: case kTile256x256w8t:
+        case kTile256x256s3: case kTile256x128s3: case kTile256x128w8: case kTile256x256w8b2:
+        case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r: case kTile256x256w8ar:
+        case 16: case 17: case 18: case 19: case 20: case 21: case 22: return 256;
         case kTile128x128: case kTile128x64: return 128;
         case kTile64x64: return 64;
         default: return 0;
@@ -524,8 +683,10 @@ int mma_tile_rows(int tile) {
 
 int mma_tile_cols(int tile) {
     switch (tile) {
-        case kTile256x256: return 256;
-        case kTile256x128: case kTile128x128: return 128;
+        case kTile256x256: case kTile256x256w8: case kTile256x256w8t: case kTile256x256s3:
+        case kTile256x256w8b2: case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r:
+        case kTile256x256w8ar: case 16: case 17: case 18: case 19: case 20: case 21: case 22: return 256;
+        case kTile256x128: case kTile128x128: case kTile256x128s3: case kTile256x128w8: return 128;
         default: return 64;
     }
 }

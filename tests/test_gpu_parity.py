@@ -22,6 +22,8 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 # amplified by the channel's BN scale, so the chain gets twice the fused tolerance.
 TOL_UNFUSED = {"f32": 1e-4, "bf16": 4e-2}
 GUARD = 4096
+CONV_TILES = (0, 1, 2, 3, 4, 5)                  # tile shapes shared by conv and GEMM
+GEMM_TILES = CONV_TILES + tuple(range(6, 16))    # plus the dense-GEMM pipeline variants
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -135,7 +137,7 @@ RAGGED_BF16 = [
 @pytest.mark.parametrize("i", range(len(RAGGED_BF16)))
 def test_bf16_conv_ragged_shapes_every_tile(i):
     wl = workloads.workload(1, conv_bias=bool(i % 2), **RAGGED_BF16[i])
-    check_conv(wl, tiles=(None, 0, 1, 2, 3, 4, 5), unfused=(i < 3))
+    check_conv(wl, tiles=(None,) + CONV_TILES, unfused=(i < 3))
 
 
 RAGGED_F32 = [
@@ -225,7 +227,7 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
     ref = gemm_reference(inp, rows, res)
     L = layers().make_layer(inp)
     res_d = layers().to_device(res, "bf16") if res is not None else None
-    for tile in (None, 0, 1, 2, 3, 4, 5):
+    for tile in (None,) + GEMM_TILES:
         if tile is None:
             os.environ.pop("DLF_TILE", None)
         else:
@@ -297,7 +299,7 @@ def test_fp8_gemm_ragged_shapes_every_tile(i):
     rows = np.arange(wl.m)
     ref, u = fp8_reference(inp, rows)
     L = layers().make_layer(inp)
-    for tile in (None, 0, 1, 2, 3, 4, 5):
+    for tile in (None,) + GEMM_TILES:
         if tile is None:
             os.environ.pop("DLF_TILE", None)
         else:
