@@ -172,6 +172,27 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
         a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
         return hip_status(dlf::launch_conv_f32(a, act_code(d->act), s), what);
     }
+    // 3x3, stride 1, pad 1: the halo kernels.  DLF_CONV=generic forces the implicit GEMM,
+    // DLF_CONV=stream the halo kernel that streams weights (tests of every route).
+    dlf::HaloPlan plan{};
+    const char* force = std::getenv("DLF_CONV");
+    const bool generic = force && std::strcmp(force, "generic") == 0;
+    const bool stream_only = force && std::strcmp(force, "stream") == 0;
+    if (!generic && g.K > 0 && d->kh == 3 && d->kw == 3 && d->stride_h == 1 && d->stride_w == 1 &&
+        d->pad_h == 1 && d->pad_w == 1 &&
+        dlf::conv_halo_plan(static_cast<int>(d->n), static_cast<int>(d->h), static_cast<int>(d->w),
+                            static_cast<int>(d->c_in), static_cast<int>(d->c_out), !stream_only, &plan)) {
+        dlf::HaloArgs h{};
+        h.x = static_cast<const uint16_t*>(x);
+        h.w = static_cast<const uint16_t*>(w);
+        h.bias = bias;
+        h.res = static_cast<const uint16_t*>(residual);
+        h.y = static_cast<uint16_t*>(y);
+        h.N = static_cast<int>(d->n); h.H = static_cast<int>(d->h); h.W = static_cast<int>(d->w);
+        h.Cin = static_cast<int>(d->c_in); h.Cout = static_cast<int>(d->c_out);
+        h.co_tiles = h.Cout / 64;
+        return hip_status(dlf::launch_conv_halo(h, plan, act_code(d->act), s), what);
+    }
     dlf::MmaArgs a{};
     a.a = x;
     a.b = w;

@@ -1,0 +1,556 @@
+// Stride-1 3x3 convolution (bf16, pad 1) as an implicit GEMM whose activation
+// operand never leaves LDS: the fused Conv -> BN -> [residual] -> act kernel for
+// the ResNet-stage shapes.
+//
+// A workgroup (4 waves) owns TH output rows x the full width of one image and
+// 64 output channels.  It loads the (TH+2) x (W+2) x Cin input halo (zero
+// outside the image) into LDS once, straight from global memory, and builds the
+// A fragments of all nine taps from it by shifted reads; there is no per-tap
+// re-fetch of the input, which is what makes the generic implicit GEMM fetch
+// every input pixel nine times.  The folded weights W' (OHWI, i.e. [co][tap][ci])
+// stream through a four-stage LDS ring in slices of one tap x 64 input channels,
+// with the same software pipeline as the GEMM kernel: fragment double buffering,
+// LDS reads interleaved with the MFMAs, one barrier per slice, refills issued
+// S slices ahead.  The contraction is v_mfma_f32_32x32x16_bf16 issued as
+// D = W . X^T, so a lane holds one output pixel and runs of four consecutive
+// output channels; the epilogue (bias, residual, activation, one rounding) runs
+// on those registers and the tile leaves through LDS with coalesced 16-byte
+// stores, each output element written once: the conv + epilogue of
+// "OpenPPL算子融合深度解析" §4.3, with the zero padding of the direct
+// convolution loop in the discosf.com fusion article §3.3.
+//
+// LDS layouts (16-byte chunks XOR-swizzled so that the 16 lanes one fragment
+// read serves per cycle hit 16 distinct bank groups):
+//   halo:   pixel-major, Cin*2 bytes per pixel; chunk k of pixel q is stored at
+//           k ^ ((q >> 1) & 7) when Cin == 64, k ^ (q & 15) when Cin >= 128.
+//   weights: 64 rows (output channels) x 128 bytes; chunk k of row r at k ^ ((r >> 1) & 7).
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "mma_common.h"
+
+namespace dlf {
+namespace {
+
+constexpr int kCo = 64;                    // output channels per workgroup
+constexpr int kS = 4;                      // weight ring stages
+constexpr int kWStage = kCo * 128;         // one weight slice: 64 rows x 128 bytes
+constexpr int kWLoads = kWStage / 1024 / 4;   // 1 KB weight loads per wave per slice (2)
+
+__device__ __attribute__((aligned(64))) uint8_t g_halo_zero[64];
+
+__device__ __forceinline__ int wchunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Output staging: 64 channels = 128 B per pixel row; chunk c of row m sits at
+// c ^ ((m >> 1) & 7), so the 32 rows one 8-byte register write covers fall on
+// 16 distinct (row parity, chunk) slots and the 16-byte read-back of two
+// neighbouring rows by 16 lanes touches every bank group once.
+__device__ __forceinline__ int stg_swz(int m) { return (m >> 1) & 7; }
+
+template <int WF, int HALO_KB, int ACT>
+__global__ __launch_bounds__(256, 1) void conv_halo_kernel(const HaloArgs p, const int th, const int row_tiles) {
+    constexpr int HALO = HALO_KB * 1024;
+    constexpr int STAGED = 4 * WF * 32 * kCo * 2;          // output tile staging (reuses the LDS)
+    constexpr int RING = kS * kWStage;
+    constexpr int SMEM = HALO + RING > STAGED ? HALO + RING : STAGED;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+    uint8_t* const halo = smem;
+    uint8_t* const ring = smem + HALO;
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63, wave = tid >> 6;
+    // workgroup -> (co tile, image, row tile); consecutive ids share an image (L2 reuse)
+    const int bid = static_cast<int>(blockIdx.x);
+    const int co_tile = bid % p.co_tiles;
+    const int rt_img = bid / p.co_tiles;
+    const int img = rt_img / row_tiles, rt = rt_img - img * row_tiles;
+    const int h0 = rt * th;
+    const int th_eff = min(th, p.H - h0);
+    const int W = p.W, W2 = p.W + 2, Cin = p.Cin;
+    const int npix = th_eff * W;                            // output pixels of this tile
+    const int c0 = co_tile * kCo;
+    const int K = 9 * Cin;
+    const int Q = Cin >> 6;                                 // 64-channel groups
+    const int KT = 9 * Q;                                   // K slices
+    const int ps = Cin * 2;                                 // halo bytes per pixel
+    const int sh = Cin >= 128 ? 0 : 1, xm = Cin >= 128 ? 15 : 7;   // halo swizzle
+    const void* const zp = g_halo_zero;
+    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
+    const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
+
+    // ---- halo: (th+2) x (W+2) pixels, one 1 KB load instruction per 1024/ps pixels ----
+    {
+        const int nhp = (th_eff + 2) * W2;
+        const int nhi = (nhp * ps + 1023) >> 10;
+        for (int li = wave; li < nhi; li += 4) {
+            const int byte = li * 1024 + lane * 16;
+            const int q = byte / ps, pc = (byte - q * ps) >> 4;
+            const int lc = pc ^ ((q >> sh) & xm);
+            const int hr = q / W2, wc = q - hr * W2;
+            const int hi = h0 - 1 + hr, wi = wc - 1;
+            const bool ok = q < nhp && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                            static_cast<unsigned>(wi) < static_cast<unsigned>(W);
+            const int64_t off = ((static_cast<int64_t>(img) * p.H + hi) * W + wi) * ps + lc * 16;
+            load_lds16(ok ? static_cast<const void*>(xb + off) : zp, halo + li * 1024);
+        }
+    }
+
+    // ---- weight slices: slice kt = (tap kt / Q, channel group kt % Q); past KT: zero page ----
+    auto issue_w = [&](int kt) {
+        uint8_t* st = ring + (kt % kS) * kWStage;
+        const bool kin = kt < KT;
+        const int t = kin ? kt / Q : 0, q = kin ? kt - (kt / Q) * Q : 0;
+#pragma unroll
+        for (int j = 0; j < kWLoads; ++j) {
+            const int blk = wave * kWLoads + j;                 // 8 rows per 1 KB
+            const int r = blk * 8 + (lane >> 3), pc = lane & 7;
+            const int lc = wchunk(r, pc);
+            const int64_t off = (static_cast<int64_t>(c0 + r) * K + t * Cin + q * 64 + lc * 8) * 2;
+            load_lds16(kin ? static_cast<const void*>(wb + off) : zp, st + blk * 1024);
+        }
+    };
+
+    // ---- this lane's pixels: fragment i holds tile pixel (wave*WF + i)*32 + (lane & 31) ----
+    int hp[WF];
+#pragma unroll
+    for (int i = 0; i < WF; ++i) {
+        const int pix = (wave * WF + i) * 32 + (lane & 31);
+        const int pp = pix < npix ? pix : 0;
+        const int ho = pp / W;
+        hp[i] = ho * W2 + (pp - ho * W);                    // halo pixel of tap (0, 0)
+    }
+
+    f32x16_t acc[2][WF];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < WF; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+    bf16x8_t xf[2][WF], wf[2][2];
+    auto read_frags = [&](auto b_c, int kt, int st) {
+        constexpr int b = decltype(b_c)::value;
+        const int t = kt / Q, q = kt - t * Q;
+        const int r = t / 3, s = t - r * 3;
+        const int c = 2 * st + (lane >> 5);                 // 16-byte chunk within the 64 channels
+        const int cix = q * 8 + c;
+#pragma unroll
+        for (int i = 0; i < WF; ++i) {
+            const int qp = hp[i] + r * W2 + s;
+            xf[b][i] = *reinterpret_cast<const bf16x8_t*>(halo + qp * ps + ((cix ^ ((qp >> sh) & xm)) << 4));
+        }
+        const uint8_t* stg = ring + (kt % kS) * kWStage;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 32 * j + (lane & 31);
+            wf[b][j] = *reinterpret_cast<const bf16x8_t*>(stg + row * 128 + (wchunk(row, c) << 4));
+        }
+    };
+    auto mma_all = [&](auto b_c) {
+        constexpr int b = decltype(b_c)::value;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < WF; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], xf[b][i], acc[j][i], 0, 0, 0);
+    };
+    constexpr int MF = 2 * WF, R = 2 + WF;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+#pragma unroll
+    for (int s2 = 0; s2 < kS; ++s2) issue_w(s2);
+    wait_vmcnt<(kS - 1) * kWLoads>();   // the halo and weight slice 0 have landed
+    barrier();
+    read_frags(I0{}, 0, 0);
+
+    // four k-steps of 16 channels per slice; the transition to slice kt+1 happens in step 3
+    for (int kt = 0; kt < KT; ++kt) {
+        read_frags(I1{}, kt, 1);
+        mma_all(I0{});
+        interleave<MF, R, 0>();
+        read_frags(I0{}, kt, 2);
+        mma_all(I1{});
+        interleave<MF, R, 0>();
+        read_frags(I1{}, kt, 3);
+        mma_all(I0{});
+        interleave<MF, R, 0>();
+        wait_vmcnt<(kS - 2) * kWLoads>();
+        barrier();
+        issue_w(kt + kS);
+        read_frags(I0{}, kt + 1 < KT ? kt + 1 : kt, 0);
+        mma_all(I1{});
+        interleave<MF, R, kWLoads>();
+    }
+
+    wait_vmcnt<0>();   // the zero-page refills past the last slice have landed
+    // ---- epilogue: lane holds pixel (wave*WF + i)*32 + (lane & 31) and, in register group g,
+    //      output channels 32 j + 8 g + 4 (lane / 32) + e%4 of this tile ----
+    __syncthreads();   // the LDS is reused for staging
+    const int lrow = lane & 31, half = lane >> 5;
+    constexpr int SROW = kCo * 2, CPR = SROW / 16;
+    const int64_t m0 = (static_cast<int64_t>(img) * p.H + h0) * W;   // first output row of the tile
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int nl = 32 * j + 8 * g + 4 * half;
+            float sh4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                const f32x4_t t = *reinterpret_cast<const f32x4_t*>(p.bias + c0 + nl);
+                sh4[0] = t[0]; sh4[1] = t[1]; sh4[2] = t[2]; sh4[3] = t[3];
+            }
+#pragma unroll
+            for (int i = 0; i < WF; ++i) {
+                const int ml = (wave * WF + i) * 32 + lrow;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e] + sh4[e];
+                if (p.res) {
+                    const int64_t mr = m0 + (ml < npix ? ml : 0);
+                    const uint2 t = *reinterpret_cast<const uint2*>(p.res + mr * p.Cout + c0 + nl);
+                    v[0] += __uint_as_float(t.x << 16);
+                    v[1] += __uint_as_float(t.x & 0xFFFF0000u);
+                    v[2] += __uint_as_float(t.y << 16);
+                    v[3] += __uint_as_float(t.y & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                                    (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+                                    (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                const int cb = nl * 2;
+                *reinterpret_cast<uint2*>(smem + ml * SROW + (((cb >> 4) ^ stg_swz(ml)) << 4) + (cb & 15)) =
+                    make_uint2(lo, hi);
+            }
+        }
+    }
+    __syncthreads();
+    uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
+    for (int qd = tid; qd < npix * CPR; qd += 256) {
+        const int ml = qd / CPR, cc = qd - ml * CPR;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + ml * SROW + ((cc ^ stg_swz(ml)) << 4));
+        *reinterpret_cast<u32x4_t*>(yb + ((m0 + ml) * p.Cout + c0) * 2 + cc * 16) = v;
+    }
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// ---- 64 input channels: weights resident in LDS, persistent workgroups ----
+//
+// With Cin = 64 all nine taps of a 64-channel output tile are 72 KB, so each
+// workgroup loads them once and keeps them; the rest of LDS holds two halo
+// buffers.  One workgroup per CU walks a list of row tiles.  Its eight waves are
+// split by role: four consumer waves (one per SIMD) only read LDS, issue MFMAs
+// and run the register epilogue; four producer waves own all global memory
+// traffic: the next tile's halo (LDS-DMA into the idle buffer) and the previous
+// tile's output (read back from LDS staging, stored with 16-byte writes).  A
+// producer blocked on a full memory queue therefore never holds up the matrix
+// pipe of its SIMD.  Tiles are dealt to the eight XCDs in contiguous ranges
+// (workgroup b runs on XCD b mod 8), so the halo rows that neighbouring tiles
+// share are fetched once per L2.
+//
+// Per tile k (halo buffer b = k mod 2), both roles pass the same two barriers:
+//   consumers: compute on b | Y_k | epilogue into staging (reusing b) | X_k+1
+//   producers: store tile k-1 from staging in b^1, load halo k+1 into b^1,
+//              wait for both                          | Y_k |              | X_k+1
+// Each producer wave reads back exactly the 1 KB staging blocks its own halo
+// loads later overwrite, so only its own LDS reads have to finish first.
+constexpr int kRWeights = 9 * kWStage;   // 72 KB
+constexpr int kRHalo = 44 * 1024;        // one halo buffer: (th + 2) (W + 2) pixels x 128 B
+constexpr int kRBlocks = 256;            // 32 per XCD
+constexpr int kRDist = 2;                // fragment prefetch distance (k-steps)
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0) only
+
+template <int WF, int ACT>
+__global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p, const int th, const int row_tiles,
+                                                               const int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kRWeights + 2 * kRHalo];
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63, wave = tid >> 6;
+    const int bid = static_cast<int>(blockIdx.x);
+    const int xcd = bid & 7, jb = bid >> 3;
+    const int co_tile = jb % p.co_tiles, U = 32 / p.co_tiles;
+    const int T = p.N * row_tiles;
+    const int s_end = min(T, (xcd + 1) * per_xcd);
+    const int s_first = xcd * per_xcd + jb / p.co_tiles;
+    if (s_first >= s_end) return;
+    const int W = p.W, W2 = p.W + 2, H = p.H;
+    const int c0 = co_tile * kCo;
+    constexpr int SROW = kCo * 2, CPR = SROW / 16;
+
+    if (wave >= 4) {
+        // ================= producers =================
+        const int pw = wave - 4, ptid = tid - 256;
+        const void* const zp = g_halo_zero;
+        const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
+        const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
+        uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
+        auto load_halo = [&](int st, uint8_t* buf) {
+            const int img = st / row_tiles, h0 = (st - img * row_tiles) * th;
+            const int nhp = (min(th, H - h0) + 2) * W2;
+            const int nhi = (nhp * 128 + 1023) >> 10;
+            for (int li = pw; li < nhi; li += 4) {
+                const int q = li * 8 + (lane >> 3), pc = lane & 7;
+                const int hr = q / W2, wc = q - hr * W2;
+                const int hi = h0 - 1 + hr, wi = wc - 1;
+                const bool ok = q < nhp && static_cast<unsigned>(hi) < static_cast<unsigned>(H) &&
+                                static_cast<unsigned>(wi) < static_cast<unsigned>(W);
+                const int64_t off =
+                    ((static_cast<int64_t>(img) * H + hi) * W + wi) * 128 + ((pc ^ ((q >> 1) & 7)) << 4);
+                load_lds16(ok ? static_cast<const void*>(xb + off) : zp, buf + li * 1024);
+            }
+        };
+        // staged output of spatial tile st (in buf) -> y; rows past the tile are skipped
+        auto store_tile = [&](int st, const uint8_t* buf) {
+            const int img = st / row_tiles, h0 = (st - img * row_tiles) * th;
+            const int npix = min(th, H - h0) * W;
+            const int64_t m0 = (static_cast<int64_t>(img) * H + h0) * W;
+            for (int qd = ptid; qd < npix * CPR; qd += 256) {
+                const int ml = qd / CPR, cc = qd - ml * CPR;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(buf + ml * SROW + ((cc ^ stg_swz(ml)) << 4));
+                *reinterpret_cast<u32x4_t*>(yb + ((m0 + ml) * p.Cout + c0) * 2 + cc * 16) = v;
+            }
+        };
+        // weights of this output tile: tap t at smem + t * 8 KB, 64 rows x 128 B, swizzled chunks
+        for (int l = pw; l < 72; l += 4) {
+            const int tap = l >> 3, blk = l & 7;
+            const int r = blk * 8 + (lane >> 3), pc = lane & 7;
+            const int64_t off = (static_cast<int64_t>(c0 + r) * 576 + tap * 64 + wchunk(r, pc) * 8) * 2;
+            load_lds16(wb + off, smem + tap * kWStage + blk * 1024);
+        }
+        load_halo(s_first, smem + kRWeights);
+        wait_vmcnt<0>();
+        barrier();   // X_0
+        int k = 0;
+        for (int s = s_first; s < s_end; s += U, ++k) {
+            uint8_t* const other = smem + kRWeights + ((k + 1) & 1) * kRHalo;
+            if (k > 0) store_tile(s - U, other);
+            wait_lgkm0();   // this wave's staging reads are done before its halo loads reuse the blocks
+            if (s + U < s_end) load_halo(s + U, other);
+            wait_vmcnt<0>();
+            barrier();   // Y_k
+            barrier();   // X_k+1
+        }
+        store_tile(s_first + (k - 1) * U, smem + kRWeights + ((k - 1) & 1) * kRHalo);
+        return;
+    }
+
+    // ================= consumers =================
+    const int tp = th * W;
+    int hq[WF];
+#pragma unroll
+    for (int i = 0; i < WF; ++i) {
+        const int pix = (wave * WF + i) * 32 + (lane & 31);
+        const int pp = pix < tp ? pix : 0;
+        const int ho = pp / W;
+        hq[i] = ho * W2 + (pp - ho * W);
+    }
+    const int half = lane >> 5;
+    int wrow[2], wsw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 32 * j + (lane & 31);
+        wrow[j] = row * 128;
+        wsw[j] = (row >> 1) & 7;
+    }
+    f32x4_t bias[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if (p.bias) {
+                bias[j][g] = *reinterpret_cast<const f32x4_t*>(p.bias + c0 + 32 * j + 8 * g + 4 * half);
+            } else {
+                bias[j][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+    barrier();   // X_0
+    int k = 0;
+    for (int s = s_first; s < s_end; s += U, ++k) {
+        uint8_t* const hb = smem + kRWeights + (k & 1) * kRHalo;
+
+        // ---- 36 k-steps (9 taps x 4 x 16 channels), fragments read kRDist steps ahead ----
+        f32x16_t acc[2][WF];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < WF; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+        bf16x8_t xf[4][WF], wf[4][2];
+        auto rd = [&](auto g_c) {
+            constexpr int g = decltype(g_c)::value;
+            constexpr int t = g >> 2, st = g & 3, r = t / 3, sc = t % 3, b = g & 3;
+            const int c = 2 * st + half;
+            const int d = r * W2 + sc;
+#pragma unroll
+            for (int i = 0; i < WF; ++i) {
+                const int qp = hq[i] + d;
+                xf[b][i] = *reinterpret_cast<const bf16x8_t*>(hb + qp * 128 + ((c ^ ((qp >> 1) & 7)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                wf[b][j] = *reinterpret_cast<const bf16x8_t*>(smem + t * kWStage + wrow[j] + ((c ^ wsw[j]) << 4));
+        };
+        static_for<0, kRDist>(rd);
+        static_for<0, 36>([&](auto g_c) {
+            constexpr int g = decltype(g_c)::value;
+            constexpr int b = g & 3;
+            if constexpr (g + kRDist < 36) rd(std::integral_constant<int, g + kRDist>{});
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < WF; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], xf[b][i], acc[j][i], 0, 0, 0);
+            // keep the program order: this step's MFMAs consume reads issued kRDist steps earlier
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        barrier();   // Y_k: every consumer is done with this halo; the next one has landed
+
+        // ---- epilogue: bias, residual, activation, one rounding; staged through hb ----
+        const int img = s / row_tiles, h0 = (s - img * row_tiles) * th;
+        const int npix = min(th, H - h0) * W;
+        const int64_t m0 = (static_cast<int64_t>(img) * H + h0) * W;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = 32 * j + 8 * g + 4 * half;
+#pragma unroll
+                for (int i = 0; i < WF; ++i) {
+                    const int ml = (wave * WF + i) * 32 + (lane & 31);
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e] + bias[j][g][e];
+                    if (p.res) {
+                        const int64_t mr = m0 + (ml < npix ? ml : 0);
+                        const uint2 t = *reinterpret_cast<const uint2*>(p.res + mr * p.Cout + c0 + nl);
+                        v[0] += __uint_as_float(t.x << 16);
+                        v[1] += __uint_as_float(t.x & 0xFFFF0000u);
+                        v[2] += __uint_as_float(t.y << 16);
+                        v[3] += __uint_as_float(t.y & 0xFFFF0000u);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                                        (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+                                        (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                    const int cb = nl * 2;
+                    *reinterpret_cast<uint2*>(hb + ml * SROW + (((cb >> 4) ^ stg_swz(ml)) << 4) + (cb & 15)) =
+                        make_uint2(lo, hi);
+                }
+            }
+        }
+        barrier();   // X_k+1: staging complete
+    }
+}
+
+template <int WF>
+hipError_t launch_res(const HaloArgs& a, const HaloPlan& pl, int act, hipStream_t s) {
+    switch (act) {
+        case kActNone:
+            hipLaunchKernelGGL((conv_halo_res_kernel<WF, kActNone>), dim3(kRBlocks), dim3(512), 0, s, a, pl.th,
+                               pl.row_tiles, pl.per_xcd);
+            break;
+        case kActRelu:
+            hipLaunchKernelGGL((conv_halo_res_kernel<WF, kActRelu>), dim3(kRBlocks), dim3(512), 0, s, a, pl.th,
+                               pl.row_tiles, pl.per_xcd);
+            break;
+        case kActGelu:
+            hipLaunchKernelGGL((conv_halo_res_kernel<WF, kActGelu>), dim3(kRBlocks), dim3(512), 0, s, a, pl.th,
+                               pl.row_tiles, pl.per_xcd);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int WF, int HALO_KB>
+hipError_t launch_act(const HaloArgs& a, int th, int row_tiles, int act, hipStream_t s) {
+    const int blocks = a.N * row_tiles * a.co_tiles;
+    switch (act) {
+        case kActNone:
+            hipLaunchKernelGGL((conv_halo_kernel<WF, HALO_KB, kActNone>), dim3(blocks), dim3(256), 0, s, a, th, row_tiles);
+            break;
+        case kActRelu:
+            hipLaunchKernelGGL((conv_halo_kernel<WF, HALO_KB, kActRelu>), dim3(blocks), dim3(256), 0, s, a, th, row_tiles);
+            break;
+        case kActGelu:
+            hipLaunchKernelGGL((conv_halo_kernel<WF, HALO_KB, kActGelu>), dim3(blocks), dim3(256), 0, s, a, th, row_tiles);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile plan for the halo kernel, or false when the shape does not qualify.
+bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, HaloPlan* plan) {
+    if (N <= 0 || H <= 0 || W <= 0 || Cout <= 0 || Cout % kCo != 0) return false;
+    // Cin = 64: resident weights when 32 workgroups per XCD divide evenly among the output
+    // tiles and a halo of at least one row fits its 44 KB buffer
+    const int co_tiles = Cout / kCo;
+    if (resident_ok && Cin == 64 && 32 % co_tiles == 0 && W <= 256 && 3 * (W + 2) * 128 <= kRHalo) {
+        int th = 256 / W;
+        if (th > H) th = H;
+        while (th > 1 && (th + 2) * (W + 2) * 128 > kRHalo) --th;
+        const int64_t tiles = static_cast<int64_t>(N) * ((H + th - 1) / th);
+        if (tiles <= 0x7fffffff) {
+            plan->kind = 1;
+            plan->th = th;
+            plan->row_tiles = (H + th - 1) / th;
+            plan->wf = th * W <= 128 ? 1 : 2;
+            plan->halo_kb = 44;
+            plan->per_xcd = static_cast<int>((tiles + 7) / 8);
+            return true;
+        }
+    }
+    if (Cin != 64 && (Cin <= 0 || Cin % 128 != 0)) return false;   // the halo swizzle stays inside a pixel
+    if (Cin > 1024 || W > 256) return false;
+    const int ps = Cin * 2;
+    int th = 256 / W;                      // at most 8 fragments of 32 pixels
+    if (th > H) th = H;
+    if (th < 1) return false;
+    auto halo_kb = [&](int t) { return (((t + 2) * (W + 2) * ps) + 1023) / 1024; };
+    while (th > 1 && halo_kb(th) > 96) --th;
+    if (halo_kb(th) > 96) return false;
+    // equal row tiles: the fewest tiles at this height, then the smallest height giving that many
+    auto balance = [&](int t) { const int rt = (H + t - 1) / t; return (H + rt - 1) / rt; };
+    th = balance(th);
+    // enough workgroups to occupy the chip
+    auto blocks = [&](int t) { return static_cast<int64_t>(N) * ((H + t - 1) / t) * (Cout / kCo); };
+    while (th > 1 && blocks(th) < 256) th = balance((th + 1) / 2);
+    if (static_cast<int64_t>(N) * ((H + th - 1) / th) * (Cout / kCo) > 0x7fffffff) return false;
+    const int frags = (th * W + 31) / 32;
+    plan->kind = 0;
+    plan->per_xcd = 0;
+    plan->th = th;
+    plan->row_tiles = (H + th - 1) / th;
+    plan->wf = frags <= 4 ? 1 : 2;
+    plan->halo_kb = halo_kb(th) <= 48 ? 48 : 96;
+    return true;
+}
+
+hipError_t launch_conv_halo(const HaloArgs& a, const HaloPlan& plan, int act, hipStream_t s) {
+    if (plan.kind == 1) return plan.wf == 1 ? launch_res<1>(a, plan, act, s) : launch_res<2>(a, plan, act, s);
+    if (plan.wf == 1)
+        return plan.halo_kb == 48 ? launch_act<1, 48>(a, plan.th, plan.row_tiles, act, s)
+                                  : launch_act<1, 96>(a, plan.th, plan.row_tiles, act, s);
+    return plan.halo_kb == 48 ? launch_act<2, 48>(a, plan.th, plan.row_tiles, act, s)
+                              : launch_act<2, 96>(a, plan.th, plan.row_tiles, act, s);
+}
+
+}  // namespace dlf

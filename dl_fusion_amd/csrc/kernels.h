@@ -66,6 +66,30 @@ struct ConvF32Args {
 };
 hipError_t launch_conv_f32(const ConvF32Args& args, int act, hipStream_t stream);
 
+// bf16 3x3 stride-1 pad-1 convolution with the input halo resident in LDS.
+struct HaloArgs {
+    const uint16_t* x;      // [N][H][W][Cin]
+    const uint16_t* w;      // [Cout][3][3][Cin]
+    const float* bias;      // [Cout] or nullptr
+    const uint16_t* res;    // [N][H][W][Cout] or nullptr
+    uint16_t* y;            // [N][H][W][Cout]
+    int N, H, W, Cin, Cout;
+    int co_tiles;           // Cout / 64
+};
+struct HaloPlan {
+    int kind;        // 0: one row tile per workgroup, weights streamed; 1: Cin = 64, weights resident
+    int th;          // output rows per tile
+    int row_tiles;   // ceil(H / th)
+    int wf;          // 32-pixel fragments per wave (1 or 2)
+    int halo_kb;     // LDS reserved for one halo
+    int per_xcd;     // kind 1: spatial tiles per XCD
+};
+// False when the shape does not qualify (Cin = 64 or a multiple of 128, Cout a
+// multiple of 64, the halo of one output row within 96 KB).  resident_ok = false
+// keeps Cin = 64 layers on the streaming kernel.
+bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, HaloPlan* plan);
+hipError_t launch_conv_halo(const HaloArgs& args, const HaloPlan& plan, int act, hipStream_t stream);
+
 // Elementwise passes of the unfused chain.  dt: 0 fp32, 1 bf16.
 hipError_t launch_bn_apply(int64_t rows, int64_t c, int dt, const void* y, const float* gamma,
                            const float* beta, const float* mean, const float* var, float eps,

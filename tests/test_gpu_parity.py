@@ -34,6 +34,7 @@ def _gpu():
     torch.cuda.set_device(0)
     yield
     os.environ.pop("DLF_TILE", None)
+    os.environ.pop("DLF_CONV", None)
 
 
 def dlf():
@@ -79,27 +80,42 @@ def host(t, dtype):
 # ---------------------------------------------------------------------------
 # Convolutions
 # ---------------------------------------------------------------------------
-def check_conv(wl, tiles=(None,), unfused=True):
+def set_route(conv, tile):
+    """conv: None = the library's own choice; "stream" = keep 64-channel 3x3 stride-1 layers
+    off the resident-weight halo kernel; "generic" = force the implicit-GEMM kernel instead
+    of any halo kernel; tile: force an MFMA tile of the implicit GEMM."""
+    for key, val in (("DLF_CONV", conv), ("DLF_TILE", None if tile is None else str(tile))):
+        if val is None:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = val
+
+
+def check_conv(wl, tiles=(), unfused=True):
+    """The default route, then (bf16) the generic implicit GEMM with its default tile and
+    with every tile in `tiles`."""
     inp = workloads.generate(wl)
     ref = oracle.conv_bn_act(inp)
     L = layers().make_layer(inp, with_unfused=unfused)
     tdt = L.y.dtype
-    for tile in tiles:
-        if tile is None:
-            os.environ.pop("DLF_TILE", None)
-        else:
-            os.environ["DLF_TILE"] = str(tile)
-        case(f"conv_fused {wl} tile={tile}")
-        buf, y = guarded(L.out_shape, tdt)
-        L.forward(y=y)
-        torch.cuda.synchronize()
-        got = oracle.widen(host(y, wl.dtype), wl.dtype)
-        err = oracle.rel_error(got, ref)
-        assert err <= TOL[wl.dtype], (wl, tile, err)
-        assert guard_intact(buf, y.numel()), "store beyond the output"
-        if wl.act == "relu":
-            assert np.all(got >= 0)
-    os.environ.pop("DLF_TILE", None)
+    routes = [(None, None)]
+    if wl.dtype == "bf16":
+        routes += [("stream", None), ("generic", None)] + [("generic", t) for t in tiles]
+    try:
+        for conv, tile in routes:
+            set_route(conv, tile)
+            case(f"conv_fused {wl} route={conv} tile={tile}")
+            buf, y = guarded(L.out_shape, tdt)
+            L.forward(y=y)
+            torch.cuda.synchronize()
+            got = oracle.widen(host(y, wl.dtype), wl.dtype)
+            err = oracle.rel_error(got, ref)
+            assert err <= TOL[wl.dtype], (wl, conv, tile, err)
+            assert guard_intact(buf, y.numel()), "store beyond the output"
+            if wl.act == "relu":
+                assert np.all(got >= 0)
+    finally:
+        set_route(None, None)
     if unfused:
         case(f"conv_unfused {wl}")
         yu = L.forward_unfused()
@@ -137,7 +153,34 @@ RAGGED_BF16 = [
 @pytest.mark.parametrize("i", range(len(RAGGED_BF16)))
 def test_bf16_conv_ragged_shapes_every_tile(i):
     wl = workloads.workload(1, conv_bias=bool(i % 2), **RAGGED_BF16[i])
-    check_conv(wl, tiles=(None,) + CONV_TILES, unfused=(i < 3))
+    check_conv(wl, tiles=CONV_TILES, unfused=(i < 3))
+
+
+# 3x3 stride-1 pad-1 layers the halo kernel takes: several rows per workgroup with a
+# shorter last row tile, one row per workgroup, 64 / 128 / 256 / 384 input channels,
+# one or two 32-pixel fragments per wave, 48 KB and 96 KB halos.
+HALO_BF16 = [
+    dict(n=16, h=15, w=16, cin=64, cout=128, act="relu", residual=True),      # 2 rows, last 1
+    dict(n=128, h=11, w=50, cin=64, cout=64, act="gelu_tanh", residual=False),  # 4 rows x 50, last 3
+    dict(n=4, h=9, w=9, cin=128, cout=192, act="relu", residual=True),        # 1 row
+    dict(n=2, h=5, w=6, cin=384, cout=64, act="none", residual=False),        # 1 row, 3 channel groups
+    dict(n=64, h=14, w=14, cin=256, cout=64, act="relu", residual=True),      # 4 rows, last 2
+    # 64 input channels with resident weights: one tile per workgroup with a residual, and
+    # two output-channel tiles with up to three row tiles per workgroup
+    dict(n=96, h=9, w=20, cin=64, cout=64, act="relu", residual=True),
+    dict(n=320, h=2, w=8, cin=64, cout=128, act="gelu_tanh", residual=False),
+    # 1x1 and 2x3 images: every tap but the centre (or nearly) reads padding.  One image is
+    # not enough here: the metric floors each channel at its rms, and with one pixel per
+    # channel the bf16-rounded folded weights alone reach 3% of a cancelled output.
+    dict(n=64, h=1, w=1, cin=64, cout=64, act="relu", residual=False),
+    dict(n=16, h=2, w=3, cin=64, cout=64, act="none", residual=True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(HALO_BF16)))
+def test_bf16_conv_halo_shapes(i):
+    wl = workloads.workload(1, conv_bias=bool(i % 2), kh=3, kw=3, stride=1, pad=1, **HALO_BF16[i])
+    check_conv(wl, unfused=(i == 0))
 
 
 RAGGED_F32 = [
