@@ -277,8 +277,8 @@ def main():
                 "frac": head["frac_hbm_peak"]}
     tr = head["traffic_measured"]
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr else None
-    roof["kernel"] = "dlf::mma_kernel (implicit-GEMM conv, bf16 MFMA)" if wl.kind == "conv" and wl.dtype == "bf16" \
-        else "dlf::mma_kernel"
+    from dl_fusion_amd.rocprof import fused_kernel
+    roof["kernel"] = "dlf::" + fused_kernel(wl)
 
     out = {
         "metric": METRIC,
