@@ -251,22 +251,28 @@ __device__ __forceinline__ void static_for(F&& f) {
 // workgroup loads them once and keeps them; the rest of LDS holds two halo
 // buffers.  One workgroup per CU walks a list of row tiles.  Its eight waves are
 // split by role: four consumer waves (one per SIMD) only read LDS, issue MFMAs
-// and run the register epilogue; four producer waves own all global memory
-// traffic: the next tile's halo (LDS-DMA into the idle buffer) and the previous
-// tile's output (read back from LDS staging, stored with 16-byte writes).  A
-// producer blocked on a full memory queue therefore never holds up the matrix
-// pipe of its SIMD.  Tiles are dealt to the eight XCDs in contiguous ranges
-// (workgroup b runs on XCD b mod 8), so the halo rows that neighbouring tiles
-// share are fetched once per L2.
+// and run the register epilogue into LDS staging; four producer waves own all
+// global memory traffic: the next tile's halo (LDS-DMA into the idle buffer) and
+// the previous tile's output (read back from staging, written as whole 128-byte
+// rows).  A producer stalled on memory never holds up the matrix pipe of its
+// SIMD.  Tiles are dealt to the eight XCDs in contiguous ranges (workgroup b runs
+// on XCD b mod 8), so the halo rows that neighbouring tiles share are fetched
+// once per L2.
 //
 // Per tile k (halo buffer b = k mod 2), both roles pass the same two barriers:
 //   consumers: compute on b | Y_k | epilogue into staging (reusing b) | X_k+1
 //   producers: store tile k-1 from staging in b^1, load halo k+1 into b^1,
 //              wait for both                          | Y_k |              | X_k+1
-// Each producer wave reads back exactly the 1 KB staging blocks its own halo
-// loads later overwrite, so only its own LDS reads have to finish first.
+// Producer wave w reads back, and later loads the halo into, only the 1 KB
+// blocks w, w + 4, w + 8, ... of a buffer, so its own LDS reads are the only
+// ones that must finish before its halo loads reuse the space.
+//
+// Every address that does not change from tile to tile is computed once: the
+// consumer's fragment reads cost one XOR each, the producer's halo loads a
+// select and a compare each.
 constexpr int kRWeights = 9 * kWStage;   // 72 KB
 constexpr int kRHalo = 44 * 1024;        // one halo buffer: (th + 2) (W + 2) pixels x 128 B
+constexpr int kRLoads = kRHalo / 4096;   // halo loads per producer wave (1 KB each)
 constexpr int kRBlocks = 256;            // 32 per XCD
 constexpr int kRDist = 2;                // fragment prefetch distance (k-steps)
 
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
     if (s_first >= s_end) return;
     const int W = p.W, W2 = p.W + 2, H = p.H;
     const int c0 = co_tile * kCo;
-    constexpr int SROW = kCo * 2, CPR = SROW / 16;
+    constexpr int SROW = kCo * 2;
 
     if (wave >= 4) {
         // ================= producers =================
@@ -296,38 +302,59 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
         const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
         const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
         uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
+        // halo load n of this wave covers halo pixel q_n = 8 (pw + 4 n) + lane / 8, chunk lane % 8
+        // (stored at swizzled chunk position lane % 8, i.e. global chunk lc_n).  Tile-independent:
+        // the byte offset from halo pixel (0, 0), the halo row, and whether the column is inside.
+        int voff[kRLoads], hrow[kRLoads];
+        uint32_t colok = 0;
+#pragma unroll
+        for (int n = 0; n < kRLoads; ++n) {
+            const int q = 8 * (pw + 4 * n) + (lane >> 3);
+            const int hr = q / W2, wc = q - hr * W2;
+            hrow[n] = hr;
+            voff[n] = (hr * W + wc - 1) * 128 + (((lane & 7) ^ ((q >> 1) & 7)) << 4);
+            if (wc >= 1 && wc <= W) colok |= 1u << n;
+        }
+        // halo of spatial tile st into buf (zero outside the image)
         auto load_halo = [&](int st, uint8_t* buf) {
             const int img = st / row_tiles, h0 = (st - img * row_tiles) * th;
-            const int nhp = (min(th, H - h0) + 2) * W2;
+            const int the = min(th, H - h0);
+            const int nhp = (the + 2) * W2;
             const int nhi = (nhp * 128 + 1023) >> 10;
-            for (int li = pw; li < nhi; li += 4) {
-                const int q = li * 8 + (lane >> 3), pc = lane & 7;
-                const int hr = q / W2, wc = q - hr * W2;
-                const int hi = h0 - 1 + hr, wi = wc - 1;
-                const bool ok = q < nhp && static_cast<unsigned>(hi) < static_cast<unsigned>(H) &&
-                                static_cast<unsigned>(wi) < static_cast<unsigned>(W);
-                const int64_t off =
-                    ((static_cast<int64_t>(img) * H + hi) * W + wi) * 128 + ((pc ^ ((q >> 1) & 7)) << 4);
-                load_lds16(ok ? static_cast<const void*>(xb + off) : zp, buf + li * 1024);
+            // rows of the halo inside the image: hr in [rlo, rhi)
+            const int rlo = h0 == 0 ? 1 : 0, rhi = min(the + 2, H - h0 + 1);
+            const uint8_t* const xrow = xb + (static_cast<int64_t>(img) * H + h0 - 1) * W * 128;
+            const int q0 = 8 * pw + (lane >> 3);
+#pragma unroll
+            for (int n = 0; n < kRLoads; ++n) {
+                if (pw + 4 * n >= nhi) break;
+                const bool ok = ((colok >> n) & 1u) && q0 + 32 * n < nhp && hrow[n] >= rlo && hrow[n] < rhi;
+                load_lds16(ok ? static_cast<const void*>(xrow + voff[n]) : zp, buf + (pw + 4 * n) * 1024);
             }
         };
-        // staged output of spatial tile st (in buf) -> y; rows past the tile are skipped
+        // staged output of spatial tile st (in buf) -> y; lane handles chunk ptid % 8 of rows
+        // ptid / 8 + 32 i, so both addresses advance by constants (the swizzle repeats every 16 rows)
         auto store_tile = [&](int st, const uint8_t* buf) {
             const int img = st / row_tiles, h0 = (st - img * row_tiles) * th;
             const int npix = min(th, H - h0) * W;
-            const int64_t m0 = (static_cast<int64_t>(img) * H + h0) * W;
-            for (int qd = ptid; qd < npix * CPR; qd += 256) {
-                const int ml = qd / CPR, cc = qd - ml * CPR;
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(buf + ml * SROW + ((cc ^ stg_swz(ml)) << 4));
-                *reinterpret_cast<u32x4_t*>(yb + ((m0 + ml) * p.Cout + c0) * 2 + cc * 16) = v;
-            }
+            const int ml0 = ptid >> 3, cc = ptid & 7;
+            const uint8_t* src = buf + ml0 * SROW + ((cc ^ stg_swz(ml0)) << 4);
+            uint8_t* dst = yb + (((static_cast<int64_t>(img) * H + h0) * W + ml0) * p.Cout + c0) * 2 + cc * 16;
+            const int64_t dstep = static_cast<int64_t>(32) * p.Cout * 2;
+            for (int ml = ml0; ml < npix; ml += 32, src += 32 * SROW, dst += dstep)
+                *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
         };
-        // weights of this output tile: tap t at smem + t * 8 KB, 64 rows x 128 B, swizzled chunks
-        for (int l = pw; l < 72; l += 4) {
-            const int tap = l >> 3, blk = l & 7;
-            const int r = blk * 8 + (lane >> 3), pc = lane & 7;
-            const int64_t off = (static_cast<int64_t>(c0 + r) * 576 + tap * 64 + wchunk(r, pc) * 8) * 2;
-            load_lds16(wb + off, smem + tap * kWStage + blk * 1024);
+        // weights of this output tile: tap t at smem + t * 8 KB, 64 rows x 128 B, swizzled chunks;
+        // load l = pw + 4 n is tap l / 8, rows 8 (l % 8) .. +7, and l % 8 is pw or pw + 4
+        {
+            const int r0 = pw * 8 + (lane >> 3), r1 = r0 + 32;
+            const uint8_t* const w0 = wb + (static_cast<int64_t>(c0 + r0) * 576 + wchunk(r0, lane & 7) * 8) * 2;
+            const uint8_t* const w1 = wb + (static_cast<int64_t>(c0 + r1) * 576 + wchunk(r1, lane & 7) * 8) * 2;
+#pragma unroll
+            for (int n = 0; n < 18; ++n) {
+                const int l = pw + 4 * n, tap = l >> 3;
+                load_lds16(((l & 7) < 4 ? w0 : w1) + tap * 128, smem + tap * kWStage + (l & 7) * 1024);
+            }
         }
         load_halo(s_first, smem + kRWeights);
         wait_vmcnt<0>();
@@ -348,60 +375,69 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
 
     // ================= consumers =================
     const int tp = th * W;
-    int hq[WF];
+    const int half = lane >> 5;
+    // x fragment of tap t: halo pixel qp = hq + (t / 3) W2 + t % 3 of this lane's output pixel;
+    // chunk c sits at (qp 128 + swizzle(qp) 16) ^ (c << 4), and c = 2 st + half, so the address
+    // of k-step (t, st) is xa[i][t] ^ (32 st) with half folded into xa.
+    int xa[WF][9];
 #pragma unroll
     for (int i = 0; i < WF; ++i) {
         const int pix = (wave * WF + i) * 32 + (lane & 31);
         const int pp = pix < tp ? pix : 0;
         const int ho = pp / W;
-        hq[i] = ho * W2 + (pp - ho * W);
+        const int hq = ho * W2 + (pp - ho * W);
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            const int qp = hq + (t / 3) * W2 + t % 3;
+            xa[i][t] = (qp * 128 + (((qp >> 1) & 7) << 4)) ^ (half << 4);
+        }
     }
-    const int half = lane >> 5;
-    int wrow[2], wsw[2];
+    // weight row 32 j + lane % 32, chunk 2 st + half of tap t at t * 8 KB + woff[j][st]
+    int woff[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = 32 * j + (lane & 31);
-        wrow[j] = row * 128;
-        wsw[j] = (row >> 1) & 7;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) woff[j][st] = row * 128 + (((2 * st + half) ^ ((row >> 1) & 7)) << 4);
     }
-    f32x4_t bias[2][4];
+    // bias in the accumulator layout: register 4g + e of set j holds channel 32j + 8g + 4 half + e;
+    // it enters the first MFMA as its C operand, so the epilogue needs no add
+    f32x16_t biasv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            if (p.bias) {
-                bias[j][g] = *reinterpret_cast<const f32x4_t*>(p.bias + c0 + 32 * j + 8 * g + 4 * half);
-            } else {
-                bias[j][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+            f32x4_t b4 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) b4 = *reinterpret_cast<const f32x4_t*>(p.bias + c0 + 32 * j + 8 * g + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) biasv[j][4 * g + e] = b4[e];
         }
+    // staging address of chunk 0 of each fragment row (with this lane's half); chunk c is
+    // sbase ^ (c << 4) because the swizzle occupies address bits 4..6
+    int sbase[WF];
+#pragma unroll
+    for (int i = 0; i < WF; ++i) {
+        const int ml = (wave * WF + i) * 32 + (lane & 31);
+        sbase[i] = ml * SROW + (stg_swz(ml) << 4) + 8 * half;
+    }
     barrier();   // X_0
     int k = 0;
     for (int s = s_first; s < s_end; s += U, ++k) {
         uint8_t* const hb = smem + kRWeights + (k & 1) * kRHalo;
+        const int hoff = (k & 1) * kRHalo;   // hb - halo buffer 0; a multiple of 1 KB
 
         // ---- 36 k-steps (9 taps x 4 x 16 channels), fragments read kRDist steps ahead ----
         f32x16_t acc[2][WF];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < WF; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
         bf16x8_t xf[4][WF], wf[4][2];
         auto rd = [&](auto g_c) {
             constexpr int g = decltype(g_c)::value;
-            constexpr int t = g >> 2, st = g & 3, r = t / 3, sc = t % 3, b = g & 3;
-            const int c = 2 * st + half;
-            const int d = r * W2 + sc;
+            constexpr int t = g >> 2, st = g & 3, b = g & 3;
 #pragma unroll
-            for (int i = 0; i < WF; ++i) {
-                const int qp = hq[i] + d;
-                xf[b][i] = *reinterpret_cast<const bf16x8_t*>(hb + qp * 128 + ((c ^ ((qp >> 1) & 7)) << 4));
-            }
+            for (int i = 0; i < WF; ++i)
+                xf[b][i] = *reinterpret_cast<const bf16x8_t*>(smem + kRWeights + ((hoff + xa[i][t]) ^ (32 * st)));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                wf[b][j] = *reinterpret_cast<const bf16x8_t*>(smem + t * kWStage + wrow[j] + ((c ^ wsw[j]) << 4));
+                wf[b][j] = *reinterpret_cast<const bf16x8_t*>(smem + t * kWStage + woff[j][st]);
         };
         static_for<0, kRDist>(rd);
         static_for<0, 36>([&](auto g_c) {
@@ -412,46 +448,64 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < WF; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], xf[b][i], acc[j][i], 0, 0, 0);
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], xf[b][i],
+                                                                        g == 0 ? biasv[j] : acc[j][i], 0, 0, 0);
             // keep the program order: this step's MFMAs consume reads issued kRDist steps earlier
             __builtin_amdgcn_sched_barrier(0);
         });
         barrier();   // Y_k: every consumer is done with this halo; the next one has landed
 
-        // ---- epilogue: bias, residual, activation, one rounding; staged through hb ----
-        const int img = s / row_tiles, h0 = (s - img * row_tiles) * th;
-        const int npix = min(th, H - h0) * W;
-        const int64_t m0 = (static_cast<int64_t>(img) * H + h0) * W;
+        // ---- epilogue (bias is already in acc): residual, activation, one rounding, staged in hb ----
+        auto stage = [&](auto res_c) {
+            constexpr bool RES = decltype(res_c)::value;
+            const int img = s / row_tiles, h0 = (s - img * row_tiles) * th;
+            const int npix = min(th, H - h0) * W;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = 32 * j + 8 * g + 4 * half;
-#pragma unroll
-                for (int i = 0; i < WF; ++i) {
+            for (int i = 0; i < WF; ++i) {
+                const uint16_t* rrow = nullptr;
+                if constexpr (RES) {
                     const int ml = (wave * WF + i) * 32 + (lane & 31);
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e] + bias[j][g][e];
-                    if (p.res) {
-                        const int64_t mr = m0 + (ml < npix ? ml : 0);
-                        const uint2 t = *reinterpret_cast<const uint2*>(p.res + mr * p.Cout + c0 + nl);
-                        v[0] += __uint_as_float(t.x << 16);
-                        v[1] += __uint_as_float(t.x & 0xFFFF0000u);
-                        v[2] += __uint_as_float(t.y << 16);
-                        v[3] += __uint_as_float(t.y & 0xFFFF0000u);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
-                    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) |
-                                        (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-                    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) |
-                                        (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-                    const int cb = nl * 2;
-                    *reinterpret_cast<uint2*>(hb + ml * SROW + (((cb >> 4) ^ stg_swz(ml)) << 4) + (cb & 15)) =
-                        make_uint2(lo, hi);
+                    rrow = p.res + ((static_cast<int64_t>(img) * H + h0) * W + (ml < npix ? ml : 0)) * p.Cout + c0 +
+                           4 * half;
                 }
+                uint2 rv[2][4];
+                if constexpr (RES) {   // all eight residual loads first, one wait
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) rv[j][g] = *reinterpret_cast<const uint2*>(rrow + 32 * j + 8 * g);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e];
+                        if constexpr (RES) {
+                            const uint2 t = rv[j][g];
+                            v[0] += __uint_as_float(t.x << 16);
+                            v[1] += __uint_as_float(t.x & 0xFFFF0000u);
+                            v[2] += __uint_as_float(t.y << 16);
+                            v[3] += __uint_as_float(t.y & 0xFFFF0000u);
+                        }
+                        if constexpr (ACT == kActGelu) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+                        }
+                        uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                        if constexpr (ACT == kActRelu) {
+                            lo = relu_bf16x2(lo);
+                            hi = relu_bf16x2(hi);
+                        }
+                        *reinterpret_cast<uint2*>(hb + (sbase[i] ^ ((4 * j + g) << 4))) = make_uint2(lo, hi);
+                    }
             }
+        };
+        if (p.res) {
+            stage(std::true_type{});
+        } else {
+            stage(std::false_type{});
         }
         barrier();   // X_k+1: staging complete
     }

@@ -45,6 +45,22 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+
+// Two values rounded to bf16 (nearest even) in one conversion; a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// ReLU of two packed bf16 values: a value with the sign bit set becomes +0.  Rounding
+// to nearest keeps the sign, so ReLU after the rounding equals the rounding of ReLU.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t u) {
+    const i16x2_t s = __builtin_bit_cast(i16x2_t, u);
+    return __builtin_bit_cast(uint32_t, s & ~(s >> 15));
+}
+
 template <int ACT>
 __device__ __forceinline__ float activate(float v) {
     if constexpr (ACT == kActRelu) {
