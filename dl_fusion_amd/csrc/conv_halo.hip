@@ -42,6 +42,12 @@ __device__ __attribute__((aligned(64))) uint8_t g_halo_zero[64];
 
 __device__ __forceinline__ int wchunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// Chunk swizzle of halo pixel (hr, wc) of an image of width W, keyed on its unpadded index
+// hr * W + wc - 1: the output pixels a fragment read serves are consecutive in that index even
+// across a row end (where the halo index jumps by 2), so 16 of them always take 16 distinct
+// (pixel parity, chunk position) bank slots.
+__device__ __forceinline__ int hswz(int hr, int wc, int W) { return ((hr * W + wc - 1) >> 1) & 7; }
+
 // Output staging: 64 channels = 128 B per pixel row; chunk c of row m sits at
 // c ^ ((m >> 1) & 7), so the 32 rows one 8-byte register write covers fall on
 // 16 distinct (row parity, chunk) slots and the 16-byte read-back of two
@@ -531,6 +537,256 @@ hipError_t launch_res(const HaloArgs& a, const HaloPlan& pl, int act, hipStream_
     return hipGetLastError();
 }
 
+// ---- small images (halo of a 64-channel group <= 32 KB): one image per workgroup ----
+//
+// For late-stage layers (e.g. 14 x 14 x 256) a row tile is too small to amortise the
+// weights: a 64-channel output tile streams all 9 Cin x 64 weights for ~100 pixels.  Here a
+// workgroup takes a whole image and 32 output channels, halving the weight bytes per CU, and
+// streams the input halo by 64-channel groups through three 32 KB buffers in the order the
+// contraction uses them: k runs channel group by channel group, and within a group over the
+// nine taps, so groups q + 1 and q + 2 load while the taps of group q run.  Weight slices
+// (32 rows x one tap x 64 channels, 4 KB) stream through a twelve-stage ring.
+//
+// This tiling reads 1.5 KB of fragments from LDS per MFMA, and a wave can keep at most 15
+// LDS reads in flight, so eight waves issue them: waves w and w + 4 own the same 64 pixels x
+// 32 channels and split every 32-channel k-step into its two 16-channel halves; the second
+// wave's partial sums join the first's through LDS at the end.  Fragments are read two slices
+// (four k-steps) ahead.
+constexpr int kIGroup = 32 * 1024;       // one halo channel group: (H+2)(W+2) pixels x 128 B
+constexpr int kIG = 3;                   // halo group buffers
+constexpr int kIS = 12;                  // weight ring stages (11 slices of lookahead)
+constexpr int kILook = 2;                // fragments are read kILook slices (2 kILook steps) ahead
+constexpr int kIB = 6;                   // fragment register buffers (> 2 kILook, divides 18)
+constexpr int kISlice = 32 * 128;        // 32 output channels x 64 input channels x 2 B
+constexpr int kIGLoads = kIGroup / 8192; // halo group pieces per wave (1 KB each, 8 waves)
+
+template <int ACT>
+__global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kIG * kIGroup + kIS * kISlice];
+    uint8_t* const ring = smem + kIG * kIGroup;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int pg = wave & 3, kh = wave >> 2;   // pixel fragments 2 pg, 2 pg + 1; k half
+    const int bid = static_cast<int>(blockIdx.x);
+    const int img = bid % p.N, ct = bid / p.N;   // the output tiles of one image share an XCD when N % 8 == 0
+    const int c0 = ct * 32;
+    const int H = p.H, W = p.W, W2 = p.W + 2, Cin = p.Cin;
+    const int HW = H * W, NQ = (H + 2) * W2;
+    const int Q = Cin >> 6, KT = 9 * Q, K = 9 * Cin;
+    const void* const zp = g_halo_zero;
+    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x) + static_cast<int64_t>(img) * HW * Cin * 2;
+    const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
+
+    // halo group q (channels 64 q .. 64 q + 63) into buffer q % kIG: pixel-major, 128 B per pixel,
+    // chunk position c holds chunk c ^ hswz(pixel); kIGLoads pieces of 1 KB per wave
+    auto load_group = [&](int q) {
+        uint8_t* const buf = smem + (q % kIG) * kIGroup;
+        const int nhi = (NQ * 128 + 1023) >> 10;
+#pragma unroll
+        for (int n = 0; n < kIGLoads; ++n) {
+            const int li = wave + 8 * n;
+            const int qq = li * 8 + (lane >> 3), pc = lane & 7;
+            const int hr = qq / W2, wc = qq - hr * W2;
+            const int hi = hr - 1, wi = wc - 1;
+            const bool ok = li < nhi && qq < NQ && static_cast<unsigned>(hi) < static_cast<unsigned>(H) &&
+                            static_cast<unsigned>(wi) < static_cast<unsigned>(W);
+            const int64_t off = (static_cast<int64_t>(hi * W + wi) * Cin + q * 64 + ((pc ^ hswz(hr, wc, W)) << 3)) * 2;
+            load_lds16(ok ? static_cast<const void*>(xb + off) : zp, buf + li * 1024);
+        }
+    };
+    // weight slice kt = (group kt / 9, tap kt % 9): rows c0 .. c0+31, 64 channels; waves 0-3 load
+    // 8 rows each; past KT the zero page keeps their load count uniform
+    const int wr = (wave & 3) * 8 + (lane >> 3);
+    const uint8_t* const wrow = wb + (static_cast<int64_t>(c0 + wr) * K + wchunk(wr, lane & 7) * 8) * 2;
+    auto issue_w = [&](int kt) {
+        uint8_t* const st = ring + (kt % kIS) * kISlice + (wave & 3) * 1024;
+        if (kt < KT) {
+            const int q = kt / 9, t = kt - q * 9;
+            load_lds16(wrow + (t * Cin + q * 64) * 2, st);
+        } else {
+            load_lds16(zp, st);
+        }
+    };
+
+    // this wave's pixels: fragment i holds image pixel (2 pg + i) * 32 + lane % 32; the halo
+    // address of each tap's pixel with swizzle and half folded in (chunk 2 u + half of 16-channel
+    // sub-step u is at xa ^ (32 u))
+    int xa[2][9];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pix = (2 * pg + i) * 32 + (lane & 31);
+        const int pp = pix < HW ? pix : 0;
+        const int ho = pp / W, wo = pp - ho * W;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            const int hr = ho + t / 3, wc = wo + t % 3;
+            xa[i][t] = ((hr * W2 + wc) * 128 + (hswz(hr, wc, W) << 4)) ^ (half << 4);
+        }
+    }
+    // this wave's sub-step of k-step s is u = 2 s + kh; weight row lane % 32, chunk 2 u + half
+    const int row = lane & 31;
+    int wo2[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) wo2[s2] = row * 128 + (((2 * (2 * s2 + kh) + half) ^ ((row >> 1) & 7)) << 4);
+    f32x16_t biasv;   // the bias enters the first MFMA of the k-half-0 waves only
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        f32x4_t b4 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.bias && kh == 0) b4 = *reinterpret_cast<const f32x4_t*>(p.bias + c0 + 8 * g + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) biasv[4 * g + e] = b4[e];
+    }
+
+    // ---- prologue: groups 0 and 1, weight slices 0 .. kIS-2; slices 0 .. kILook visible ----
+    load_group(0);
+    if (Q > 1) load_group(1);
+    if (kh == 0) {
+#pragma unroll
+        for (int kt = 0; kt < kIS - 1; ++kt) issue_w(kt);
+        wait_vmcnt<kIS - 2 - kILook>();
+    } else {
+        if (Q > 1) {
+            wait_vmcnt<kIGLoads>();   // group 0
+        } else {
+            wait_vmcnt<0>();
+        }
+    }
+    barrier();
+
+    f32x16_t acc[2];
+    bf16x8_t xf[kIB][2], wf[kIB];   // buffer = step % kIB
+    // fragments of global step gs (slice gs / 2, this wave's 16 channels of its 32-channel
+    // step gs % 2); steps past the end re-read the last one (values unused)
+    auto rd = [&](auto b_c, int gs) {
+        constexpr int b = decltype(b_c)::value;
+        gs = gs < 2 * KT ? gs : 2 * KT - 1;
+        const int kt = gs >> 1, s2 = gs & 1;
+        const int q = kt / 9, t = kt - q * 9;
+        const uint8_t* const hb = smem + (q % kIG) * kIGroup;
+        const int u = 2 * s2 + kh;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) xf[b][i] = *reinterpret_cast<const bf16x8_t*>(hb + (xa[i][t] ^ (32 * u)));
+        wf[b] = *reinterpret_cast<const bf16x8_t*>(ring + (kt % kIS) * kISlice + wo2[s2]);
+    };
+    auto mma = [&](auto b_c, bool first) {
+        constexpr int b = decltype(b_c)::value;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b], xf[b][i], first ? biasv : acc[i], 0, 0, 0);
+    };
+    static_for<0, 2 * kILook>([&](auto g_c) { rd(g_c, decltype(g_c)::value); });
+    // Step gs reads step gs + 2 kILook, i.e. slice kt + kILook during slice kt, so that slice must
+    // be visible when slice kt starts.  One iteration is a channel group: 9 slices = 18 steps,
+    // a multiple of kIB, so every register buffer index is a compile-time constant.
+    for (int q = 0; q < Q; ++q) {
+        static_for<0, 18>([&](auto r_c) {
+            constexpr int r = decltype(r_c)::value;
+            const int kt = 9 * q + r / 2;
+            if constexpr (r % 2 == 0) {
+                if (kt > 0) {
+                    if (kh == 0) {
+                        // loads issued after slice kt + kILook's: slices kt + kILook + 1 ..
+                        // kt + kIS - 2 and the halo groups issued at slices in
+                        // [kt + kILook + 1 - kIS, kt - 1] (at most one: groups start every 9)
+                        const int lo = max(0, kt + kILook + 1 - kIS);
+                        const int m = (lo + 8) / 9;
+                        if (9 * m <= kt - 1 && m + 2 < Q) {
+                            wait_vmcnt<kIS - 2 - kILook + kIGLoads>();
+                        } else {
+                            wait_vmcnt<kIS - 2 - kILook>();
+                        }
+                    } else {
+                        // this wave loads halo groups only: the group slice kt + kILook reads
+                        // (clamped to the last) and the newer ones issued since
+                        const int need = min(kt + kILook, KT - 1) / 9;
+                        const int newest = min(Q - 1, max(Q > 1 ? 1 : 0, (kt - 1) / 9 + 2));
+                        const int after = newest - need;
+                        if (after <= 0) {
+                            wait_vmcnt<0>();
+                        } else if (after == 1) {
+                            wait_vmcnt<kIGLoads>();
+                        } else {
+                            wait_vmcnt<2 * kIGLoads>();
+                        }
+                    }
+                    barrier();
+                }
+                if (kh == 0) issue_w(kt + kIS - 1);
+                if (r == 0 && q + 2 < Q) load_group(q + 2);
+            }
+            const int gs = 18 * q + r;
+            rd(std::integral_constant<int, (r + 2 * kILook) % kIB>{}, gs + 2 * kILook);
+            mma(std::integral_constant<int, r % kIB>{}, q == 0 && r == 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+    wait_vmcnt<0>();
+
+    // ---- the two k halves meet: waves 4-7 hand their partial sums to waves 0-3 through LDS ----
+    barrier();   // every wave is done with the halo buffers
+    float* const red = reinterpret_cast<float*>(smem) + pg * 2 * 16 * 64 + lane;
+    if (kh == 1) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[(i * 16 + e) * 64] = acc[i][e];
+    }
+    barrier();
+    if (kh == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] += red[(i * 16 + e) * 64];
+
+    // ---- epilogue (bias already in acc): residual, activation, 8-byte stores of channels
+    //      c0 + 8 g + 4 half .. +3 ----
+    uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pix = (2 * pg + i) * 32 + (lane & 31);
+        if (pix >= HW) continue;
+        const int64_t e0 = (static_cast<int64_t>(img) * HW + pix) * p.Cout + c0 + 4 * half;
+        uint2 rv[4];
+        if (p.res) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) rv[g] = *reinterpret_cast<const uint2*>(p.res + e0 + 8 * g);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][4 * g + e];
+            if (p.res) {
+                v[0] += __uint_as_float(rv[g].x << 16);
+                v[1] += __uint_as_float(rv[g].x & 0xFFFF0000u);
+                v[2] += __uint_as_float(rv[g].y << 16);
+                v[3] += __uint_as_float(rv[g].y & 0xFFFF0000u);
+            }
+            if constexpr (ACT == kActGelu) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+            }
+            uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+            if constexpr (ACT == kActRelu) {
+                lo = relu_bf16x2(lo);
+                hi = relu_bf16x2(hi);
+            }
+            *reinterpret_cast<uint2*>(yb + (e0 + 8 * g) * 2) = make_uint2(lo, hi);
+        }
+    }
+}
+
+hipError_t launch_img(const HaloArgs& a, int act, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.N * (a.Cout / 32))), block(512);
+    switch (act) {
+        case kActNone: hipLaunchKernelGGL((conv_halo_img_kernel<kActNone>), grid, block, 0, s, a); break;
+        case kActRelu: hipLaunchKernelGGL((conv_halo_img_kernel<kActRelu>), grid, block, 0, s, a); break;
+        case kActGelu: hipLaunchKernelGGL((conv_halo_img_kernel<kActGelu>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int WF, int HALO_KB>
 hipError_t launch_act(const HaloArgs& a, int th, int row_tiles, int act, hipStream_t s) {
     const int blocks = a.N * row_tiles * a.co_tiles;
@@ -572,6 +828,17 @@ bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, Ha
             return true;
         }
     }
+    // small images: the whole image per workgroup (kind 2) when that still gives >= 128 workgroups
+    if (resident_ok && Cin % 64 == 0 && Cin > 0 && Cout % 32 == 0 && H * W <= 256 && (H + 2) * (W + 2) * 128 <= kIGroup &&
+        static_cast<int64_t>(N) * (Cout / 32) >= 128 && static_cast<int64_t>(N) * (Cout / 32) <= 0x7fffffff) {
+        plan->kind = 2;
+        plan->th = H;
+        plan->row_tiles = 1;
+        plan->wf = 2;
+        plan->halo_kb = kIG * kIGroup / 1024;
+        plan->per_xcd = 0;
+        return true;
+    }
     if (Cin != 64 && (Cin <= 0 || Cin % 128 != 0)) return false;   // the halo swizzle stays inside a pixel
     if (Cin > 1024 || W > 256) return false;
     const int ps = Cin * 2;
@@ -599,6 +866,7 @@ bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, Ha
 }
 
 hipError_t launch_conv_halo(const HaloArgs& a, const HaloPlan& plan, int act, hipStream_t s) {
+    if (plan.kind == 2) return launch_img(a, act, s);
     if (plan.kind == 1) return plan.wf == 1 ? launch_res<1>(a, plan, act, s) : launch_res<2>(a, plan, act, s);
     if (plan.wf == 1)
         return plan.halo_kb == 48 ? launch_act<1, 48>(a, plan.th, plan.row_tiles, act, s)

@@ -77,7 +77,8 @@ struct HaloArgs {
     int co_tiles;           // Cout / 64
 };
 struct HaloPlan {
-    int kind;        // 0: one row tile per workgroup, weights streamed; 1: Cin = 64, weights resident
+    int kind;        // 0: one row tile per workgroup, weights streamed; 1: Cin = 64, weights resident;
+                     // 2: small images, one image x 32 output channels per workgroup
     int th;          // output rows per tile
     int row_tiles;   // ceil(H / th)
     int wf;          // 32-pixel fragments per wave (1 or 2)
@@ -85,8 +86,9 @@ struct HaloPlan {
     int per_xcd;     // kind 1: spatial tiles per XCD
 };
 // False when the shape does not qualify (Cin = 64 or a multiple of 128, Cout a
-// multiple of 64, the halo of one output row within 96 KB).  resident_ok = false
-// keeps Cin = 64 layers on the streaming kernel.
+// multiple of 64, the halo of one output row within 96 KB; or, for kind 2, Cin a
+// multiple of 64, Cout of 32 and a small image).  resident_ok = false restricts the
+// plan to the streaming kernel (kind 0).
 bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, HaloPlan* plan);
 hipError_t launch_conv_halo(const HaloArgs& args, const HaloPlan& plan, int act, hipStream_t stream);
 

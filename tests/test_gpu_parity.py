@@ -81,9 +81,9 @@ def host(t, dtype):
 # Convolutions
 # ---------------------------------------------------------------------------
 def set_route(conv, tile):
-    """conv: None = the library's own choice; "stream" = keep 64-channel 3x3 stride-1 layers
-    off the resident-weight halo kernel; "generic" = force the implicit-GEMM kernel instead
-    of any halo kernel; tile: force an MFMA tile of the implicit GEMM."""
+    """conv: None = the library's own choice; "stream" = the halo kernel that streams weights
+    per row tile, never the resident-weight or whole-image ones; "generic" = the implicit-GEMM
+    kernel instead of any halo kernel; tile: force an MFMA tile of the implicit GEMM."""
     for key, val in (("DLF_CONV", conv), ("DLF_TILE", None if tile is None else str(tile))):
         if val is None:
             os.environ.pop(key, None)
@@ -169,6 +169,9 @@ HALO_BF16 = [
     # two output-channel tiles with up to three row tiles per workgroup
     dict(n=96, h=9, w=20, cin=64, cout=64, act="relu", residual=True),
     dict(n=320, h=2, w=8, cin=64, cout=128, act="gelu_tanh", residual=False),
+    # small images, one image x 32 output channels per workgroup: 8 and 3 input channel groups
+    dict(n=16, h=7, w=7, cin=512, cout=256, act="relu", residual=True),
+    dict(n=48, h=13, w=11, cin=192, cout=96, act="gelu_tanh", residual=True),
     # 1x1 and 2x3 images: every tap but the centre (or nearly) reads padding.  One image is
     # not enough here: the metric floors each channel at its rms, and with one pixel per
     # channel the bf16-rounded folded weights alone reach 3% of a cancelled output.
