@@ -56,10 +56,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<0..15> forces one
-// (tuning only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x
-// (tile area / relative MFMA efficiency of the tile shape).
-int pick_tile(int64_t M, int64_t N) {
+// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<n> forces one (tuning
+// only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x (tile area /
+// relative MFMA efficiency of the tile shape).  Where that picks 256 x 256 for a
+// dense GEMM, the eight-wave 256 x 256 variant with one barrier per two K slices
+// runs instead: measured 7-10% faster on the 4096 x 11008 x 4096 bf16 and
+// 8192 x 4096 x 4096 fp8 GEMMs.
+int pick_tile(int64_t M, int64_t N, bool dense) {
     if (const char* env = std::getenv("DLF_TILE")) {
         const int t = std::atoi(env);
         if (t >= 0 && t < dlf::kTileCount) return t;
@@ -81,6 +84,7 @@ int pick_tile(int64_t M, int64_t N) {
             best_cost = cost;
         }
     }
+    if (dense && best == dlf::kTile256x256) best = dlf::kTile256x256w8ab2;
     return best;
 }
 
@@ -208,7 +212,7 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     a.H = static_cast<int>(d->h); a.W = static_cast<int>(d->w); a.Cin = static_cast<int>(d->c_in);
     a.Ho = static_cast<int>(g.ho); a.Wo = static_cast<int>(g.wo); a.KW = static_cast<int>(d->kw);
     a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
-    return hip_status(dlf::launch_mma_bf16(a, true, act_code(d->act), pick_tile(g.M, d->c_out), s), what);
+    return hip_status(dlf::launch_mma_bf16(a, true, act_code(d->act), pick_tile(g.M, d->c_out, false), s), what);
 }
 
 dlf_status check_gemm_common(const dlf_gemm_desc* d, const void* a, const void* b, const void* c) {
@@ -359,7 +363,7 @@ dlf_status dlf_gemm_fused(const dlf_gemm_desc* d, const void* a, const void* b, 
     x.out_inv_scale = d->out_inv_scale;
     x.dequant = 1.0f;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int tile = pick_tile(d->m, d->n);
+    const int tile = pick_tile(d->m, d->n, true);
     if (bf16_path) return hip_status(dlf::launch_mma_bf16(x, false, act_code(d->act), tile, s), "dlf_gemm_fused");
     const int out = d->out_dtype == DLF_FP8_E4M3 ? dlf::kOutFp8 : dlf::kOutBf16;
     return hip_status(dlf::launch_mma_fp8(x, act_code(d->act), out, tile, s), "dlf_gemm_fused");
@@ -390,7 +394,7 @@ dlf_status dlf_gemm_plain(const dlf_gemm_desc* d, const void* a, const void* b, 
     x.out_inv_scale = 1.0f;
     x.dequant = dequant;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int tile = pick_tile(d->m, d->n);
+    const int tile = pick_tile(d->m, d->n, true);
     if (bf16_path) return hip_status(dlf::launch_mma_bf16(x, false, dlf::kActNone, tile, s), "dlf_gemm_plain");
     return hip_status(dlf::launch_mma_fp8(x, dlf::kActNone, dlf::kOutF32, tile, s), "dlf_gemm_plain");
 }

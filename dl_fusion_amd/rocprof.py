@@ -48,10 +48,16 @@ def fused_kernel(wl) -> str:
     if wl.kind == "conv":
         if wl.dtype == "f32":
             return "conv_f32_kernel"
-        halo = (wl.kh, wl.kw, wl.stride, wl.pad) == (3, 3, 1, 1) and wl.cout % 64 == 0
-        if halo and wl.cin == 64 and 32 % (wl.cout // 64) == 0 and 3 * (wl.w + 2) * 128 <= 44 * 1024:
+        # the routes of the library's halo plan, in its order
+        if (wl.kh, wl.kw, wl.stride, wl.pad) != (3, 3, 1, 1) or wl.cout % 32 != 0:
+            return "mma_kernel"
+        if wl.cout % 64 == 0 and wl.cin == 64 and 32 % (wl.cout // 64) == 0 and wl.w <= 256 \
+                and 3 * (wl.w + 2) * 128 <= 44 * 1024:
             return "conv_halo_res_kernel"
-        if halo and (wl.cin == 64 or wl.cin % 128 == 0):
+        if wl.cin % 64 == 0 and wl.h * wl.w <= 256 and (wl.h + 2) * (wl.w + 2) * 128 <= 32 * 1024 \
+                and wl.n * (wl.cout // 32) >= 128:
+            return "conv_halo_img_kernel"
+        if wl.cout % 64 == 0 and (wl.cin == 64 or wl.cin % 128 == 0) and wl.cin <= 1024 and wl.w <= 256:
             return "conv_halo_kernel"
     return "mma_kernel"
 
@@ -182,6 +188,10 @@ def main() -> None:
                           "| kernel | calls | avg us | total us | % |", "|---|---|---|---|---|"]
                 for name, calls, avg, tot, pct in rows[:8]:
                     lines.append(f"| `{name[:110]}` | {calls} | {avg:.3f} | {tot:.1f} | {pct:.1f} |")
+                ours = [r for r in rows if "dlf::" in r[0]]
+                if not ours or f"dlf::(anonymous namespace)::{frag}<" not in ours[0][0]:
+                    raise SystemExit(f"workload {idx}: expected {frag} to dominate the trace, found "
+                                     f"{ours[0][0] if ours else 'no library kernel'}")
                 fused = [r for r in rows if frag in r[0]]
                 if fused:
                     res["avg_us"] = fused[0][2]
