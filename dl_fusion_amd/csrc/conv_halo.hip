@@ -269,6 +269,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   consumers: compute on b | Y_k | epilogue into staging (reusing b) | X_k+1
 //   producers: store tile k-1 from staging in b^1, load halo k+1 into b^1,
 //              wait for both                          | Y_k |              | X_k+1
+// The first tile has one more, X_0': X_0 publishes the first halo and weight taps
+// 0..2, X_0' (before the consumers read tap 3) taps 3..8, so the MFMAs of the first
+// twelve k-steps overlap the rest of the weight fill.
 // Producer wave w reads back, and later loads the halo into, only the 1 KB
 // blocks w, w + 4, w + 8, ... of a buffer, so its own LDS reads are the only
 // ones that must finish before its halo loads reuse the space.
@@ -308,15 +311,33 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
         const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
         const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
         uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
+        // weights of this output tile: tap t at smem + t * 8 KB, 64 rows x 128 B, swizzled chunks;
+        // load l = pw + 4 n is tap l / 8, rows 8 (l % 8) .. +7, and l % 8 is pw or pw + 4.  Loads
+        // 0..5 (taps 0..2) go out first, before any halo address is computed, loads 6..17 (taps
+        // 3..8) after the first halo: the first tile starts once taps 0..2 and its halo are in.
+        const int wr0 = pw * 8 + (lane >> 3), wr1 = wr0 + 32;
+        const uint8_t* const w0 = wb + (static_cast<int64_t>(c0 + wr0) * 576 + wchunk(wr0, lane & 7) * 8) * 2;
+        const uint8_t* const w1 = wb + (static_cast<int64_t>(c0 + wr1) * 576 + wchunk(wr1, lane & 7) * 8) * 2;
+        auto load_weights = [&](auto n0_c, auto n1_c) {
+            static_for<decltype(n0_c)::value, decltype(n1_c)::value>([&](auto n_c) {
+                constexpr int n = decltype(n_c)::value;
+                const int l = pw + 4 * n, tap = l >> 3;
+                load_lds16(((l & 7) < 4 ? w0 : w1) + tap * 128, smem + tap * kWStage + (l & 7) * 1024);
+            });
+        };
+        load_weights(std::integral_constant<int, 0>{}, std::integral_constant<int, 6>{});
         // halo load n of this wave covers halo pixel q_n = 8 (pw + 4 n) + lane / 8, chunk lane % 8
         // (stored at swizzled chunk position lane % 8, i.e. global chunk lc_n).  Tile-independent:
         // the byte offset from halo pixel (0, 0), the halo row, and whether the column is inside.
+        // q / W2 is taken as (q + 1/2) / W2 in fp32: exact for q < 2^12 and W2 <= 258, since the
+        // product is never within 1/(2 W2) of an integer while its rounding error stays below 1e-3.
+        const float rw2 = 1.0f / static_cast<float>(W2);
         int voff[kRLoads], hrow[kRLoads];
         uint32_t colok = 0;
 #pragma unroll
         for (int n = 0; n < kRLoads; ++n) {
             const int q = 8 * (pw + 4 * n) + (lane >> 3);
-            const int hr = q / W2, wc = q - hr * W2;
+            const int hr = static_cast<int>((static_cast<float>(q) + 0.5f) * rw2), wc = q - hr * W2;
             hrow[n] = hr;
             voff[n] = (hr * W + wc - 1) * 128 + (((lane & 7) ^ ((q >> 1) & 7)) << 4);
             if (wc >= 1 && wc <= W) colok |= 1u << n;
@@ -350,21 +371,12 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
             for (int ml = ml0; ml < npix; ml += 32, src += 32 * SROW, dst += dstep)
                 *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
         };
-        // weights of this output tile: tap t at smem + t * 8 KB, 64 rows x 128 B, swizzled chunks;
-        // load l = pw + 4 n is tap l / 8, rows 8 (l % 8) .. +7, and l % 8 is pw or pw + 4
-        {
-            const int r0 = pw * 8 + (lane >> 3), r1 = r0 + 32;
-            const uint8_t* const w0 = wb + (static_cast<int64_t>(c0 + r0) * 576 + wchunk(r0, lane & 7) * 8) * 2;
-            const uint8_t* const w1 = wb + (static_cast<int64_t>(c0 + r1) * 576 + wchunk(r1, lane & 7) * 8) * 2;
-#pragma unroll
-            for (int n = 0; n < 18; ++n) {
-                const int l = pw + 4 * n, tap = l >> 3;
-                load_lds16(((l & 7) < 4 ? w0 : w1) + tap * 128, smem + tap * kWStage + (l & 7) * 1024);
-            }
-        }
         load_halo(s_first, smem + kRWeights);
-        wait_vmcnt<0>();
+        load_weights(std::integral_constant<int, 6>{}, std::integral_constant<int, 18>{});
+        wait_vmcnt<12>();   // all but the twelve loads of taps 3..8
         barrier();   // X_0
+        wait_vmcnt<0>();
+        barrier();   // X_0': taps 3..8
         int k = 0;
         for (int s = s_first; s < s_end; s += U, ++k) {
             uint8_t* const other = smem + kRWeights + ((k + 1) & 1) * kRHalo;
@@ -449,6 +461,10 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
         static_for<0, 36>([&](auto g_c) {
             constexpr int g = decltype(g_c)::value;
             constexpr int b = g & 3;
+            // first tile: taps 3..8 of the weights are known to have landed only after X_0'
+            if constexpr (g + kRDist == 12) {
+                if (k == 0) barrier();   // X_0'
+            }
             if constexpr (g + kRDist < 36) rd(std::integral_constant<int, g + kRDist>{});
 #pragma unroll
             for (int j = 0; j < 2; ++j)
