@@ -567,7 +567,9 @@ hipError_t launch_res(const HaloArgs& a, const HaloPlan& pl, int act, hipStream_
 // LDS reads in flight, so eight waves issue them: waves w and w + 4 own the same 64 pixels x
 // 32 channels and split every 32-channel k-step into its two 16-channel halves; the second
 // wave's partial sums join the first's through LDS at the end.  Fragments are read two slices
-// (four k-steps) ahead.
+// (four k-steps) ahead, and the slice barriers leave those reads in flight.  The loads into
+// LDS use the buffer form: with the global (FLAT) form in flight the compiler cannot count
+// outstanding LDS reads and waits for all of them before MFMAs.
 constexpr int kIGroup = 32 * 1024;       // one halo channel group: (H+2)(W+2) pixels x 128 B
 constexpr int kIG = 3;                   // halo group buffers
 constexpr int kIS = 12;                  // weight ring stages (11 slices of lookahead)
@@ -575,13 +577,18 @@ constexpr int kILook = 2;                // fragments are read kILook slices (2 
 constexpr int kIB = 6;                   // fragment register buffers (> 2 kILook, divides 18)
 constexpr int kISlice = 32 * 128;        // 32 output channels x 64 input channels x 2 B
 constexpr int kIGLoads = kIGroup / 8192; // halo group pieces per wave (1 KB each, 8 waves)
+// LDS reads a wave may leave in flight at a slice barrier: the reads of the last 2 kILook
+// steps (three per step).  The buffers refilled after the barrier of slice kt were last read
+// for slice kt - 1, whose reads went out 2 kILook steps before that slice, so they are older.
+constexpr int kIKeep = 2 * kILook * 3;
 
 template <int ACT>
 __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kIG * kIGroup + kIS * kISlice];
     uint8_t* const ring = smem + kIG * kIGroup;
     const int tid = static_cast<int>(threadIdx.x);
-    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    // the wave index is uniform: in a scalar register the role branches below stay scalar
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), half = lane >> 5;
     const int pg = wave & 3, kh = wave >> 2;   // pixel fragments 2 pg, 2 pg + 1; k half
     const int bid = static_cast<int>(blockIdx.x);
     const int img = bid % p.N, ct = bid / p.N;   // the output tiles of one image share an XCD when N % 8 == 0
@@ -589,9 +596,14 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
     const int H = p.H, W = p.W, W2 = p.W + 2, Cin = p.Cin;
     const int HW = H * W, NQ = (H + 2) * W2;
     const int Q = Cin >> 6, KT = 9 * Q, K = 9 * Cin;
-    const void* const zp = g_halo_zero;
-    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x) + static_cast<int64_t>(img) * HW * Cin * 2;
-    const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
+    // this image's input and this tile's 32 weight rows as buffers (both well below 4 GB:
+    // H W <= 256 pixels); loads outside the image or past the last slice read zeros
+    const __amdgpu_buffer_rsrc_t xr =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(p.x) + static_cast<int64_t>(img) * HW * Cin * 2,
+                    static_cast<uint32_t>(HW * Cin * 2));
+    const __amdgpu_buffer_rsrc_t wr_ =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(p.w) + static_cast<int64_t>(c0) * K * 2,
+                    static_cast<uint32_t>(32 * K * 2));
 
     // halo group q (channels 64 q .. 64 q + 63) into buffer q % kIG: pixel-major, 128 B per pixel,
     // chunk position c holds chunk c ^ hswz(pixel); kIGLoads pieces of 1 KB per wave
@@ -606,22 +618,18 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
             const int hi = hr - 1, wi = wc - 1;
             const bool ok = li < nhi && qq < NQ && static_cast<unsigned>(hi) < static_cast<unsigned>(H) &&
                             static_cast<unsigned>(wi) < static_cast<unsigned>(W);
-            const int64_t off = (static_cast<int64_t>(hi * W + wi) * Cin + q * 64 + ((pc ^ hswz(hr, wc, W)) << 3)) * 2;
-            load_lds16(ok ? static_cast<const void*>(xb + off) : zp, buf + li * 1024);
+            const uint32_t off = static_cast<uint32_t>(((hi * W + wi) * Cin + q * 64 + ((pc ^ hswz(hr, wc, W)) << 3)) * 2);
+            load_lds16_buf(xr, ok ? off : kOutOfRange, buf + li * 1024);
         }
     };
     // weight slice kt = (group kt / 9, tap kt % 9): rows c0 .. c0+31, 64 channels; waves 0-3 load
     // 8 rows each; past KT the zero page keeps their load count uniform
     const int wr = (wave & 3) * 8 + (lane >> 3);
-    const uint8_t* const wrow = wb + (static_cast<int64_t>(c0 + wr) * K + wchunk(wr, lane & 7) * 8) * 2;
+    const uint32_t wrow = static_cast<uint32_t>((wr * K + wchunk(wr, lane & 7) * 8) * 2);
     auto issue_w = [&](int kt) {
         uint8_t* const st = ring + (kt % kIS) * kISlice + (wave & 3) * 1024;
-        if (kt < KT) {
-            const int q = kt / 9, t = kt - q * 9;
-            load_lds16(wrow + (t * Cin + q * 64) * 2, st);
-        } else {
-            load_lds16(zp, st);
-        }
+        const int q = kt / 9, t = kt - q * 9;
+        load_lds16_buf(wr_, kt < KT ? wrow + static_cast<uint32_t>((t * Cin + q * 64) * 2) : kOutOfRange, st);
     };
 
     // this wave's pixels: fragment i holds image pixel (2 pg + i) * 32 + lane % 32; the halo
@@ -703,13 +711,17 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
                     if (kh == 0) {
                         // loads issued after slice kt + kILook's: slices kt + kILook + 1 ..
                         // kt + kIS - 2 and the halo groups issued at slices in
-                        // [kt + kILook + 1 - kIS, kt - 1] (at most one: groups start every 9)
+                        // [kt + kILook + 1 - kIS, kt - 1]: group m + 2 goes out at slice 9 m, so
+                        // a window of kIS - kILook - 1 <= 18 slices holds at most two
+                        static_assert(kIS - kILook - 1 <= 18, "at most two group loads per window");
                         const int lo = max(0, kt + kILook + 1 - kIS);
-                        const int m = (lo + 8) / 9;
-                        if (9 * m <= kt - 1 && m + 2 < Q) {
-                            wait_vmcnt<kIS - 2 - kILook + kIGLoads>();
+                        const int ng = max(0, min((kt - 1) / 9, Q - 3) - (lo + 8) / 9 + 1);
+                        if (ng >= 2) {
+                            wait_vm_lgkm<kIS - 2 - kILook + 2 * kIGLoads, kIKeep>();
+                        } else if (ng == 1) {
+                            wait_vm_lgkm<kIS - 2 - kILook + kIGLoads, kIKeep>();
                         } else {
-                            wait_vmcnt<kIS - 2 - kILook>();
+                            wait_vm_lgkm<kIS - 2 - kILook, kIKeep>();
                         }
                     } else {
                         // this wave loads halo groups only: the group slice kt + kILook reads
@@ -718,11 +730,11 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
                         const int newest = min(Q - 1, max(Q > 1 ? 1 : 0, (kt - 1) / 9 + 2));
                         const int after = newest - need;
                         if (after <= 0) {
-                            wait_vmcnt<0>();
+                            wait_vm_lgkm<0, kIKeep>();
                         } else if (after == 1) {
-                            wait_vmcnt<kIGLoads>();
+                            wait_vm_lgkm<kIGLoads, kIKeep>();
                         } else {
-                            wait_vmcnt<2 * kIGLoads>();
+                            wait_vm_lgkm<2 * kIGLoads, kIKeep>();
                         }
                     }
                     barrier();
@@ -737,6 +749,18 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
         });
     }
     wait_vmcnt<0>();
+
+    // the residual of this wave's outputs is fetched before the two k halves meet
+    uint2 rv[2][4];
+    if (kh == 0 && p.res) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pix = (2 * pg + i) * 32 + (lane & 31);
+            const int64_t e0 = (static_cast<int64_t>(img) * HW + (pix < HW ? pix : 0)) * p.Cout + c0 + 4 * half;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) rv[i][g] = *reinterpret_cast<const uint2*>(p.res + e0 + 8 * g);
+        }
+    }
 
     // ---- the two k halves meet: waves 4-7 hand their partial sums to waves 0-3 through LDS ----
     barrier();   // every wave is done with the halo buffers
@@ -762,21 +786,16 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
         const int pix = (2 * pg + i) * 32 + (lane & 31);
         if (pix >= HW) continue;
         const int64_t e0 = (static_cast<int64_t>(img) * HW + pix) * p.Cout + c0 + 4 * half;
-        uint2 rv[4];
-        if (p.res) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) rv[g] = *reinterpret_cast<const uint2*>(p.res + e0 + 8 * g);
-        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = acc[i][4 * g + e];
             if (p.res) {
-                v[0] += __uint_as_float(rv[g].x << 16);
-                v[1] += __uint_as_float(rv[g].x & 0xFFFF0000u);
-                v[2] += __uint_as_float(rv[g].y << 16);
-                v[3] += __uint_as_float(rv[g].y & 0xFFFF0000u);
+                v[0] += __uint_as_float(rv[i][g].x << 16);
+                v[1] += __uint_as_float(rv[i][g].x & 0xFFFF0000u);
+                v[2] += __uint_as_float(rv[i][g].y << 16);
+                v[3] += __uint_as_float(rv[i][g].y & 0xFFFF0000u);
             }
             if constexpr (ACT == kActGelu) {
 #pragma unroll

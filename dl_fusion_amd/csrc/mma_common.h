@@ -19,6 +19,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(L): as wait_vmcnt, but up to L of this wave's newest LDS
+// reads may stay in flight (LDS reads complete in issue order when no scalar loads are
+// outstanding).
+template <int N, int L>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "counter ranges");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (L << 8));
+}
+
 // Workgroup barrier without the implied memory fence of __syncthreads() (which
 // would drain every outstanding LDS-DMA load); the asm statement keeps the
 // compiler from moving LDS accesses across it.
@@ -48,6 +57,26 @@ __device__ __forceinline__ void interleave() {
 // lds_wave_base + 16 i (the base must be uniform across the wave).
 __device__ __forceinline__ void load_lds16(const void* g, uint8_t* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+// Buffer resource over [base, base + bytes) for the buffer form of the LDS-DMA load (word 3
+// is the raw-buffer format of the gfx9 family: no swizzle, no stride, 32-bit offsets).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+// Offset that lies outside every buffer: the load returns zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// One 16-byte load per lane from buffer r at byte offset voff into LDS (lane i's data lands at
+// lds_wave_base + 16 i; the base must be uniform across the wave).  Offsets past the buffer
+// read as zero.  Unlike the global form it is not a FLAT instruction, so the compiler does not
+// have to assume it may touch LDS through a generic address, and keeps counting this wave's
+// outstanding LDS reads exactly while it is in flight.
+__device__ __forceinline__ void load_lds16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voff,
+                                             0, 0, 0);
 }
 
 }  // namespace

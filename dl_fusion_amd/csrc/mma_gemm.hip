@@ -43,7 +43,10 @@ constexpr int kRowsPerLoad = 16;   // one load instruction fills 1 KB = 16 rows
 // Zero-initialised device memory read by lanes whose chunk is padding.
 __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64];
 
-enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2 };
+// Operand A modes: dense rows read through a buffer resource per tile panel (32-bit offsets,
+// rows below 8 MB), dense rows read by 64-bit global addresses (longer rows), or gathered
+// from an NHWC convolution input.
+enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2, kDenseWide = 3 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1, bool REG_ = false,
           int SCHED_ = 0>
@@ -139,6 +142,11 @@ struct Frag<1> {   // fp8 e4m3: 64 K per MFMA; a lane supplies 32 values (two ch
 template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const int tiles_m,
                                                           const int tiles_n) {
+    constexpr bool DENSE = AMODE == kDense || AMODE == kDenseWide;
+    // dense operands as buffers: the LDS-DMA loads are then not FLAT instructions, which
+    // keeps the compiler's count of outstanding LDS reads exact while they are in flight, and
+    // the offsets are 32-bit (the register path keeps its global loads)
+    constexpr bool BUF = AMODE == kDense && !TS::REG;
     constexpr int CE = 16 / ELEM;                 // elements per 16-byte chunk
     constexpr int KE = kRowBytes / ELEM;          // K elements per slice
     constexpr int S = TS::STAGES;
@@ -170,14 +178,14 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     const uint8_t* a_ptr[TS::LA];     // dense: row base + logical chunk offset
     int a_lchunk[TS::LA];             // logical chunk of this lane's slot
     bool a_rowok[TS::LA];
-    int a_pix[AMODE != kDense ? TS::LA : 1], a_h[AMODE != kDense ? TS::LA : 1], a_w[AMODE != kDense ? TS::LA : 1];
+    int a_pix[!DENSE ? TS::LA : 1], a_h[!DENSE ? TS::LA : 1], a_w[!DENSE ? TS::LA : 1];
 #pragma unroll
     for (int j = 0; j < TS::LA; ++j) {
         const int r = (wave * TS::LA + j) * kRowsPerLoad + prow;
         const int64_t m = m0 + r;
         a_rowok[j] = m < M;
         a_lchunk[j] = swz_chunk(r, pch);          // the swizzle is an involution
-        if constexpr (AMODE == kDense) {
+        if constexpr (DENSE) {
             a_ptr[j] = a_bytes + (a_rowok[j] ? m : 0) * row_bytes + a_lchunk[j] * 16;
         } else {
             const int mm = static_cast<int>(a_rowok[j] ? m : 0);
@@ -201,6 +209,22 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     }
 
     const void* const zp = g_zero_page;   // kept in registers across the loop
+    // buffer form: this tile's A and B panels; rows past M or N lie outside and read zeros.
+    // The host uses it only while 256 rows span less than 2 GB, so every offset fits.
+    const int64_t a_rows = M - m0 < TS::BM ? M - m0 : TS::BM;
+    const int b_rows = N - n0 < TS::BN ? N - n0 : TS::BN;
+    const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(a_bytes + m0 * row_bytes, static_cast<uint32_t>(a_rows * row_bytes));
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        buffer_rsrc(b_bytes + static_cast<int64_t>(n0) * row_bytes, static_cast<uint32_t>(b_rows * row_bytes));
+    uint32_t a_off[BUF ? TS::LA : 1], b_off[BUF ? TS::LB : 1];
+    if constexpr (BUF) {
+#pragma unroll
+        for (int j = 0; j < TS::LA; ++j)
+            a_off[j] = static_cast<uint32_t>(((wave * TS::LA + j) * kRowsPerLoad + prow) * row_bytes + a_lchunk[j] * 16);
+#pragma unroll
+        for (int j = 0; j < TS::LB; ++j)
+            b_off[j] = static_cast<uint32_t>(((wave * TS::LB + j) * kRowsPerLoad + prow) * row_bytes + b_lchunk[j] * 16);
+    }
     // register staging for the REG path: two sets of this lane's 16-byte pieces of a slice
     u32x4_t rv[TS::REG ? 2 : 1][TS::LA + TS::LB];
     // Issues this lane's loads of slice kt (kt may exceed the last slice: then all zero
@@ -239,6 +263,20 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
                 const int64_t off = (static_cast<int64_t>(a_pix[j] + r * p.W + s) * p.Cin + ci) * ELEM;
                 sink(j, ok ? static_cast<const void*>(a_bytes + off) : zp, sA + (wave * TS::LA + j) * 1024);
             }
+        } else if constexpr (BUF) {
+#pragma unroll
+            for (int j = 0; j < TS::LA; ++j) {
+                const bool ok = kbase + a_lchunk[j] * CE < K;
+                load_lds16_buf(a_rsrc, ok ? a_off[j] + static_cast<uint32_t>(kt * kRowBytes) : kOutOfRange,
+                               sA + (wave * TS::LA + j) * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < TS::LB; ++j) {
+                const bool ok = kbase + b_lchunk[j] * CE < K;
+                load_lds16_buf(b_rsrc, ok ? b_off[j] + static_cast<uint32_t>(kt * kRowBytes) : kOutOfRange,
+                               sB + (wave * TS::LB + j) * 1024);
+            }
+            return;
         } else {
 #pragma unroll
             for (int j = 0; j < TS::LA; ++j) {
@@ -651,25 +689,39 @@ int mma_tile_cols(int tile) {
     }
 }
 
+// The buffer form holds while a 256-row panel spans less than 2 GB (rows under 8 MB); longer
+// rows take the global-address form, which has the six basic tiles only.
+bool dense_buffer_ok(const MmaArgs& a, int elem) { return static_cast<int64_t>(a.K) * elem < (int64_t(1) << 23); }
+int wide_tile(int tile) { return tile <= kTile256x128 ? tile : static_cast<int>(kTile256x256); }
+
 hipError_t launch_mma_bf16(const MmaArgs& a, bool conv, int act, int tile, hipStream_t s) {
-    if (!conv) return launch_bf16_act<kDense>(a, act, tile, s);
+    if (!conv) {
+        if (dense_buffer_ok(a, 2)) return launch_bf16_act<kDense>(a, act, tile, s);
+        return launch_bf16_act<kDenseWide>(a, act, wide_tile(tile), s);
+    }
     // a 64-byte slice (32 bf16) stays inside one kernel tap when Cin % 32 == 0
     if (a.Cin % 32 == 0) return launch_bf16_act<kConvAligned>(a, act, tile, s);
     return launch_bf16_act<kConvGeneric>(a, act, tile, s);
 }
 
-hipError_t launch_mma_fp8(const MmaArgs& a, int act, int out, int tile, hipStream_t s) {
-    if (out == kOutF32) return act == kActNone ? launch_tile<1, kDense, kActNone, kOutF32>(a, tile, s)
+template <int AMODE>
+hipError_t launch_fp8_mode(const MmaArgs& a, int act, int out, int tile, hipStream_t s) {
+    if (out == kOutF32) return act == kActNone ? launch_tile<1, AMODE, kActNone, kOutF32>(a, tile, s)
                                                : hipErrorInvalidValue;
     if (out == kOutFp8) {
-        if (act == kActNone) return launch_tile<1, kDense, kActNone, kOutFp8>(a, tile, s);
-        if (act == kActRelu) return launch_tile<1, kDense, kActRelu, kOutFp8>(a, tile, s);
+        if (act == kActNone) return launch_tile<1, AMODE, kActNone, kOutFp8>(a, tile, s);
+        if (act == kActRelu) return launch_tile<1, AMODE, kActRelu, kOutFp8>(a, tile, s);
     }
     if (out == kOutBf16) {
-        if (act == kActNone) return launch_tile<1, kDense, kActNone, kOutBf16>(a, tile, s);
-        if (act == kActRelu) return launch_tile<1, kDense, kActRelu, kOutBf16>(a, tile, s);
+        if (act == kActNone) return launch_tile<1, AMODE, kActNone, kOutBf16>(a, tile, s);
+        if (act == kActRelu) return launch_tile<1, AMODE, kActRelu, kOutBf16>(a, tile, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_mma_fp8(const MmaArgs& a, int act, int out, int tile, hipStream_t s) {
+    if (dense_buffer_ok(a, 1)) return launch_fp8_mode<kDense>(a, act, out, tile, s);
+    return launch_fp8_mode<kDenseWide>(a, act, out, wide_tile(tile), s);
 }
 
 }  // namespace dlf

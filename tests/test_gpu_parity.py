@@ -293,6 +293,57 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
         assert oracle.rel_error(oracle.widen(host(yu, "bf16"), "bf16"), ref) <= TOL_UNFUSED["bf16"]
 
 
+# Rows of 8 MB or more are past the 32-bit offsets of the buffer-resource loads: the library
+# reads them with 64-bit global addresses and the basic tiles (a tuned tile falls back to
+# 256 x 256).  One K just past that limit per input type, on the default, a tuned and a small
+# tile; the fp8 case draws small e4m3 codes directly, with an output scale that keeps the
+# codes unsaturated.
+WIDE_K = [
+    (3, dict(m=3, n=40, k=(1 << 22) + 32, act="gelu_tanh", bias=True)),
+    (4, dict(m=3, n=40, k=(1 << 23) + 16, out_scale=128.0)),
+]
+
+
+def wide_fp8_inputs(wl):
+    """fp8 inputs at a very large K without quantising normals (slow at this size): e4m3 codes
+    of magnitude 0.5 .. 1.875 with random signs, unit scales, and the BN parameters the seeded
+    generator draws for the same output channels."""
+    inp = workloads.generate(workloads.workload(4, m=wl.m, n=wl.n, k=16))
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 1))
+    def codes(shape):
+        return (rng.integers(0x30, 0x40, shape, dtype=np.uint8) | (rng.integers(0, 2, shape, dtype=np.uint8) << 7))
+    inp.update(workload=wl, x=codes((wl.m, wl.k)), w=codes((wl.n, wl.k)), s_x=1.0, s_w=1.0,
+               s_y=float(np.float32(wl.out_scale)))
+    return inp
+
+
+@pytest.mark.parametrize("i", range(len(WIDE_K)))
+def test_gemm_rows_past_the_buffer_range(i):
+    idx, over = WIDE_K[i]
+    wl = workloads.workload(idx, **over)
+    inp = workloads.generate(wl) if idx == 3 else wide_fp8_inputs(wl)
+    rows = np.arange(wl.m)
+    ref = gemm_reference(inp, rows) if idx == 3 else fp8_reference(inp, rows)[0]
+    L = layers().make_layer(inp, with_unfused=False)
+    for tile in (None, 12, 1):
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"wide-row gemm {wl} tile={tile}")
+        dt = torch.bfloat16 if idx == 3 else torch.uint8
+        buf, y = guarded((wl.m, wl.n), dt)
+        L.forward(y=y)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, y.numel())
+        if idx == 3:
+            err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+            assert err <= TOL["bf16"], (tile, err)
+        else:
+            assert_codes_within_one(host(y, "fp8"), ref)
+    os.environ.pop("DLF_TILE", None)
+
+
 # ---------------------------------------------------------------------------
 # fp8 GEMM + scale/shift + ReLU + static e4m3 quantisation
 # ---------------------------------------------------------------------------
