@@ -307,7 +307,6 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
     if (wave >= 4) {
         // ================= producers =================
         const int pw = wave - 4, ptid = tid - 256;
-        const void* const zp = g_halo_zero;
         const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
         const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
         uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
@@ -315,14 +314,17 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
         // load l = pw + 4 n is tap l / 8, rows 8 (l % 8) .. +7, and l % 8 is pw or pw + 4.  Loads
         // 0..5 (taps 0..2) go out first, before any halo address is computed, loads 6..17 (taps
         // 3..8) after the first halo: the first tile starts once taps 0..2 and its halo are in.
+        // (all loads use the buffer form: the 64 weight rows and each tile's image as buffers,
+        // with halo positions outside the image at an offset past the end, which reads zeros)
         const int wr0 = pw * 8 + (lane >> 3), wr1 = wr0 + 32;
-        const uint8_t* const w0 = wb + (static_cast<int64_t>(c0 + wr0) * 576 + wchunk(wr0, lane & 7) * 8) * 2;
-        const uint8_t* const w1 = wb + (static_cast<int64_t>(c0 + wr1) * 576 + wchunk(wr1, lane & 7) * 8) * 2;
+        const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(wb + static_cast<int64_t>(c0) * 576 * 2, 64 * 576 * 2);
+        const uint32_t w0 = static_cast<uint32_t>((wr0 * 576 + wchunk(wr0, lane & 7) * 8) * 2);
+        const uint32_t w1 = static_cast<uint32_t>((wr1 * 576 + wchunk(wr1, lane & 7) * 8) * 2);
         auto load_weights = [&](auto n0_c, auto n1_c) {
             static_for<decltype(n0_c)::value, decltype(n1_c)::value>([&](auto n_c) {
                 constexpr int n = decltype(n_c)::value;
                 const int l = pw + 4 * n, tap = l >> 3;
-                load_lds16(((l & 7) < 4 ? w0 : w1) + tap * 128, smem + tap * kWStage + (l & 7) * 1024);
+                load_lds16_buf(wrs, ((l & 7) < 4 ? w0 : w1) + tap * 128, smem + tap * kWStage + (l & 7) * 1024);
             });
         };
         load_weights(std::integral_constant<int, 0>{}, std::integral_constant<int, 6>{});
@@ -350,13 +352,15 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
             const int nhi = (nhp * 128 + 1023) >> 10;
             // rows of the halo inside the image: hr in [rlo, rhi)
             const int rlo = h0 == 0 ? 1 : 0, rhi = min(the + 2, H - h0 + 1);
-            const uint8_t* const xrow = xb + (static_cast<int64_t>(img) * H + h0 - 1) * W * 128;
+            const __amdgpu_buffer_rsrc_t xr =
+                buffer_rsrc(xb + static_cast<int64_t>(img) * H * W * 128, static_cast<uint32_t>(H * W * 128));
+            const int row0 = (h0 - 1) * W * 128;   // halo pixel (0, 0) sits one row above h0
             const int q0 = 8 * pw + (lane >> 3);
 #pragma unroll
             for (int n = 0; n < kRLoads; ++n) {
                 if (pw + 4 * n >= nhi) break;
                 const bool ok = ((colok >> n) & 1u) && q0 + 32 * n < nhp && hrow[n] >= rlo && hrow[n] < rhi;
-                load_lds16(ok ? static_cast<const void*>(xrow + voff[n]) : zp, buf + (pw + 4 * n) * 1024);
+                load_lds16_buf(xr, ok ? static_cast<uint32_t>(row0 + voff[n]) : kOutOfRange, buf + (pw + 4 * n) * 1024);
             }
         };
         // staged output of spatial tile st (in buf) -> y; lane handles chunk ptid % 8 of rows
@@ -848,7 +852,8 @@ bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, Ha
     // Cin = 64: resident weights when 32 workgroups per XCD divide evenly among the output
     // tiles and a halo of at least one row fits its 44 KB buffer
     const int co_tiles = Cout / kCo;
-    if (resident_ok && Cin == 64 && 32 % co_tiles == 0 && W <= 256 && 3 * (W + 2) * 128 <= kRHalo) {
+    if (resident_ok && Cin == 64 && 32 % co_tiles == 0 && W <= 256 && 3 * (W + 2) * 128 <= kRHalo &&
+        static_cast<int64_t>(H) * W * 128 < (int64_t(1) << 31)) {
         int th = 256 / W;
         if (th > H) th = H;
         while (th > 1 && (th + 2) * (W + 2) * 128 > kRHalo) --th;

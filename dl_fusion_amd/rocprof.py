@@ -52,7 +52,7 @@ def fused_kernel(wl) -> str:
         if (wl.kh, wl.kw, wl.stride, wl.pad) != (3, 3, 1, 1) or wl.cout % 32 != 0:
             return "mma_kernel"
         if wl.cout % 64 == 0 and wl.cin == 64 and 32 % (wl.cout // 64) == 0 and wl.w <= 256 \
-                and 3 * (wl.w + 2) * 128 <= 44 * 1024:
+                and 3 * (wl.w + 2) * 128 <= 44 * 1024 and wl.h * wl.w * 128 < 2 ** 31:
             return "conv_halo_res_kernel"
         if wl.cin % 64 == 0 and wl.h * wl.w <= 256 and (wl.h + 2) * (wl.w + 2) * 128 <= 32 * 1024 \
                 and wl.n * (wl.cout // 32) >= 128:
