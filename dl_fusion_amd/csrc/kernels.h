@@ -33,7 +33,9 @@ enum MmaTile : int {
     kTile64x64 = 3,     // 2x2 waves of 32x32
     kTile128x64 = 4,    // 2x2 waves of 64x32
     kTile256x128 = 5,   // 2x2 waves of 128x64
-    // dense-GEMM variants for tuning: eight waves (two per SIMD) or three stages
+    // dense-GEMM pipeline variants (DLF_TILE selects one): eight waves (two per SIMD), three
+    // or five stages, one barrier per two K slices, register staging.  kTile256x256w8ab2 is
+    // the default wherever the cost model picks 256 x 256 for a dense GEMM.
     kTile256x256w8 = 6,   // 2x4 waves of 128x64
     kTile256x256w8t = 7,  // 4x2 waves of 64x128
     kTile256x256s3 = 8,   // 2x2 waves of 128x128, three stages
@@ -44,7 +46,7 @@ enum MmaTile : int {
     kTile256x256w8s5 = 13,   // 4x2 waves of 64x128, five stages
     kTile256x256w8r = 14,    // 4x2 waves of 64x128, operands staged through registers
     kTile256x256w8ar = 15,   // 2x4 waves of 128x64, operands staged through registers
-    kTileCount = 23   // 16..22: schedule variants of the eight-wave tiles (tuning)
+    kTileCount = 16
 };
 int mma_tile_rows(int tile);
 int mma_tile_cols(int tile);

@@ -48,13 +48,8 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64];
 // from an NHWC convolution input.
 enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2, kDenseWide = 3 };
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1, bool REG_ = false,
-          int SCHED_ = 0>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1, bool REG_ = false>
 struct TileShape {
-    // SCHED 0: MFMAs interleaved one by one with LDS reads / loads; 1: compiler's own
-    // order; 2: loads and reads first, then the MFMA cluster; 3: as 0 with the wave's
-    // priority raised while it issues MFMAs
-    static constexpr int SCHED = SCHED_;
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int SPB = SPB_;                       // K slices consumed per barrier
     // REG: operand slices travel global -> registers -> LDS (global_load_dwordx4 +
@@ -363,18 +358,8 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     };
     constexpr int MF = TS::FM * TS::FN, R = (TS::FM + TS::FN) * F::kReads;
     auto schedule = [&](auto r_c, auto g_c, auto w_c) {
-        constexpr int RR = decltype(r_c)::value, GG = decltype(g_c)::value, WW = decltype(w_c)::value;
-        if constexpr (TS::SCHED == 0 || TS::SCHED == 3) {
-            interleave<MF, RR, GG, WW>();
-        } else if constexpr (TS::SCHED == 2 || TS::SCHED == 4) {
-            if constexpr (GG > 0) __builtin_amdgcn_sched_group_barrier(0x020, GG, 0);
-            if constexpr (WW > 0) __builtin_amdgcn_sched_group_barrier(0x200, WW, 0);
-            if constexpr (RR > 0) __builtin_amdgcn_sched_group_barrier(0x100, RR, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-        }
+        interleave<MF, decltype(r_c)::value, decltype(g_c)::value, decltype(w_c)::value>();
     };
-    auto prio_hi = [&]() { if constexpr (TS::SCHED == 3 || TS::SCHED == 4) __builtin_amdgcn_s_setprio(2); };
-    auto prio_lo = [&]() { if constexpr (TS::SCHED == 3 || TS::SCHED == 4) __builtin_amdgcn_s_setprio(0); };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -409,16 +394,12 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         const int kt = g0 / F::kSteps + slice_in_iter;
         if constexpr (same_slice) {
             read_frags(std::integral_constant<int, n>{}, kt, st + 1);
-            prio_hi();
             mma_all(std::integral_constant<int, c>{});
-            prio_lo();
             schedule(std::integral_constant<int, R>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
         } else if constexpr (!transition) {
             // the next slice landed at the previous transition
             read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
-            prio_hi();
             mma_all(std::integral_constant<int, c>{});
-            prio_lo();
             schedule(std::integral_constant<int, R>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
         } else if constexpr (TS::REG) {
             // slice kt+2 has reached its registers (kt+3 may be in flight) and this wave's
@@ -430,9 +411,7 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
             write_slice(std::integral_constant<int, set>{}, kt + 2);
             load_slice(std::integral_constant<int, set>{}, kt + 4);
             read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
-            prio_hi();
             mma_all(std::integral_constant<int, c>{});
-            prio_lo();
             schedule(std::integral_constant<int, R>{}, std::integral_constant<int, LOADS>{},
                      std::integral_constant<int, LOADS>{});
         } else {
@@ -441,9 +420,7 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
 #pragma unroll
             for (int i = 0; i < SPB; ++i) issue_slice(kt + 1 - SPB + S + i);
             read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
-            prio_hi();
             mma_all(std::integral_constant<int, c>{});
-            prio_lo();
             schedule(std::integral_constant<int, R>{}, std::integral_constant<int, SPB * LOADS>{},
                      std::integral_constant<int, 0>{});
         }
@@ -599,13 +576,6 @@ using T256x256w8ab2 = TileShape<256, 256, 2, 4, 4, 2>; // 8 waves of 128x64, bar
 using T256x256w8s5 = TileShape<256, 256, 4, 2, 5>;     // 8 waves of 64x128, five stages
 using T256x256w8r = TileShape<256, 256, 4, 2, 3, 1, true>;   // 8 waves of 64x128, register path
 using T256x256w8ar = TileShape<256, 256, 2, 4, 3, 1, true>;  // 8 waves of 128x64, register path
-using T256x256w8ab2s1 = TileShape<256, 256, 2, 4, 4, 2, false, 1>;
-using T256x256w8ab2s2 = TileShape<256, 256, 2, 4, 4, 2, false, 2>;
-using T256x256w8ab2s3 = TileShape<256, 256, 2, 4, 4, 2, false, 3>;
-using T256x256w8b2s2 = TileShape<256, 256, 4, 2, 4, 2, false, 2>;
-using T256x256w8as2 = TileShape<256, 256, 2, 4, 4, 1, false, 2>;
-using T256x256w8ab2s4 = TileShape<256, 256, 2, 4, 4, 2, false, 4>;
-using T256x256w8ars2 = TileShape<256, 256, 2, 4, 3, 1, true, 2>;
 
 template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 hipError_t launch_one(const MmaArgs& a, hipStream_t stream) {
@@ -633,13 +603,6 @@ hipError_t launch_tile(const MmaArgs& a, int tile, hipStream_t s) {
     if constexpr (AMODE == kDense) {
         switch (tile) {
             case kTile256x256w8r: return launch_one<ELEM, T256x256w8r, AMODE, ACT, OUT>(a, s);
-            case 16: return launch_one<ELEM, T256x256w8ab2s1, AMODE, ACT, OUT>(a, s);
-            case 17: return launch_one<ELEM, T256x256w8ab2s2, AMODE, ACT, OUT>(a, s);
-            case 18: return launch_one<ELEM, T256x256w8ab2s3, AMODE, ACT, OUT>(a, s);
-            case 19: return launch_one<ELEM, T256x256w8b2s2, AMODE, ACT, OUT>(a, s);
-            case 20: return launch_one<ELEM, T256x256w8as2, AMODE, ACT, OUT>(a, s);
-            case 21: return launch_one<ELEM, T256x256w8ab2s4, AMODE, ACT, OUT>(a, s);
-            case 22: return launch_one<ELEM, T256x256w8ars2, AMODE, ACT, OUT>(a, s);
             case kTile256x256w8ar: return launch_one<ELEM, T256x256w8ar, AMODE, ACT, OUT>(a, s);
             case kTile256x256w8: return launch_one<ELEM, T256x256w8, AMODE, ACT, OUT>(a, s);
             case kTile256x256w8t: return launch_one<ELEM, T256x256w8t, AMODE, ACT, OUT>(a, s);
@@ -671,8 +634,7 @@ int mma_tile_rows(int tile) {
     switch (tile) {
         case kTile256x256: case kTile256x128: case kTile256x64: case kTile256x256w8: case kTile256x256w8t:
         case kTile256x256s3: case kTile256x128s3: case kTile256x128w8: case kTile256x256w8b2:
-        case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r: case kTile256x256w8ar:
-        case 16: case 17: case 18: case 19: case 20: case 21: case 22: return 256;
+        case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r: case kTile256x256w8ar: return 256;
         case kTile128x128: case kTile128x64: return 128;
         case kTile64x64: return 64;
         default: return 0;
@@ -683,7 +645,7 @@ int mma_tile_cols(int tile) {
     switch (tile) {
         case kTile256x256: case kTile256x256w8: case kTile256x256w8t: case kTile256x256s3:
         case kTile256x256w8b2: case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r:
-        case kTile256x256w8ar: case 16: case 17: case 18: case 19: case 20: case 21: case 22: return 256;
+        case kTile256x256w8ar: return 256;
         case kTile256x128: case kTile128x128: case kTile256x128s3: case kTile256x128w8: return 128;
         default: return 64;
     }
