@@ -57,6 +57,7 @@ def _load():
         "orc_add": (None, [_i64, _dp, _dp, _dp]),
         "orc_relu": (None, [_i64, _dp, _dp]),
         "orc_gelu_tanh": (None, [_i64, _dp, _dp]),
+        "orc_gelu_erf": (None, [_i64, _dp, _dp]),
         "orc_fold_bn": (None, [_i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]),
         "orc_e4m3_to_double": (ctypes.c_double, [ctypes.c_int]),
         "orc_e4m3_from_double": (ctypes.c_int, [ctypes.c_double]),
@@ -215,11 +216,21 @@ def gelu_tanh(u):
     return out
 
 
+def gelu_erf(u):
+    """Exact GELU, u Phi(u) ([RFC] §2.1, §2.4)."""
+    u = _d(u)
+    out = np.empty_like(u)
+    _load().orc_gelu_erf(u.size, _ptr(u), _ptr(out))
+    return out
+
+
 def activation(u, act: str):
     if act == "relu":
         return relu(u)
     if act == "gelu_tanh":
         return gelu_tanh(u)
+    if act == "gelu_erf":
+        return gelu_erf(u)
     if act == "none":
         return _d(u)
     raise ValueError(act)
@@ -275,6 +286,18 @@ def gemm_bias_act(inp: dict, rows=None):
     if inp.get("bias") is not None:
         y = bias_add(y, inp["bias"])
     return activation(y, wl.act)
+
+
+def gemm_bias_act_split(inp: dict, parts: int, rows=None):
+    """One MatMul over weights concatenated along the output dimension at load, with bias and
+    activation, split by columns into `parts` equal tensors ([OPPL] §3.2: the Q, K and V
+    projections as one [3 h, h] GEMM whose result is cut into Q, K and V)."""
+    y = gemm_bias_act(inp, rows)
+    n = y.shape[1]
+    if parts < 1 or n % parts:
+        raise ValueError("columns must split evenly")
+    w = n // parts
+    return [np.ascontiguousarray(y[:, p * w:(p + 1) * w]) for p in range(parts)]
 
 
 def fp8_gemm_bn_relu_quant(inp: dict, rows=None):

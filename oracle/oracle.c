@@ -173,6 +173,22 @@ void orc_gelu_tanh(int64_t count, const double *in, double *out)
     }
 }
 
+/* GELU, exact (erf) form, [RFC] §2.1 (the GELU type of the quantised MatMul +
+ * GELU operator may be tanh or erf) and §2.4 (erf GELU as its own operator).
+ * The pages do not print it; it is the Gaussian CDF form
+ *   gelu(u) = u Phi(u) = 0.5 u (1 + erf(u / sqrt(2))) = 0.5 u erfc(-u / sqrt(2)),
+ * evaluated through erfc, which keeps full relative precision in the negative
+ * tail where 1 + erf cancels. */
+void orc_gelu_erf(int64_t count, const double *in, double *out)
+{
+    const double r2 = 1.0 / sqrt(2.0);
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        const double u = in[i];
+        out[i] = 0.5 * u * erfc(-u * r2);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* BN folding, used only as a self-check of the unfolded path.               */
 /* [OPPL] §3.1: scale = gamma / sqrt(var + eps); W_new = W * scale per output */

@@ -249,6 +249,44 @@ def test_gelu_tanh_identities_and_library():
     assert abs(oracle.gelu_tanh(np.array([-30.0]))[0]) < 1e-300
 
 
+def test_gelu_erf_is_u_times_normal_cdf():
+    """Exact GELU ([RFC] §2.1, §2.4) = u Phi(u): pinned to scipy's normal CDF, the odd symmetry
+    of erf, a textbook value, and a measurable gap to the tanh form (which must not stand in)."""
+    from scipy.stats import norm
+    rng = np.random.default_rng(11)
+    u = np.concatenate([rng.standard_normal(2000) * 4, np.linspace(-12, 12, 241)])
+    g = oracle.gelu_erf(u)
+    np.testing.assert_allclose(g, u * norm.cdf(u), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(g - oracle.gelu_erf(-u), u, rtol=1e-14, atol=1e-15)   # erf is odd
+    assert oracle.gelu_erf(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.gelu_erf(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15   # Phi(1)
+    assert oracle.gelu_erf(np.array([40.0]))[0] == 40.0
+    assert abs(oracle.gelu_erf(np.array([-40.0]))[0]) < 1e-300
+    gap = np.abs(g - oracle.gelu_tanh(u))
+    assert 1e-4 < gap.max() < 1e-3, gap.max()
+
+
+def test_split_gemm_equals_separate_projections():
+    """[OPPL] §3.2: one GEMM over [W_q; W_k; W_v] cut into three column blocks equals the three
+    projections computed separately (here with numpy on the blocks, not the oracle's matmul)."""
+    for act in ("none", "gelu_erf"):
+        wl = workloads.workload(3, m=7, n=3 * 16, k=40, act=act, bias=True)
+        inp = workloads.generate(wl)
+        parts = oracle.gemm_bias_act_split(inp, 3)
+        x = oracle.widen(inp["x"], "bf16")
+        w = oracle.widen(inp["w"], "bf16")
+        for p, got in enumerate(parts):
+            sl = slice(16 * p, 16 * (p + 1))
+            ref = x @ w[sl].T + inp["bias"][sl].astype(np.float64)
+            if act == "gelu_erf":
+                from scipy.stats import norm
+                ref = ref * norm.cdf(ref)
+            assert got.shape == (7, 16)
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.gemm_bias_act_split(inp, 5)
+
+
 # ---------------------------------------------------------------------------
 # O6 / O7: the fp8 e4m3 codec and the exact fp8 product
 # ---------------------------------------------------------------------------
