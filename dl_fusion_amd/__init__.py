@@ -31,10 +31,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 # ---------------------------------------------------------------------------
 DLF_OK, DLF_ERR_INVALID_ARG, DLF_ERR_UNSUPPORTED, DLF_ERR_HIP, DLF_ERR_ALIAS = 0, -1, -2, -3, -4
 DLF_F32, DLF_BF16, DLF_FP8_E4M3 = 0, 1, 2
-DLF_ACT_NONE, DLF_ACT_RELU, DLF_ACT_GELU_TANH = 0, 1, 2
+DLF_ACT_NONE, DLF_ACT_RELU, DLF_ACT_GELU_TANH, DLF_ACT_GELU_ERF = 0, 1, 2, 3
 
 DTYPES = {"f32": DLF_F32, "bf16": DLF_BF16, "fp8": DLF_FP8_E4M3}
-ACTS = {"none": DLF_ACT_NONE, "relu": DLF_ACT_RELU, "gelu_tanh": DLF_ACT_GELU_TANH}
+ACTS = {"none": DLF_ACT_NONE, "relu": DLF_ACT_RELU, "gelu_tanh": DLF_ACT_GELU_TANH, "gelu_erf": DLF_ACT_GELU_ERF}
 
 
 class dlf_conv_desc(ctypes.Structure):
@@ -69,6 +69,8 @@ _SIGS = {
     "dlf_bn_scale_shift": [_i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_double, _vp, _vp],
     "dlf_conv_fused": [ctypes.POINTER(dlf_conv_desc), _vp, _vp, _vp, _vp, _vp, _vp],
     "dlf_gemm_fused": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "dlf_gemm_fused_split": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, _vp, _vp, ctypes.c_int32,
+                             ctypes.POINTER(_vp), _vp],
     "dlf_conv_plain": [ctypes.POINTER(dlf_conv_desc), _vp, _vp, _vp, _vp, _vp],
     "dlf_gemm_plain": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, ctypes.c_float, _vp, _vp],
     "dlf_bn_apply": [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp],
@@ -178,6 +180,13 @@ def dlf_conv_fused(desc, x, w, bias, residual, y, stream=None):
 def dlf_gemm_fused(desc, a, b, col_scale, col_shift, residual, c, stream=None):
     _check(_lib.dlf_gemm_fused(ctypes.byref(desc), _dev(a), _dev(b), _dev(col_scale), _dev(col_shift),
                                _dev(residual), _dev(c), _stream(stream)), "dlf_gemm_fused")
+
+
+def dlf_gemm_fused_split(desc, a, b, col_scale, col_shift, outs, stream=None):
+    """One GEMM, its columns stored to len(outs) tensors (see include/dlfusion.h)."""
+    arr = (_vp * max(1, len(outs)))(*[_dev(o) for o in outs])
+    _check(_lib.dlf_gemm_fused_split(ctypes.byref(desc), _dev(a), _dev(b), _dev(col_scale), _dev(col_shift),
+                                     len(outs), arr, _stream(stream)), "dlf_gemm_fused_split")
 
 
 def dlf_conv_plain(desc, x, w, conv_bias, y, stream=None):

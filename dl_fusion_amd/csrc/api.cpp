@@ -47,7 +47,9 @@ size_t dtype_size(dlf_dtype d) {
 }
 
 bool valid_dtype(int d) { return d == DLF_F32 || d == DLF_BF16 || d == DLF_FP8_E4M3; }
-bool valid_act(int a) { return a == DLF_ACT_NONE || a == DLF_ACT_RELU || a == DLF_ACT_GELU_TANH; }
+bool valid_act(int a) {
+    return a == DLF_ACT_NONE || a == DLF_ACT_RELU || a == DLF_ACT_GELU_TANH || a == DLF_ACT_GELU_ERF;
+}
 
 // Byte ranges [p, p + n) overlap?
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -89,7 +91,12 @@ int pick_tile(int64_t M, int64_t N, bool dense) {
 }
 
 int act_code(dlf_act a) {
-    return a == DLF_ACT_RELU ? dlf::kActRelu : a == DLF_ACT_GELU_TANH ? dlf::kActGelu : dlf::kActNone;
+    switch (a) {
+        case DLF_ACT_RELU: return dlf::kActRelu;
+        case DLF_ACT_GELU_TANH: return dlf::kActGelu;
+        case DLF_ACT_GELU_ERF: return dlf::kActGeluErf;
+        default: return dlf::kActNone;
+    }
 }
 
 // Single round-to-nearest-even of a binary64 value to bfloat16 (no pass
@@ -325,9 +332,17 @@ dlf_status dlf_conv_plain(const dlf_conv_desc* d, const void* x, const void* w, 
     return launch_conv(d, g, x, w, conv_bias, nullptr, y, stream, "dlf_conv_plain");
 }
 
-dlf_status dlf_gemm_fused(const dlf_gemm_desc* d, const void* a, const void* b, const float* col_scale,
-                          const float* col_shift, const void* residual, void* c, void* stream) {
-    dlf_status st = check_gemm_common(d, a, b, c);
+}  // extern "C"
+
+namespace {
+
+// dlf_gemm_fused and its split-store form: parts == 0 stores c as [m][n]; parts >= 1 stores
+// columns [p n/parts, (p+1) n/parts) to outs[p].
+dlf_status gemm_fused_impl(const dlf_gemm_desc* d, const void* a, const void* b, const float* col_scale,
+                           const float* col_shift, const void* residual, void* c, int parts, void* const* outs,
+                           void* stream, const char* what) {
+    void* const first = parts > 0 ? (outs ? outs[0] : nullptr) : c;
+    dlf_status st = check_gemm_common(d, a, b, first);
     if (st != DLF_OK) return st;
     const bool bf16_path = d->in_dtype == DLF_BF16 && d->out_dtype == DLF_BF16;
     const bool fp8_path = d->in_dtype == DLF_FP8_E4M3 &&
@@ -339,24 +354,51 @@ dlf_status dlf_gemm_fused(const dlf_gemm_desc* d, const void* a, const void* b, 
                     residual ? "yes" : "no");
     if (d->out_dtype == DLF_FP8_E4M3 && (!std::isfinite(d->out_inv_scale) || !(d->out_inv_scale > 0.0f)))
         return fail(DLF_ERR_INVALID_ARG, "out_inv_scale must be finite and > 0");
+    const size_t in_es = dtype_size(d->in_dtype), out_es = dtype_size(d->out_dtype);
+    int part_cols = 0;
+    if (parts > 0) {
+        if (parts > 4) return fail(DLF_ERR_UNSUPPORTED, "at most 4 output parts");
+        if (residual) return fail(DLF_ERR_UNSUPPORTED, "the split store takes no residual");
+        if (d->n % parts != 0) return fail(DLF_ERR_INVALID_ARG, "n must split into %d equal parts", parts);
+        part_cols = static_cast<int>(d->n / parts);
+        if ((static_cast<size_t>(part_cols) * out_es) % 16 != 0)
+            return fail(DLF_ERR_UNSUPPORTED, "each part's row must be a whole number of 16-byte chunks");
+    }
     if (d->m == 0 || d->n == 0) return ok();
     if ((col_scale && !aligned16(col_scale)) || (col_shift && !aligned16(col_shift)) ||
         (residual && !aligned16(residual)))
         return fail(DLF_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-    const size_t in_es = dtype_size(d->in_dtype), out_es = dtype_size(d->out_dtype);
-    const size_t cbytes = static_cast<size_t>(d->m * d->n) * out_es;
-    if (overlaps(c, cbytes, a, static_cast<size_t>(d->m * d->k) * in_es) ||
-        overlaps(c, cbytes, b, static_cast<size_t>(d->n * d->k) * in_es) ||
-        overlaps(c, cbytes, col_scale, static_cast<size_t>(d->n) * 4) ||
-        overlaps(c, cbytes, col_shift, static_cast<size_t>(d->n) * 4) || overlaps(c, cbytes, residual, cbytes))
-        return fail(DLF_ERR_ALIAS, "output overlaps an input");
+    const size_t abytes = static_cast<size_t>(d->m * d->k) * in_es, bbytes = static_cast<size_t>(d->n * d->k) * in_es;
+    auto clobbers_input = [&](const void* out, size_t bytes) {
+        return overlaps(out, bytes, a, abytes) || overlaps(out, bytes, b, bbytes) ||
+               overlaps(out, bytes, col_scale, static_cast<size_t>(d->n) * 4) ||
+               overlaps(out, bytes, col_shift, static_cast<size_t>(d->n) * 4) || overlaps(out, bytes, residual, bytes);
+    };
     dlf::MmaArgs x{};
+    if (parts > 0) {
+        const size_t pbytes = static_cast<size_t>(d->m) * part_cols * out_es;
+        for (int q = 0; q < parts; ++q) {
+            if (!outs[q] || !aligned16(outs[q]))
+                return fail(DLF_ERR_INVALID_ARG, "output part %d is NULL or not 16-byte aligned", q);
+            if (clobbers_input(outs[q], pbytes)) return fail(DLF_ERR_ALIAS, "output part %d overlaps an input", q);
+            for (int r = 0; r < q; ++r)
+                if (overlaps(outs[q], pbytes, outs[r], pbytes))
+                    return fail(DLF_ERR_ALIAS, "output parts %d and %d overlap", r, q);
+            x.outs[q] = outs[q];
+        }
+        x.parts = parts;
+        x.part_cols = part_cols;
+        x.c = outs[0];
+    } else {
+        if (clobbers_input(c, static_cast<size_t>(d->m * d->n) * out_es))
+            return fail(DLF_ERR_ALIAS, "output overlaps an input");
+        x.c = c;
+    }
     x.a = a;
     x.b = b;
     x.scale = col_scale;
     x.shift = col_shift;
     x.res = static_cast<const uint16_t*>(residual);
-    x.c = c;
     x.M = d->m;
     x.N = static_cast<int>(d->n);
     x.K = static_cast<int>(d->k);
@@ -364,9 +406,26 @@ dlf_status dlf_gemm_fused(const dlf_gemm_desc* d, const void* a, const void* b, 
     x.dequant = 1.0f;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int tile = pick_tile(d->m, d->n, true);
-    if (bf16_path) return hip_status(dlf::launch_mma_bf16(x, false, act_code(d->act), tile, s), "dlf_gemm_fused");
+    if (bf16_path) return hip_status(dlf::launch_mma_bf16(x, false, act_code(d->act), tile, s), what);
     const int out = d->out_dtype == DLF_FP8_E4M3 ? dlf::kOutFp8 : dlf::kOutBf16;
-    return hip_status(dlf::launch_mma_fp8(x, act_code(d->act), out, tile, s), "dlf_gemm_fused");
+    return hip_status(dlf::launch_mma_fp8(x, act_code(d->act), out, tile, s), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+dlf_status dlf_gemm_fused(const dlf_gemm_desc* d, const void* a, const void* b, const float* col_scale,
+                          const float* col_shift, const void* residual, void* c, void* stream) {
+    return gemm_fused_impl(d, a, b, col_scale, col_shift, residual, c, 0, nullptr, stream, "dlf_gemm_fused");
+}
+
+dlf_status dlf_gemm_fused_split(const dlf_gemm_desc* d, const void* a, const void* b, const float* col_scale,
+                                const float* col_shift, int32_t parts, void* const* outs, void* stream) {
+    if (parts < 1) return fail(DLF_ERR_INVALID_ARG, "parts must be >= 1");
+    if (!outs) return fail(DLF_ERR_INVALID_ARG, "outs is NULL");
+    return gemm_fused_impl(d, a, b, col_scale, col_shift, nullptr, nullptr, parts, outs, stream,
+                           "dlf_gemm_fused_split");
 }
 
 dlf_status dlf_gemm_plain(const dlf_gemm_desc* d, const void* a, const void* b, float dequant, void* y,

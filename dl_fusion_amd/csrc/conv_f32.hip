@@ -81,6 +81,7 @@ hipError_t launch_tc(const ConvF32Args& a, int act, hipStream_t s) {
         case kActNone: hipLaunchKernelGGL((conv_f32_kernel<TC, kActNone>), grid, dim3(256), 0, s, a); break;
         case kActRelu: hipLaunchKernelGGL((conv_f32_kernel<TC, kActRelu>), grid, dim3(256), 0, s, a); break;
         case kActGelu: hipLaunchKernelGGL((conv_f32_kernel<TC, kActGelu>), grid, dim3(256), 0, s, a); break;
+        case kActGeluErf: hipLaunchKernelGGL((conv_f32_kernel<TC, kActGeluErf>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -515,9 +515,9 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
                             v[2] += __uint_as_float(t.y << 16);
                             v[3] += __uint_as_float(t.y & 0xFFFF0000u);
                         }
-                        if constexpr (ACT == kActGelu) {
+                        if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+                            for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
                         }
                         uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
                         if constexpr (ACT == kActRelu) {
@@ -550,6 +550,10 @@ hipError_t launch_res(const HaloArgs& a, const HaloPlan& pl, int act, hipStream_
             break;
         case kActGelu:
             hipLaunchKernelGGL((conv_halo_res_kernel<WF, kActGelu>), dim3(kRBlocks), dim3(512), 0, s, a, pl.th,
+                               pl.row_tiles, pl.per_xcd);
+            break;
+        case kActGeluErf:
+            hipLaunchKernelGGL((conv_halo_res_kernel<WF, kActGeluErf>), dim3(kRBlocks), dim3(512), 0, s, a, pl.th,
                                pl.row_tiles, pl.per_xcd);
             break;
         default: return hipErrorInvalidValue;
@@ -801,9 +805,9 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
                 v[2] += __uint_as_float(rv[i][g].y << 16);
                 v[3] += __uint_as_float(rv[i][g].y & 0xFFFF0000u);
             }
-            if constexpr (ACT == kActGelu) {
+            if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+                for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
             }
             uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
             if constexpr (ACT == kActRelu) {
@@ -821,6 +825,7 @@ hipError_t launch_img(const HaloArgs& a, int act, hipStream_t s) {
         case kActNone: hipLaunchKernelGGL((conv_halo_img_kernel<kActNone>), grid, block, 0, s, a); break;
         case kActRelu: hipLaunchKernelGGL((conv_halo_img_kernel<kActRelu>), grid, block, 0, s, a); break;
         case kActGelu: hipLaunchKernelGGL((conv_halo_img_kernel<kActGelu>), grid, block, 0, s, a); break;
+        case kActGeluErf: hipLaunchKernelGGL((conv_halo_img_kernel<kActGeluErf>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -835,6 +840,9 @@ hipError_t launch_act(const HaloArgs& a, int th, int row_tiles, int act, hipStre
             break;
         case kActRelu:
             hipLaunchKernelGGL((conv_halo_kernel<WF, HALO_KB, kActRelu>), dim3(blocks), dim3(256), 0, s, a, th, row_tiles);
+            break;
+        case kActGeluErf:
+            hipLaunchKernelGGL((conv_halo_kernel<WF, HALO_KB, kActGeluErf>), dim3(blocks), dim3(256), 0, s, a, th, row_tiles);
             break;
         case kActGelu:
             hipLaunchKernelGGL((conv_halo_kernel<WF, HALO_KB, kActGelu>), dim3(blocks), dim3(256), 0, s, a, th, row_tiles);

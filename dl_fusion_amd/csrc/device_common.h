@@ -21,7 +21,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-enum : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
+enum : int { kActNone = 0, kActRelu = 1, kActGelu = 2, kActGeluErf = 3 };
 enum : int { kOutBf16 = 0, kOutFp8 = 1, kOutF32 = 2 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -43,6 +43,12 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     const float t = v * fmaf(0.044715f * v, v, 1.0f);                                   // v + 0.044715 v^3
     const float e = __builtin_amdgcn_exp2f(k * t);
     return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// GELU, exact form: v Phi(v) = 0.5 v erfc(-v / sqrt(2)), with the device library's erfc
+// (erfc keeps the negative tail free of the cancellation in 1 + erf).
+__device__ __forceinline__ float gelu_erf(float v) {
+    return 0.5f * v * erfcf(-0.70710678118654752440f * v);
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -67,6 +73,8 @@ __device__ __forceinline__ float activate(float v) {
         return v > 0.0f ? v : 0.0f;
     } else if constexpr (ACT == kActGelu) {
         return gelu_tanh(v);
+    } else if constexpr (ACT == kActGeluErf) {
+        return gelu_erf(v);
     } else {
         return v;
     }

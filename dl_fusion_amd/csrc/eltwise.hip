@@ -197,11 +197,13 @@ hipError_t launch_act(int64_t count, int dt, int act, const void* in, void* out,
     if (dt == 0) {
         if (act == kActNone) DLF_ACT_CASE(0, kActNone);
         else if (act == kActRelu) DLF_ACT_CASE(0, kActRelu);
-        else DLF_ACT_CASE(0, kActGelu);
+        else if (act == kActGelu) DLF_ACT_CASE(0, kActGelu);
+        else DLF_ACT_CASE(0, kActGeluErf);
     } else {
         if (act == kActNone) DLF_ACT_CASE(1, kActNone);
         else if (act == kActRelu) DLF_ACT_CASE(1, kActRelu);
-        else DLF_ACT_CASE(1, kActGelu);
+        else if (act == kActGelu) DLF_ACT_CASE(1, kActGelu);
+        else DLF_ACT_CASE(1, kActGeluErf);
     }
 #undef DLF_ACT_CASE
     return hipGetLastError();

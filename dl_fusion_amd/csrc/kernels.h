@@ -21,6 +21,10 @@ struct MmaArgs {
     int N, K;
     float out_inv_scale;    // fp8 output: fp32(1/s_y)
     float dequant;          // fp32 output of the plain fp8 GEMM: s_x * s_w
+    // split store (parts > 1): columns [p * part_cols, (p + 1) * part_cols) go to outs[p], each
+    // [M][part_cols]; part_cols is a multiple of one 16-byte chunk of output.  parts == 1: c.
+    int parts, part_cols;
+    void* outs[4];
     // convolution geometry (A gather); unused by the dense kernel
     int H, W, Cin, Ho, Wo, KW, SH, SW, PH, PW;
 };

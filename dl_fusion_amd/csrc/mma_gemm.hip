@@ -539,6 +539,22 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         }
         __syncthreads();
         // coalesced write-out: 16-byte chunks of the staged tile, row-major
+        if (p.parts > 1) {
+            // split store: a chunk lies in one part (the part width is a whole number of chunks)
+            const int pc = p.part_cols;
+            for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
+                const int ml = q / CPR, cc = q - ml * CPR;
+                const int64_t m = m0 + ml;
+                const int n = n0 + cc * (16 / OB);
+                if (m >= M || n >= N) continue;
+                const int part = (n >= pc) + (n >= 2 * pc) + (n >= 3 * pc);
+                uint8_t* const base = static_cast<uint8_t*>(part == 0 ? p.outs[0] : part == 1 ? p.outs[1]
+                                                            : part == 2 ? p.outs[2] : p.outs[3]);
+                *reinterpret_cast<u32x4_t*>(base + (m * pc + (n - part * pc)) * OB) =
+                    *reinterpret_cast<const u32x4_t*>(smem + ml * SROW + ((cc ^ (ml & XM)) << 4));
+            }
+            return;
+        }
         const bool vec_ok = ((static_cast<int64_t>(N) * OB) & 15) == 0;
         uint8_t* const cbytes = static_cast<uint8_t*>(p.c);
         for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
@@ -624,6 +640,7 @@ hipError_t launch_bf16_act(const MmaArgs& a, int act, int tile, hipStream_t s) {
         case kActNone: return launch_tile<2, AMODE, kActNone, kOutBf16>(a, tile, s);
         case kActRelu: return launch_tile<2, AMODE, kActRelu, kOutBf16>(a, tile, s);
         case kActGelu: return launch_tile<2, AMODE, kActGelu, kOutBf16>(a, tile, s);
+        case kActGeluErf: return launch_tile<2, AMODE, kActGeluErf, kOutBf16>(a, tile, s);
         default: return hipErrorInvalidValue;
     }
 }

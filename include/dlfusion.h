@@ -67,11 +67,14 @@ typedef enum {
 
 /* Activation of the epilogue; numbering as the epilogue's activation field in
  * [OPPL] §4.3 (0 none, 1 ReLU, 2 GELU).  GELU is the tanh form
- * 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))). */
+ * 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  3 is the exact GELU
+ * v Phi(v) = 0.5 v (1 + erf(v / sqrt(2))), the erf type beside tanh in [RFC]
+ * §2.1 and §2.4; bf16 and fp32 outputs only (the fp8 GEMM takes 0 and 1). */
 typedef enum {
     DLF_ACT_NONE = 0,
     DLF_ACT_RELU = 1,
-    DLF_ACT_GELU_TANH = 2
+    DLF_ACT_GELU_TANH = 2,
+    DLF_ACT_GELU_ERF = 3
 } dlf_act;
 
 /* A 2-D convolution layer.  x is NHWC [n][h][w][c_in]; weights are OHWI
@@ -181,6 +184,24 @@ dlf_status dlf_conv_fused(const dlf_conv_desc *d, const void *x, const void *w,
 dlf_status dlf_gemm_fused(const dlf_gemm_desc *d, const void *a, const void *b,
                           const float *col_scale, const float *col_shift,
                           const void *residual, void *c, void *stream);
+
+/* The GEMM of dlf_gemm_fused over weights concatenated along n at load, stored
+ * split by columns: one launch computes Q, K and V (or any equal column
+ * blocks) and writes each block to its own tensor.  [OPPL] §3.2: the Q, K and
+ * V projections become one GEMM over [W_q; W_k; W_v] ([3h, h]) whose result is
+ * cut into Q, K and V, by a split kernel or by offsets; here the epilogue's
+ * store does the cut, so the [m][3h] result never exists in memory.
+ *   columns [p n/parts, (p+1) n/parts) -> outs[p], a row-major [m][n/parts]
+ *   tensor of d->out_dtype; outs is a HOST array of `parts` device pointers.
+ * Same operands, scale/shift, activation and dtypes as dlf_gemm_fused; no
+ * residual.  INVALID_ARG: parts < 1, outs or an outs[p] NULL or not 16-byte
+ * aligned, n not divisible by parts.  UNSUPPORTED: parts > 4, a part's row not
+ * a whole number of 16-byte chunks (n/parts % 8 for bf16, % 16 for fp8 output),
+ * and every case dlf_gemm_fused refuses.  ALIAS: a part overlaps an input or
+ * another part. */
+dlf_status dlf_gemm_fused_split(const dlf_gemm_desc *d, const void *a, const void *b,
+                                const float *col_scale, const float *col_shift,
+                                int32_t parts, void *const *outs, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Unfused comparison chain: one kernel per op, every intermediate goes     */

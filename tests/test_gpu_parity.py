@@ -147,6 +147,7 @@ RAGGED_BF16 = [
     dict(n=1, h=10, w=10, cin=16, cout=96, kh=5, kw=5, stride=1, pad=2, act="relu", residual=True),
     dict(n=2, h=7, w=9, cin=136, cout=33, kh=3, kw=3, stride=1, pad=1, act="relu", residual=False),
     dict(n=5, h=15, w=15, cin=32, cout=129, kh=3, kw=3, stride=1, pad=0, act="gelu_tanh", residual=False),
+    dict(n=2, h=8, w=12, cin=48, cout=80, kh=3, kw=3, stride=2, pad=1, act="gelu_erf", residual=True),
 ]
 
 
@@ -177,6 +178,10 @@ HALO_BF16 = [
     # channel the bf16-rounded folded weights alone reach 3% of a cancelled output.
     dict(n=64, h=1, w=1, cin=64, cout=64, act="relu", residual=False),
     dict(n=16, h=2, w=3, cin=64, cout=64, act="none", residual=True),
+    # exact (erf) GELU through the resident-weight and the whole-image kernels (and, via the
+    # forced routes, the streaming halo kernel and the implicit GEMM)
+    dict(n=32, h=10, w=20, cin=64, cout=64, act="gelu_erf", residual=True),
+    dict(n=64, h=7, w=7, cin=128, cout=64, act="gelu_erf", residual=False),
 ]
 
 
@@ -190,6 +195,7 @@ RAGGED_F32 = [
     dict(n=2, h=9, w=7, cin=3, cout=5, kh=3, kw=3, stride=2, pad=1, act="relu", residual=False),
     dict(n=1, h=5, w=5, cin=16, cout=70, kh=1, kw=1, stride=1, pad=0, act="gelu_tanh", residual=True),
     dict(n=3, h=11, w=6, cin=7, cout=33, kh=5, kw=3, stride=1, pad=2, act="none", residual=False),
+    dict(n=2, h=6, w=9, cin=12, cout=40, kh=3, kw=3, stride=1, pad=1, act="gelu_erf", residual=True),
 ]
 
 
@@ -259,6 +265,7 @@ RAGGED_GEMM = [
     dict(m=513, n=257, k=520, act="none", bias=False),
     dict(m=64, n=48, k=0, act="gelu_tanh", bias=True),
     dict(m=777, n=1000, k=1024, act="relu", bias=True),
+    dict(m=130, n=72, k=64, act="gelu_erf", bias=True),
 ]
 
 
@@ -341,6 +348,78 @@ def test_gemm_rows_past_the_buffer_range(i):
             assert err <= TOL["bf16"], (tile, err)
         else:
             assert_codes_within_one(host(y, "fp8"), ref)
+    os.environ.pop("DLF_TILE", None)
+
+
+# ---------------------------------------------------------------------------
+# One GEMM over concatenated weights, stored split by columns ([OPPL] §3.2, Q/K/V)
+# ---------------------------------------------------------------------------
+SPLIT_GEMM = [
+    (3, dict(m=300, n=3 * 136, k=136, act="none", bias=True)),       # Q, K, V; ragged rows
+    (2, dict(m=77, n=2 * 64, k=520, act="gelu_erf", bias=False)),
+    (4, dict(m=513, n=4 * 256, k=64, act="relu", bias=True)),        # parts meet at tile borders
+    (3, dict(m=64, n=3 * 88, k=0, act="none", bias=True)),           # k = 0: bias only
+]
+
+
+@pytest.mark.parametrize("i", range(len(SPLIT_GEMM)))
+def test_bf16_gemm_split_store_every_tile(i):
+    parts, over = SPLIT_GEMM[i]
+    wl = workloads.workload(3, **over)
+    inp = workloads.generate(wl)
+    refs = oracle.gemm_bias_act_split(inp, parts)
+    L = layers().make_layer(inp, with_unfused=False)
+    pc = wl.n // parts
+    for tile in (None,) + GEMM_TILES:
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"gemm_fused_split {wl} parts={parts} tile={tile}")
+        outs = [guarded((wl.m, pc), torch.bfloat16) for _ in range(parts)]
+        dlf().dlf_gemm_fused_split(L.desc, L.x, L.w, None, L.bias, [y for _, y in outs])
+        torch.cuda.synchronize()
+        for p, ((buf, y), ref) in enumerate(zip(outs, refs)):
+            assert guard_intact(buf, y.numel()), p
+            err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+            assert err <= TOL["bf16"], (tile, p, err)
+    os.environ.pop("DLF_TILE", None)
+
+
+def test_qkv_projection_full_size_sampled():
+    """The LLaMA-7B Q/K/V projections as one 4096 x 12288 x 4096 GEMM stored as Q, K and V."""
+    wl = workloads.workload(3, n=3 * 4096, act="none", bias=True)
+    inp = workloads.generate(wl)
+    L = layers().make_layer(inp, with_unfused=False)
+    case(f"qkv {wl}")
+    outs = [guarded((wl.m, 4096), torch.bfloat16) for _ in range(3)]
+    dlf().dlf_gemm_fused_split(L.desc, L.x, L.w, None, L.bias, [y for _, y in outs])
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m)
+    refs = oracle.gemm_bias_act_split(inp, 3, rows)
+    for p, ((buf, y), ref) in enumerate(zip(outs, refs)):
+        assert guard_intact(buf, y.numel()), p
+        err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16")[rows], ref)
+        assert err <= TOL["bf16"], (p, err)
+
+
+def test_fp8_gemm_split_store():
+    wl = workloads.workload(4, m=77, n=2 * 64, k=144)
+    inp = workloads.generate(wl)
+    codes, _ = fp8_reference(inp, np.arange(wl.m))
+    L = layers().make_layer(inp, with_unfused=False)
+    for tile in (None, 0, 12, 3):
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"fp8 split {wl} tile={tile}")
+        outs = [guarded((wl.m, 64), torch.uint8) for _ in range(2)]
+        dlf().dlf_gemm_fused_split(L.desc, L.x, L.w, L.alpha, L.shift, [y for _, y in outs])
+        torch.cuda.synchronize()
+        for p, (buf, y) in enumerate(outs):
+            assert guard_intact(buf, y.numel()), p
+            assert_codes_within_one(host(y, "fp8"), codes[:, 64 * p:64 * (p + 1)])
     os.environ.pop("DLF_TILE", None)
 
 
@@ -503,7 +582,7 @@ def test_unfused_eltwise_passes(dt):
     torch.cuda.synchronize()
     got = oracle.widen(host(out, dt), dt).ravel()[:rows * c - 3]
     assert oracle.rel_error(got, oracle.add(yw, rw).ravel()[:rows * c - 3]) <= tol
-    for act in ("relu", "gelu_tanh"):
+    for act in ("relu", "gelu_tanh", "gelu_erf"):
         case(f"act {act} {dt}")
         d.dlf_act_apply(rows * c - 5, dt, act, y, out)
         torch.cuda.synchronize()

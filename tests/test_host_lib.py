@@ -223,6 +223,35 @@ def test_gemm_validation_statuses():
 
 
 @fake_pointers
+def test_gemm_split_validation_statuses():
+    """dlf_gemm_fused_split refuses, before any launch, what it cannot store exactly."""
+    lib = dlf.raw()
+    A, B = 0x100000, 0x200000
+    def g(**kw):
+        base = dict(m=64, n=96, k=64, in_dtype="bf16", out_dtype="bf16", act="none", out_inv_scale=1.0)
+        base.update(kw)
+        return ctypes.byref(dlf.gemm_desc(**base))
+    def outs(*ptrs):
+        return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    Q, K, V = 0x300000, 0x400000, 0x500000
+    call = lib.dlf_gemm_fused_split
+    assert call(g(), A, B, None, None, 0, outs(Q), 0) == dlf.DLF_ERR_INVALID_ARG          # parts < 1
+    assert call(g(), A, B, None, None, 3, None, 0) == dlf.DLF_ERR_INVALID_ARG             # outs NULL
+    assert call(g(), A, B, None, None, 3, outs(Q, None, V), 0) == dlf.DLF_ERR_INVALID_ARG  # a NULL part
+    assert call(g(), A, B, None, None, 3, outs(Q, K + 8, V), 0) == dlf.DLF_ERR_INVALID_ARG  # misaligned part
+    assert call(g(n=100), A, B, None, None, 3, outs(Q, K, V), 0) == dlf.DLF_ERR_INVALID_ARG  # n % parts
+    assert call(g(n=5 * 16), A, B, None, None, 5, outs(Q, K, V, Q, K), 0) == dlf.DLF_ERR_UNSUPPORTED  # > 4
+    assert call(g(n=3 * 12), A, B, None, None, 3, outs(Q, K, V), 0) == dlf.DLF_ERR_UNSUPPORTED  # 24 B rows
+    assert call(g(in_dtype="fp8", out_dtype="fp8", n=3 * 8), A, B, None, None, 3, outs(Q, K, V), 0) == \
+        dlf.DLF_ERR_UNSUPPORTED                                                               # 8 B fp8 rows
+    assert call(g(), A, B, None, None, 3, outs(Q, Q + 16, V), 0) == dlf.DLF_ERR_ALIAS      # parts overlap
+    assert call(g(), A, B, None, None, 3, outs(Q, K, A), 0) == dlf.DLF_ERR_ALIAS           # part over A
+    assert call(g(act="gelu_erf", in_dtype="fp8", out_dtype="fp8"), A, B, None, None, 3, outs(Q, K, V), 0) == \
+        dlf.DLF_ERR_UNSUPPORTED                                                               # fp8 + GELU
+    assert call(g(m=0), A, B, None, None, 3, outs(Q, K, V), 0) == dlf.DLF_OK              # empty: no launch
+
+
+@fake_pointers
 def test_eltwise_validation_statuses():
     lib = dlf.raw()
     A, B, C = 0x100000, 0x200000, 0x300000
