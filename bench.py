@@ -173,6 +173,52 @@ def run_workload(torch, idx: int, steps: int, warmup: int, eager: bool, unfused:
     return wl, inp, rec
 
 
+def run_next_rows(torch, steps: int, warmup: int, eager: bool):
+    """The widened rows, each against what it replaces:
+    - the Q/K/V projections of a LLaMA-7B layer (4096 tokens, h = 4096) as one GEMM over the
+      concatenated [3h, h] weights stored split into Q, K and V, vs three separate GEMMs;
+    - the 4096 x 11008 x 4096 GEMM with the exact (erf) GELU epilogue, vs its unfused chain."""
+    import dl_fusion_amd as d
+    from dl_fusion_amd.layers import make_layer
+    timer = time_eager if eager else time_graph
+    out = {}
+    for tokens in (4096, 128):      # a prefill batch, and a small one where launches dominate
+        wl = workloads.workload(3, m=tokens, n=3 * 4096, act="none", bias=True)
+        inp = workloads.generate(wl)
+        L = make_layer(inp, with_unfused=False)
+        h = wl.n // 3
+        parts = [torch.empty((wl.m, h), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        ms_split = timer(torch, lambda: d.dlf_gemm_fused_split(L.desc, L.x, L.w, None, L.bias, parts), steps,
+                         warmup)
+        desc1 = d.gemm_desc(wl.m, h, wl.k, "bf16", "bf16", "none")
+        ws = [L.w[p * h:(p + 1) * h] for p in range(3)]
+        bs = [L.bias[p * h:(p + 1) * h] for p in range(3)]
+        def three():
+            for p in range(3):
+                d.dlf_gemm_fused(desc1, L.x, ws[p], None, bs[p], None, parts[p])
+        ms_three = timer(torch, three, steps, warmup)
+        tf = flops(wl) / (ms_split * 1e-3) / 1e12
+        out[f"f1_qkv_split_store_{tokens}"] = {
+            "workload": f"qkv_bf16_{wl.m}x{wl.n}x{wl.k}_bias_split3", "gemm_mnk": list(wl.gemm_mnk),
+            "ms": ms_split, "tflops": tf, "frac_mfma_peak": tf / PEAK_TFLOPS["bf16"], "gemm_launches": 1,
+            "ms_three_gemms": ms_three, "gemm_launches_three": 3, "speedup_vs_three_gemms": ms_three / ms_split}
+        del L, inp, parts, ws, bs
+        torch.cuda.empty_cache()
+    wl = workloads.workload(3, act="gelu_erf")
+    inp = workloads.generate(wl)
+    L = make_layer(inp, with_unfused=True)
+    ms = timer(torch, L.forward, steps, warmup)
+    ms_u = timer(torch, L.forward_unfused, steps, warmup)
+    fl = flops(wl)
+    out["f2_gelu_erf_epilogue"] = {
+        "workload": f"matmul_bf16_{wl.m}x{wl.n}x{wl.k}_bias_gelu_erf", "gemm_mnk": list(wl.gemm_mnk), "ms": ms,
+        "tflops": fl / (ms * 1e-3) / 1e12, "frac_mfma_peak": fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+        "ms_unfused_chain": ms_u, "speedup_vs_unfused": ms_u / ms}
+    del L, inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the workload, on this host's cores."""
     import oracle
@@ -304,6 +350,11 @@ def main():
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(head_inp, args.cpu_budget)
     out["workloads"] = {str(k): v for k, v in recs.items()}
+    if not args.only:
+        print("# widened rows: split-store QKV GEMM, GELU-erf epilogue", file=sys.stderr, flush=True)
+        out["next_rows"] = run_next_rows(torch, args.steps, args.warmup, args.eager)
+        for k, v in out["next_rows"].items():
+            print(f"#   {k}: {v['ms'] * 1e3:.1f} us  {v['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 

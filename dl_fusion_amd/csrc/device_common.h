@@ -45,10 +45,20 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// GELU, exact form: v Phi(v) = 0.5 v erfc(-v / sqrt(2)), with the device library's erfc
-// (erfc keeps the negative tail free of the cancellation in 1 + erf).
+// GELU, exact form: v Phi(v) = 0.5 v erfc(-z), z = v / sqrt(2).  erfc(|z|) is the rational
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erfc(x) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x), x >= 0,
+// absolute error <= 1.5e-7; erfc(-|z|) = 2 - erfc(|z|).  About 15 instructions against ~40
+// for the library erfc, and far below the bf16 rounding of the result.
 __device__ __forceinline__ float gelu_erf(float v) {
-    return 0.5f * v * erfcf(-0.70710678118654752440f * v);
+    const float z = 0.70710678118654752440f * v;
+    const float az = fabsf(z);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, az, 1.0f));
+    const float poly =
+        t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f),
+                 0.254829592f);
+    const float e = poly * __builtin_amdgcn_exp2f(-1.44269504088896340736f * az * az);   // erfc(|z|)
+    return 0.5f * v * (z >= 0.0f ? 2.0f - e : e);
 }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
