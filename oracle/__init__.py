@@ -300,21 +300,27 @@ def gemm_bias_act_split(inp: dict, parts: int, rows=None):
     return [np.ascontiguousarray(y[:, p * w:(p + 1) * w]) for p in range(parts)]
 
 
-def fp8_gemm_bn_relu_quant(inp: dict, rows=None):
-    """fp8 MatMul with static scales -> BN -> ReLU -> static e4m3 quantisation.
+def fp8_gemm_bn_act_quant(inp: dict, act: str = "relu", rows=None):
+    """fp8 MatMul with static scales -> BN -> activation -> static e4m3 quantisation.
 
     acc = sum_k dec(xq) dec(wq) (exact in binary64); y = acc * s_x * s_w;
-    z = BN(y); u = max(z, 0); code = Q(u / s_y).   ([RFC] §3.4, [FRT] §3, [OPPL] §6.4)
-    Returns (codes uint8, u binary64).
+    z = BN(y); u = act(z); code = Q(u / s_y).   ([RFC] §3.4, [FRT] §3, [OPPL] §6.4;
+    with a GELU, the quantised MatMul + GELU of [RFC] §2.1, whose GELU is tanh or erf)
+    Returns (codes uint8, u binary64); u is also the value a bf16 output rounds.
     """
     x = e4m3_decode(inp["x"] if rows is None else inp["x"][np.asarray(rows)])
     w = e4m3_decode(inp["w"])
     acc = matmul_nt(x, w)
     y = acc * inp["s_x"] * inp["s_w"]
     z = batchnorm(y, inp["gamma"], inp["beta"], inp["mean"], inp["var"], inp["eps"])
-    u = relu(z)
+    u = activation(z, act)
     v = u / inp["s_y"]
     return e4m3_encode(v), u
+
+
+def fp8_gemm_bn_relu_quant(inp: dict, rows=None):
+    """The fp8 pipeline with ReLU (the config of the fp8 workload)."""
+    return fp8_gemm_bn_act_quant(inp, "relu", rows)
 
 
 # ---------------------------------------------------------------------------

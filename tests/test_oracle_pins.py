@@ -396,6 +396,28 @@ def test_fp8_pipeline_codes_are_post_relu_and_in_range():
     np.testing.assert_array_equal(codes[u == 0], 0)
 
 
+def test_fp8_pipeline_with_gelu_forms():
+    """Quantised MatMul + GELU ([RFC] §2.1): rebuilt from the exact integer e4m3 products, BN in
+    numpy and each GELU form from an independent definition (scipy's normal CDF; the tanh
+    formula); the codes are the codec applied to u / s_y, signed where u < 0."""
+    from scipy.stats import norm
+    inp = workloads.generate(workloads.workload(4, m=19, n=24, k=64))
+    y = (e4m3_int(inp["x"]) @ e4m3_int(inp["w"]).T).astype(np.float64) * 2.0 ** -18 * inp["s_x"] * inp["s_w"]
+    g, b, mu, var = (np.asarray(inp[k], np.float64) for k in ("gamma", "beta", "mean", "var"))
+    z = g * (y - mu) / np.sqrt(var + inp["eps"]) + b
+    forms = {"gelu_erf": lambda t: t * norm.cdf(t),
+             "gelu_tanh": lambda t: 0.5 * t * (1 + np.tanh(np.sqrt(2 / np.pi) * (t + 0.044715 * t ** 3)))}
+    for act, f in forms.items():
+        codes, u = oracle.fp8_gemm_bn_act_quant(inp, act)
+        np.testing.assert_allclose(u, f(z), rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(codes, oracle.e4m3_encode(u / inp["s_y"]))
+        neg = u / inp["s_y"] < -2.0 ** -10          # below half the smallest subnormal: a signed code
+        assert np.any(neg) and np.all(codes[neg] & 0x80)
+    codes, u = oracle.fp8_gemm_bn_act_quant(inp, "relu")
+    c2, u2 = oracle.fp8_gemm_bn_relu_quant(inp)
+    np.testing.assert_array_equal(codes, c2)
+
+
 def test_metric_floor():
     o = np.array([0.0, 1.0, -1.0, 0.0])
     assert oracle.rel_error(o, o) == 0.0
