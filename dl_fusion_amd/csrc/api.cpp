@@ -347,7 +347,7 @@ dlf_status gemm_fused_impl(const dlf_gemm_desc* d, const void* a, const void* b,
     const bool bf16_path = d->in_dtype == DLF_BF16 && d->out_dtype == DLF_BF16;
     const bool fp8_path = d->in_dtype == DLF_FP8_E4M3 &&
                           (d->out_dtype == DLF_FP8_E4M3 || d->out_dtype == DLF_BF16) &&
-                          (d->act == DLF_ACT_NONE || d->act == DLF_ACT_RELU) && residual == nullptr;
+                          residual == nullptr;
     if (!bf16_path && !fp8_path)
         return fail(DLF_ERR_UNSUPPORTED, "no fused GEMM for in=%d out=%d act=%d residual=%s",
                     static_cast<int>(d->in_dtype), static_cast<int>(d->out_dtype), static_cast<int>(d->act),

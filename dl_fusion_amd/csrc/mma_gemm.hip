@@ -690,10 +690,14 @@ hipError_t launch_fp8_mode(const MmaArgs& a, int act, int out, int tile, hipStre
     if (out == kOutFp8) {
         if (act == kActNone) return launch_tile<1, AMODE, kActNone, kOutFp8>(a, tile, s);
         if (act == kActRelu) return launch_tile<1, AMODE, kActRelu, kOutFp8>(a, tile, s);
+        if (act == kActGelu) return launch_tile<1, AMODE, kActGelu, kOutFp8>(a, tile, s);
+        if (act == kActGeluErf) return launch_tile<1, AMODE, kActGeluErf, kOutFp8>(a, tile, s);
     }
     if (out == kOutBf16) {
         if (act == kActNone) return launch_tile<1, AMODE, kActNone, kOutBf16>(a, tile, s);
         if (act == kActRelu) return launch_tile<1, AMODE, kActRelu, kOutBf16>(a, tile, s);
+        if (act == kActGelu) return launch_tile<1, AMODE, kActGelu, kOutBf16>(a, tile, s);
+        if (act == kActGeluErf) return launch_tile<1, AMODE, kActGeluErf, kOutBf16>(a, tile, s);
     }
     return hipErrorInvalidValue;
 }

@@ -69,7 +69,8 @@ typedef enum {
  * [OPPL] §4.3 (0 none, 1 ReLU, 2 GELU).  GELU is the tanh form
  * 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  3 is the exact GELU
  * v Phi(v) = 0.5 v (1 + erf(v / sqrt(2))), the erf type beside tanh in [RFC]
- * §2.1 and §2.4; bf16 and fp32 outputs only (the fp8 GEMM takes 0 and 1). */
+ * §2.1 and §2.4.  Every activation is available to every fused path; on the fp8
+ * GEMM the GELU forms give the quantised MatMul + GELU of [RFC] §2.1. */
 typedef enum {
     DLF_ACT_NONE = 0,
     DLF_ACT_RELU = 1,
@@ -174,8 +175,9 @@ dlf_status dlf_conv_fused(const dlf_conv_desc *d, const void *x, const void *w,
  * (the quantisation-aware clamp of [OPPL] §6.4; the static-scale fp8 epilogue
  * of [FRT] §3 and §6; quantised MatMul + activation of [RFC] §3.4).
  * Supported: in_dtype BF16 -> out BF16 (any act, optional bf16 residual);
- *            in_dtype FP8_E4M3 -> out FP8_E4M3 or BF16 (act NONE or RELU,
- *            no residual).  Everything else -> DLF_ERR_UNSUPPORTED.
+ *            in_dtype FP8_E4M3 -> out FP8_E4M3 or BF16 (any act, no
+ *            residual; with a GELU: quantised MatMul + GELU, [RFC] §2.1).
+ *            Everything else -> DLF_ERR_UNSUPPORTED.
  *   a        device [m][k]; b device [n][k] (k % 8 == 0 bf16, % 16 == 0 fp8)
  *   col_scale device [n] fp32 or NULL (= 1); col_shift device [n] fp32 or
  *            NULL (= 0): the bias, or the folded BN scale/shift (alpha, beta')

@@ -499,6 +499,44 @@ def test_fp8_gemm_ragged_shapes_every_tile(i):
     assert_codes_within_one(host(yu, "fp8"), ref)
 
 
+def signed_code_order(codes):
+    """e4m3 codes in value order: sign-magnitude to a signed integer, with -0 equal to +0."""
+    c = codes.astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf"])
+def test_fp8_gemm_gelu_every_tile(act):
+    """Quantised MatMul + GELU ([RFC] §2.1): e4m3 codes (signed: GELU dips below zero) within one
+    code of the oracle's, and the bf16 form within the bf16 tolerance."""
+    wl = workloads.workload(4, m=300, n=200, k=144)
+    inp = workloads.generate(wl)
+    codes, u = oracle.fp8_gemm_bn_act_quant(inp, act)
+    assert np.any(codes & 0x80)
+    L = layers().make_layer(inp, with_unfused=False)
+    d = dlf()
+    desc8 = d.gemm_desc(wl.m, wl.n, wl.k, "fp8", "fp8", act, L.inv_s_y)
+    desc16 = d.gemm_desc(wl.m, wl.n, wl.k, "fp8", "bf16", act)
+    for tile in (None,) + GEMM_TILES:
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"fp8 {act} {wl} tile={tile}")
+        buf, y = guarded((wl.m, wl.n), torch.uint8)
+        d.dlf_gemm_fused(desc8, L.x, L.w, L.alpha, L.shift, None, y)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, y.numel())
+        diff = np.abs(signed_code_order(host(y, "fp8")) - signed_code_order(codes))
+        assert diff.max() <= 1, (tile, diff.max())
+    os.environ.pop("DLF_TILE", None)
+    case(f"fp8 {act} -> bf16 {wl}")
+    yb = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device="cuda")
+    d.dlf_gemm_fused(desc16, L.x, L.w, L.alpha, L.shift, None, yb)
+    torch.cuda.synchronize()
+    assert oracle.rel_error(oracle.widen(host(yb, "bf16"), "bf16"), u) <= TOL["bf16"]
+
+
 def test_fp8_saturation_variant():
     """Half the static output scale: the largest outputs must saturate to 448 (0x7E)."""
     wl = workloads.workload(4, m=256, n=256, k=512, out_scale=0.5)

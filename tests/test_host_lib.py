@@ -206,8 +206,6 @@ def test_gemm_validation_statuses():
     assert lib.dlf_gemm_fused(g(k=60), A, B, None, None, None, C, 0) == dlf.DLF_ERR_UNSUPPORTED      # k % 8
     assert lib.dlf_gemm_fused(g(in_dtype="fp8", out_dtype="fp8", k=72), A, B, None, None, None, C, 0) == \
         dlf.DLF_ERR_UNSUPPORTED                                                                     # k % 16
-    assert lib.dlf_gemm_fused(g(in_dtype="fp8", out_dtype="fp8"), A, B, None, None, None, C, 0) == \
-        dlf.DLF_ERR_UNSUPPORTED                                                                     # fp8 + GELU
     assert lib.dlf_gemm_fused(g(in_dtype="fp8", out_dtype="fp8", act="relu"), A, B, None, None, 0x400000, C, 0) == \
         dlf.DLF_ERR_UNSUPPORTED                                                                     # fp8 + residual
     assert lib.dlf_gemm_fused(g(in_dtype="fp8", out_dtype="fp8", act="relu", out_inv_scale=0.0), A, B, None, None,
@@ -246,8 +244,6 @@ def test_gemm_split_validation_statuses():
         dlf.DLF_ERR_UNSUPPORTED                                                               # 8 B fp8 rows
     assert call(g(), A, B, None, None, 3, outs(Q, Q + 16, V), 0) == dlf.DLF_ERR_ALIAS      # parts overlap
     assert call(g(), A, B, None, None, 3, outs(Q, K, A), 0) == dlf.DLF_ERR_ALIAS           # part over A
-    assert call(g(act="gelu_erf", in_dtype="fp8", out_dtype="fp8"), A, B, None, None, 3, outs(Q, K, V), 0) == \
-        dlf.DLF_ERR_UNSUPPORTED                                                               # fp8 + GELU
     assert call(g(m=0), A, B, None, None, 3, outs(Q, K, V), 0) == dlf.DLF_OK              # empty: no launch
 
 
