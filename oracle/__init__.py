@@ -58,6 +58,7 @@ def _load():
         "orc_relu": (None, [_i64, _dp, _dp]),
         "orc_gelu_tanh": (None, [_i64, _dp, _dp]),
         "orc_gelu_erf": (None, [_i64, _dp, _dp]),
+        "orc_silu": (None, [_i64, _dp, _dp]),
         "orc_fold_bn": (None, [_i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]),
         "orc_e4m3_to_double": (ctypes.c_double, [ctypes.c_int]),
         "orc_e4m3_from_double": (ctypes.c_int, [ctypes.c_double]),
@@ -224,6 +225,14 @@ def gelu_erf(u):
     return out
 
 
+def silu(u):
+    """SiLU, u / (1 + e^-u): the gate of SwiGLU ([RFC] §2.2 - §2.4)."""
+    u = _d(u)
+    out = np.empty_like(u)
+    _load().orc_silu(u.size, _ptr(u), _ptr(out))
+    return out
+
+
 def activation(u, act: str):
     if act == "relu":
         return relu(u)
@@ -231,6 +240,8 @@ def activation(u, act: str):
         return gelu_tanh(u)
     if act == "gelu_erf":
         return gelu_erf(u)
+    if act == "silu":
+        return silu(u)
     if act == "none":
         return _d(u)
     raise ValueError(act)
@@ -298,6 +309,23 @@ def gemm_bias_act_split(inp: dict, parts: int, rows=None):
         raise ValueError("columns must split evenly")
     w = n // parts
     return [np.ascontiguousarray(y[:, p * w:(p + 1) * w]) for p in range(parts)]
+
+
+def gemm_gated(inp: dict, gate: str, rows=None):
+    """Gated projection: one MatMul over gate and up weights interleaved by rows at load (row
+    2j = gate j, row 2j+1 = up j), bias added, then out[:, j] = gate_act(g_j) * u_j: SwiGLU
+    with gate = "silu", GELU x Mul with "gelu_tanh" / "gelu_erf" ([RFC] §2.2 GMM + SwiGLU,
+    §2.3 gated Linear, §2.4 gelu(x) * y).  Returns [m][n/2] in binary64."""
+    wl = inp["workload"]
+    x = widen(inp["x"], "bf16")
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    y = matmul_nt(x, widen(inp["w"], "bf16"))
+    if inp.get("bias") is not None:
+        y = bias_add(y, inp["bias"])
+    if y.shape[1] % 2:
+        raise ValueError("interleaved gate/up needs an even column count")
+    return activation(np.ascontiguousarray(y[:, 0::2]), gate) * y[:, 1::2]
 
 
 def fp8_gemm_bn_act_quant(inp: dict, act: str = "relu", rows=None):

@@ -189,6 +189,16 @@ void orc_gelu_erf(int64_t count, const double *in, double *out)
     }
 }
 
+/* SiLU (swish), the gate of SwiGLU in [RFC] §2.2 - §2.4: silu(u) = u / (1 + e^-u). */
+void orc_silu(int64_t count, const double *in, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        const double u = in[i];
+        out[i] = u / (1.0 + exp(-u));
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* BN folding, used only as a self-check of the unfolded path.               */
 /* [OPPL] §3.1: scale = gamma / sqrt(var + eps); W_new = W * scale per output */

@@ -287,6 +287,35 @@ def test_split_gemm_equals_separate_projections():
         oracle.gemm_bias_act_split(inp, 5)
 
 
+def test_silu_against_the_logistic_function():
+    from scipy.special import expit
+    rng = np.random.default_rng(12)
+    u = np.concatenate([rng.standard_normal(2000) * 6, np.linspace(-30, 30, 121)])
+    np.testing.assert_allclose(oracle.silu(u), u * expit(u), rtol=1e-14, atol=1e-300)
+    # silu(u) - silu(-u) = u (the logistic function's symmetry); silu(0) = 0
+    np.testing.assert_allclose(oracle.silu(u) - oracle.silu(-u), u, rtol=1e-13, atol=1e-13)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_gated_projection_matches_separate_gate_and_up():
+    """One MatMul over interleaved [g0; u0; g1; u1; ...] rows = act(x Wg^T + bg) * (x Wu^T + bu),
+    computed here with numpy on the de-interleaved weights and scipy's logistic / normal CDF."""
+    from scipy.special import expit
+    from scipy.stats import norm
+    wl = workloads.workload(3, m=6, n=2 * 24, k=32, act="none", bias=True)
+    inp = workloads.generate(wl)
+    x, w = oracle.widen(inp["x"], "bf16"), oracle.widen(inp["w"], "bf16")
+    b = inp["bias"].astype(np.float64)
+    g = x @ w[0::2].T + b[0::2]
+    u = x @ w[1::2].T + b[1::2]
+    forms = {"silu": g * expit(g), "gelu_erf": g * norm.cdf(g),
+             "gelu_tanh": 0.5 * g * (1 + np.tanh(np.sqrt(2 / np.pi) * (g + 0.044715 * g ** 3)))}
+    for gate, ga in forms.items():
+        got = oracle.gemm_gated(inp, gate)
+        assert got.shape == (6, 24)
+        np.testing.assert_allclose(got, ga * u, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # O6 / O7: the fp8 e4m3 codec and the exact fp8 product
 # ---------------------------------------------------------------------------
