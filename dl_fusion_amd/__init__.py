@@ -35,6 +35,8 @@ DLF_ACT_NONE, DLF_ACT_RELU, DLF_ACT_GELU_TANH, DLF_ACT_GELU_ERF = 0, 1, 2, 3
 
 DTYPES = {"f32": DLF_F32, "bf16": DLF_BF16, "fp8": DLF_FP8_E4M3}
 ACTS = {"none": DLF_ACT_NONE, "relu": DLF_ACT_RELU, "gelu_tanh": DLF_ACT_GELU_TANH, "gelu_erf": DLF_ACT_GELU_ERF}
+DLF_GATE_SILU, DLF_GATE_GELU_TANH, DLF_GATE_GELU_ERF = 0, 1, 2
+GATES = {"silu": DLF_GATE_SILU, "gelu_tanh": DLF_GATE_GELU_TANH, "gelu_erf": DLF_GATE_GELU_ERF}
 
 
 class dlf_conv_desc(ctypes.Structure):
@@ -71,6 +73,7 @@ _SIGS = {
     "dlf_gemm_fused": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "dlf_gemm_fused_split": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, _vp, _vp, ctypes.c_int32,
                              ctypes.POINTER(_vp), _vp],
+    "dlf_gemm_fused_gated": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp],
     "dlf_conv_plain": [ctypes.POINTER(dlf_conv_desc), _vp, _vp, _vp, _vp, _vp],
     "dlf_gemm_plain": [ctypes.POINTER(dlf_gemm_desc), _vp, _vp, ctypes.c_float, _vp, _vp],
     "dlf_bn_apply": [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp],
@@ -180,6 +183,12 @@ def dlf_conv_fused(desc, x, w, bias, residual, y, stream=None):
 def dlf_gemm_fused(desc, a, b, col_scale, col_shift, residual, c, stream=None):
     _check(_lib.dlf_gemm_fused(ctypes.byref(desc), _dev(a), _dev(b), _dev(col_scale), _dev(col_shift),
                                _dev(residual), _dev(c), _stream(stream)), "dlf_gemm_fused")
+
+
+def dlf_gemm_fused_gated(desc, a, b, col_scale, col_shift, gate, c, stream=None):
+    """Gated projection: c[:, j] = gate(g_j) * u_j over interleaved (gate, up) weight rows."""
+    _check(_lib.dlf_gemm_fused_gated(ctypes.byref(desc), _dev(a), _dev(b), _dev(col_scale), _dev(col_shift),
+                                     GATES.get(gate, gate), _dev(c), _stream(stream)), "dlf_gemm_fused_gated")
 
 
 def dlf_gemm_fused_split(desc, a, b, col_scale, col_shift, outs, stream=None):

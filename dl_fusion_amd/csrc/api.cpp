@@ -420,6 +420,43 @@ dlf_status dlf_gemm_fused(const dlf_gemm_desc* d, const void* a, const void* b, 
     return gemm_fused_impl(d, a, b, col_scale, col_shift, residual, c, 0, nullptr, stream, "dlf_gemm_fused");
 }
 
+dlf_status dlf_gemm_fused_gated(const dlf_gemm_desc* d, const void* a, const void* b, const float* col_scale,
+                                const float* col_shift, dlf_gate gate, void* c, void* stream) {
+    if (!d) return fail(DLF_ERR_INVALID_ARG, "gemm descriptor is NULL");
+    if (gate != DLF_GATE_SILU && gate != DLF_GATE_GELU_TANH && gate != DLF_GATE_GELU_ERF)
+        return fail(DLF_ERR_INVALID_ARG, "unknown gate %d", static_cast<int>(gate));
+    if (d->act != DLF_ACT_NONE) return fail(DLF_ERR_INVALID_ARG, "the gate replaces the activation: act must be NONE");
+    const dlf_status st = check_gemm_common(d, a, b, c);
+    if (st != DLF_OK) return st;
+    if (d->in_dtype != DLF_BF16 || d->out_dtype != DLF_BF16)
+        return fail(DLF_ERR_UNSUPPORTED, "gated epilogue: bf16 operands and output only");
+    if (d->n % 2 != 0) return fail(DLF_ERR_INVALID_ARG, "n must be even: (gate, up) column pairs");
+    if (d->m == 0 || d->n == 0) return ok();
+    if ((col_scale && !aligned16(col_scale)) || (col_shift && !aligned16(col_shift)))
+        return fail(DLF_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const size_t cbytes = static_cast<size_t>(d->m) * static_cast<size_t>(d->n / 2) * 2;
+    if (overlaps(c, cbytes, a, static_cast<size_t>(d->m * d->k) * 2) ||
+        overlaps(c, cbytes, b, static_cast<size_t>(d->n * d->k) * 2) ||
+        overlaps(c, cbytes, col_scale, static_cast<size_t>(d->n) * 4) ||
+        overlaps(c, cbytes, col_shift, static_cast<size_t>(d->n) * 4))
+        return fail(DLF_ERR_ALIAS, "output overlaps an input");
+    dlf::MmaArgs x{};
+    x.a = a;
+    x.b = b;
+    x.scale = col_scale;
+    x.shift = col_shift;
+    x.c = c;
+    x.M = d->m;
+    x.N = static_cast<int>(d->n);
+    x.K = static_cast<int>(d->k);
+    x.out_inv_scale = 1.0f;
+    x.dequant = 1.0f;
+    const int act = gate == DLF_GATE_SILU ? dlf::kActSiluMul : gate == DLF_GATE_GELU_TANH ? dlf::kActGeluMul
+                                                                                           : dlf::kActGeluErfMul;
+    return hip_status(dlf::launch_mma_bf16(x, false, act, pick_tile(d->m, d->n, true), static_cast<hipStream_t>(stream)),
+                      "dlf_gemm_fused_gated");
+}
+
 dlf_status dlf_gemm_fused_split(const dlf_gemm_desc* d, const void* a, const void* b, const float* col_scale,
                                 const float* col_shift, int32_t parts, void* const* outs, void* stream) {
     if (parts < 1) return fail(DLF_ERR_INVALID_ARG, "parts must be >= 1");

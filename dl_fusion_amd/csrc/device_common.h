@@ -22,6 +22,8 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 enum : int { kActNone = 0, kActRelu = 1, kActGelu = 2, kActGeluErf = 3 };
+// gated epilogues: the GEMM's columns come in (gate, up) pairs and the output is gate_act(g) * u
+enum : int { kActSiluMul = 4, kActGeluMul = 5, kActGeluErfMul = 6 };
 enum : int { kOutBf16 = 0, kOutFp8 = 1, kOutF32 = 2 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -75,6 +77,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t u) {
     const i16x2_t s = __builtin_bit_cast(i16x2_t, u);
     return __builtin_bit_cast(uint32_t, s & ~(s >> 15));
+}
+
+// SiLU, v / (1 + e^-v), with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float silu(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896340736f * v));
+}
+
+// The gate activation of a gated epilogue.
+template <int ACT>
+__device__ __forceinline__ float gate_act(float g) {
+    if constexpr (ACT == kActSiluMul) {
+        return silu(g);
+    } else if constexpr (ACT == kActGeluMul) {
+        return gelu_tanh(g);
+    } else {
+        static_assert(ACT == kActGeluErfMul, "gated epilogue");
+        return gelu_erf(g);
+    }
 }
 
 template <int ACT>

@@ -462,7 +462,11 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         return;
     } else {
         constexpr int OB = OUT == kOutFp8 ? 1 : 2;            // output bytes per element
-        constexpr int SROW = TS::BN * OB;                     // staging row bytes
+        // gated: columns (2j, 2j+1) are (gate j, up j) and give output column j
+        constexpr bool GATED = ACT >= kActSiluMul;
+        static_assert(!GATED || (OUT == kOutBf16 && AMODE != kConvAligned && AMODE != kConvGeneric),
+                      "gated epilogue: dense bf16 output");
+        constexpr int SROW = (GATED ? TS::BN / 2 : TS::BN) * OB;   // staging row bytes
         constexpr int CPR = SROW / 16;                        // 16-byte chunks per staged row
         // staged chunk cc of row r lives at chunk cc ^ (r & XM): the 16 rows written by one
         // store instruction land in distinct bank groups instead of one
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
                         const float t = acc[j][i][4 * g + e];
                         v[e] = scale ? fmaf(t, sc[e], sh[e]) : t + sh[e];
                     }
-                    if (p.res != nullptr) {
+                    if (!GATED && p.res != nullptr) {
                         const int64_t mc = min(m0 + ml, m_last);
                         if ((N & 3) == 0) {   // 8-byte aligned run of four
                             const uint2 t = *reinterpret_cast<const uint2*>(p.res + mc * N + min(n, n_last4));
@@ -520,6 +524,14 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
 #pragma unroll
                             for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.res[mc * N + min(n + e, N - 1)]);
                         }
+                    }
+                    if constexpr (GATED) {
+                        // output columns nl/2 and nl/2 + 1 (nl % 4 == 0): one 4-byte staging write
+                        const int cb = (nl >> 1) * OB;
+                        uint8_t* dst = smem + ml * SROW + ((((cb >> 4) ^ (ml & XM))) << 4) + (cb & 15);
+                        *reinterpret_cast<uint32_t*>(dst) =
+                            pack_bf16x2(gate_act<ACT>(v[0]) * v[1], gate_act<ACT>(v[2]) * v[3]);
+                        continue;
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         }
         __syncthreads();
         // coalesced write-out: 16-byte chunks of the staged tile, row-major
-        if (p.parts > 1) {
+        if (!GATED && p.parts > 1) {
             // split store: a chunk lies in one part (the part width is a whole number of chunks)
             const int pc = p.part_cols;
             for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
@@ -555,20 +567,22 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
             }
             return;
         }
-        const bool vec_ok = ((static_cast<int64_t>(N) * OB) & 15) == 0;
+        const int NO = GATED ? N / 2 : N;                     // output columns
+        const int no0 = GATED ? n0 / 2 : n0;                  // first output column of the tile
+        const bool vec_ok = ((static_cast<int64_t>(NO) * OB) & 15) == 0;
         uint8_t* const cbytes = static_cast<uint8_t*>(p.c);
         for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
             const int ml = q / CPR, cc = q - ml * CPR;
             const int64_t m = m0 + ml;
             const int nl = cc * (16 / OB);
-            const int n = n0 + nl;
-            if (m >= M || n >= N) continue;
+            const int n = no0 + nl;
+            if (m >= M || n >= NO) continue;
             const uint8_t* src = smem + ml * SROW + ((cc ^ (ml & XM)) << 4);
-            uint8_t* dst = cbytes + (m * N + n) * OB;
-            if (vec_ok && n + 16 / OB <= N) {
+            uint8_t* dst = cbytes + (m * NO + n) * OB;
+            if (vec_ok && n + 16 / OB <= NO) {
                 *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
             } else {
-                const int cnt = min(16 / OB, N - n) * OB;
+                const int cnt = min(16 / OB, NO - n) * OB;
                 for (int b = 0; b < cnt; ++b) dst[b] = src[b];
             }
         }
@@ -641,8 +655,17 @@ hipError_t launch_bf16_act(const MmaArgs& a, int act, int tile, hipStream_t s) {
         case kActRelu: return launch_tile<2, AMODE, kActRelu, kOutBf16>(a, tile, s);
         case kActGelu: return launch_tile<2, AMODE, kActGelu, kOutBf16>(a, tile, s);
         case kActGeluErf: return launch_tile<2, AMODE, kActGeluErf, kOutBf16>(a, tile, s);
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    if constexpr (AMODE == kDense || AMODE == kDenseWide) {
+        switch (act) {
+            case kActSiluMul: return launch_tile<2, AMODE, kActSiluMul, kOutBf16>(a, tile, s);
+            case kActGeluMul: return launch_tile<2, AMODE, kActGeluMul, kOutBf16>(a, tile, s);
+            case kActGeluErfMul: return launch_tile<2, AMODE, kActGeluErfMul, kOutBf16>(a, tile, s);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -78,6 +78,16 @@ typedef enum {
     DLF_ACT_GELU_ERF = 3
 } dlf_act;
 
+/* Gate of a gated projection (dlf_gemm_fused_gated): out = gate(g) * u.
+ * SILU gives SwiGLU (silu(g) = g / (1 + e^-g); [RFC] §2.2 GMM + SwiGLU, §2.3
+ * the gated Linear form); the GELU forms give GELU x Mul ([RFC] §2.4,
+ * gelu(x) * y). */
+typedef enum {
+    DLF_GATE_SILU = 0,
+    DLF_GATE_GELU_TANH = 1,
+    DLF_GATE_GELU_ERF = 2
+} dlf_gate;
+
 /* A 2-D convolution layer.  x is NHWC [n][h][w][c_in]; weights are OHWI
  * [c_out][kh][kw][c_in] (the GEMM view: B = [c_out][K], K = kh*kw*c_in,
  * k = (r*kw + s)*c_in + ci); y (and residual) are NHWC [n][ho][wo][c_out] with
@@ -204,6 +214,22 @@ dlf_status dlf_gemm_fused(const dlf_gemm_desc *d, const void *a, const void *b,
 dlf_status dlf_gemm_fused_split(const dlf_gemm_desc *d, const void *a, const void *b,
                                 const float *col_scale, const float *col_shift,
                                 int32_t parts, void *const *outs, void *stream);
+
+/* Gated projection: one GEMM over gate and up weights interleaved by rows at
+ * load, with a gated register epilogue, so neither projection reaches memory:
+ *     b row 2j = gate weight j, row 2j+1 = up weight j (d->n = 2 x outputs);
+ *     g = acc[2j] * col_scale[2j] + col_shift[2j]   (likewise u from 2j+1)
+ *     c[m][j] = bf16( gate(g) * u ),  c is [m][n/2].
+ * col_scale / col_shift are [n], interleaved like b (NULL = 1 / 0).  [RFC]
+ * §2.2 - §2.4 list GMM + SwiGLU, the gated Linear and gelu(x) * y among the
+ * fusion targets; the interleave keeps each (gate, up) pair in one lane's
+ * registers.  bf16 operands and output; d->act must be NONE (the gate is the
+ * activation); no residual.
+ * INVALID_ARG: unknown gate, act != NONE, odd n, NULL / misaligned pointers.
+ * UNSUPPORTED: other dtypes, k % 8 != 0.  ALIAS: c overlaps an input. */
+dlf_status dlf_gemm_fused_gated(const dlf_gemm_desc *d, const void *a, const void *b,
+                                const float *col_scale, const float *col_shift,
+                                dlf_gate gate, void *c, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Unfused comparison chain: one kernel per op, every intermediate goes     */

@@ -386,6 +386,41 @@ def test_bf16_gemm_split_store_every_tile(i):
     os.environ.pop("DLF_TILE", None)
 
 
+# ---------------------------------------------------------------------------
+# Gated projections: SwiGLU and GELU x Mul over interleaved (gate, up) rows ([RFC] §2.2 - §2.4)
+# ---------------------------------------------------------------------------
+GATED_GEMM = [
+    ("silu", dict(m=300, n=2 * 136, k=136, act="none", bias=True)),
+    ("gelu_tanh", dict(m=77, n=2 * 100, k=520, act="none", bias=False)),   # 100 outputs: chunk tail
+    ("gelu_erf", dict(m=513, n=2 * 256, k=64, act="none", bias=True)),
+    ("silu", dict(m=64, n=2 * 24, k=0, act="none", bias=True)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(GATED_GEMM)))
+def test_bf16_gemm_gated_every_tile(i):
+    gate, over = GATED_GEMM[i]
+    wl = workloads.workload(3, **over)
+    inp = workloads.generate(wl)
+    ref = oracle.gemm_gated(inp, gate)
+    L = layers().make_layer(inp, with_unfused=False)
+    d = dlf()
+    desc = d.gemm_desc(wl.m, wl.n, wl.k, "bf16", "bf16", "none")
+    for tile in (None,) + GEMM_TILES:
+        if tile is None:
+            os.environ.pop("DLF_TILE", None)
+        else:
+            os.environ["DLF_TILE"] = str(tile)
+        case(f"gemm_fused_gated {gate} {wl} tile={tile}")
+        buf, y = guarded((wl.m, wl.n // 2), torch.bfloat16)
+        d.dlf_gemm_fused_gated(desc, L.x, L.w, None, L.bias, gate, y)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, y.numel())
+        err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+        assert err <= TOL["bf16"], (tile, err)
+    os.environ.pop("DLF_TILE", None)
+
+
 def test_qkv_projection_full_size_sampled():
     """The LLaMA-7B Q/K/V projections as one 4096 x 12288 x 4096 GEMM stored as Q, K and V."""
     wl = workloads.workload(3, n=3 * 4096, act="none", bias=True)

@@ -248,6 +248,26 @@ def test_gemm_split_validation_statuses():
 
 
 @fake_pointers
+def test_gemm_gated_validation_statuses():
+    lib = dlf.raw()
+    A, B, C = 0x100000, 0x200000, 0x300000
+    def g(**kw):
+        base = dict(m=64, n=96, k=64, in_dtype="bf16", out_dtype="bf16", act="none", out_inv_scale=1.0)
+        base.update(kw)
+        return ctypes.byref(dlf.gemm_desc(**base))
+    call = lib.dlf_gemm_fused_gated
+    assert call(None, A, B, None, None, 0, C, 0) == dlf.DLF_ERR_INVALID_ARG                  # no descriptor
+    assert call(g(), A, B, None, None, 7, C, 0) == dlf.DLF_ERR_INVALID_ARG                   # unknown gate
+    assert call(g(act="relu"), A, B, None, None, 0, C, 0) == dlf.DLF_ERR_INVALID_ARG         # act != NONE
+    assert call(g(n=95), A, B, None, None, 0, C, 0) == dlf.DLF_ERR_INVALID_ARG               # odd n
+    assert call(g(in_dtype="fp8", out_dtype="fp8", k=64), A, B, None, None, 0, C, 0) == dlf.DLF_ERR_UNSUPPORTED
+    assert call(g(k=60), A, B, None, None, 0, C, 0) == dlf.DLF_ERR_UNSUPPORTED               # k % 8
+    assert call(g(), A, B, None, None, 0, A, 0) == dlf.DLF_ERR_ALIAS
+    assert call(g(), A, B, None, 0x400008, 0, C, 0) == dlf.DLF_ERR_INVALID_ARG               # misaligned
+    assert call(g(m=0), A, B, None, None, 2, C, 0) == dlf.DLF_OK
+
+
+@fake_pointers
 def test_eltwise_validation_statuses():
     lib = dlf.raw()
     A, B, C = 0x100000, 0x200000, 0x300000
