@@ -35,8 +35,9 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["mma_gemm.hip", "mma_common.h", "conv_halo.hip", "conv_f32.hip", "device_common.h",
-                  "kernels.h", "api.cpp"]   # api.cpp picks the route and tile
+KERNEL_SOURCES = ["mma_kernel.h", "mma_gemm.hip", "mma_bf16_dense.hip", "mma_bf16_gated.hip",
+                  "mma_bf16_conv.hip", "mma_fp8_q.hip", "mma_fp8_b.hip", "mma_common.h", "conv_halo.hip",
+                  "conv_f32.hip", "device_common.h", "kernels.h", "api.cpp"]   # api.cpp picks the route and tile
 
 
 def flops(wl) -> int:

@@ -58,6 +58,13 @@ int mma_tile_cols(int tile);
 // out: kOutBf16 / kOutFp8 / kOutF32; act: kActNone / kActRelu / kActGelu.
 hipError_t launch_mma_bf16(const MmaArgs& args, bool conv, int act, int tile, hipStream_t stream);
 hipError_t launch_mma_fp8(const MmaArgs& args, int act, int out, int tile, hipStream_t stream);
+// instantiation groups of the MFMA kernel (one translation unit each); wide: rows of 8 MB or
+// more, read by 64-bit global addresses
+hipError_t launch_mma_bf16_dense(const MmaArgs& args, bool wide, int act, int tile, hipStream_t stream);
+hipError_t launch_mma_bf16_gated(const MmaArgs& args, bool wide, int act, int tile, hipStream_t stream);
+hipError_t launch_mma_bf16_conv(const MmaArgs& args, int act, int tile, hipStream_t stream);
+hipError_t launch_mma_fp8_q(const MmaArgs& args, bool wide, int act, int tile, hipStream_t stream);
+hipError_t launch_mma_fp8_b(const MmaArgs& args, bool wide, int act, int out, int tile, hipStream_t stream);
 
 // fp32 direct convolution with the same epilogue (bias -> residual -> act).
 struct ConvF32Args {
