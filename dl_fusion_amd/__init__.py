@@ -63,6 +63,23 @@ def gemm_desc(m, n, k, in_dtype="bf16", out_dtype="bf16", act="none", out_inv_sc
                          ACTS.get(act, act), out_inv_scale)
 
 
+OPS = {"input": 0, "conv": 1, "matmul": 2, "matmul_fp8": 3, "bias_add": 4, "batchnorm": 5, "add": 6,
+       "relu": 7, "gelu": 8, "gelu_erf": 9, "quant": 10}
+DLF_OP_OTHER = 11
+DLF_NODE_OUTPUT, DLF_NODE_TRAINING = 1, 2
+
+
+class dlf_graph_node(ctypes.Structure):
+    _fields_ = [("op", ctypes.c_int32), ("n_inputs", ctypes.c_int32), ("inputs", ctypes.c_int32 * 2),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("rank", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("shape", ctypes.c_int64 * 4), ("flops", ctypes.c_int64)]
+
+
+class dlf_fusion_group(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("nodes", ctypes.c_int32 * 5), ("saved_bytes", ctypes.c_int64),
+                ("net_benefit", ctypes.c_double)]
+
+
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _f32p = ctypes.POINTER(ctypes.c_float)
@@ -81,6 +98,8 @@ _SIGS = {
     "dlf_add": [_i64, ctypes.c_int, _vp, _vp, _vp, _vp],
     "dlf_act_apply": [_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp],
     "dlf_quant_apply": [_i64, _vp, ctypes.c_float, _vp, _vp],
+    "dlf_fusion_plan": [ctypes.POINTER(dlf_graph_node), ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                        ctypes.POINTER(dlf_fusion_group), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -230,6 +249,44 @@ def dlf_act_apply(count, dt, act, x, out, stream=None):
 def dlf_quant_apply(count, x, inv_scale, codes, stream=None):
     _check(_lib.dlf_quant_apply(count, _dev(x), float(inv_scale), _dev(codes), _stream(stream)),
            "dlf_quant_apply")
+
+
+def graph_nodes(graph):
+    """A graph given as node dicts (op, inputs, shape, dtype, flops, output, training; op names
+    as in OPS, any other name is DLF_OP_OTHER) as a dlf_graph_node array."""
+    arr = (dlf_graph_node * len(graph))()
+    for i, nd in enumerate(graph):
+        x = arr[i]
+        x.op = OPS.get(nd["op"], DLF_OP_OTHER)
+        ins = list(nd["inputs"])
+        if len(ins) > 2:
+            raise ValueError(f"node {i}: at most two inputs")
+        x.n_inputs = len(ins)
+        for j, v in enumerate(ins):
+            x.inputs[j] = v
+        x.dtype = DTYPES.get(nd["dtype"], nd["dtype"])
+        x.flags = (DLF_NODE_OUTPUT if nd.get("output") else 0) | (DLF_NODE_TRAINING if nd.get("training") else 0)
+        shp = tuple(nd["shape"])
+        if len(shp) > 4:
+            raise ValueError(f"node {i}: rank above 4")
+        x.rank = len(shp)
+        for d, v in enumerate(shp):
+            x.shape[d] = v
+        x.flops = int(nd.get("flops", 0))
+    return arr
+
+
+def dlf_fusion_plan(graph, ridge, overhead_frac):
+    """Groups chosen by the library's fusion pass: a list of dicts with "nodes" (chain order),
+    "saved" (bytes) and "net" (bytes), in order of their first node."""
+    arr = graph_nodes(graph)
+    count = ctypes.c_int32(0)
+    cap = max(1, len(graph))        # groups are disjoint and hold two or more nodes each
+    out = (dlf_fusion_group * cap)()
+    _check(_lib.dlf_fusion_plan(arr, len(graph), float(ridge), float(overhead_frac), out, cap,
+                                ctypes.byref(count)), "dlf_fusion_plan")
+    return [{"nodes": list(out[i].nodes[:out[i].count]), "saved": int(out[i].saved_bytes),
+             "net": float(out[i].net_benefit)} for i in range(count.value)]
 
 
 def raw():

@@ -12,10 +12,13 @@
 #include "../../include/dlfusion.h"
 #include "device_common.h"
 #include "kernels.h"
+#include "status.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+namespace dlf {
 
 dlf_status fail(dlf_status s, const char* fmt, ...) {
     va_list ap;
@@ -29,6 +32,13 @@ dlf_status ok() {
     g_last_error[0] = '\0';
     return DLF_OK;
 }
+
+}  // namespace dlf
+
+namespace {
+
+using dlf::fail;
+using dlf::ok;
 
 dlf_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();

@@ -278,6 +278,89 @@ dlf_status dlf_quant_apply(int64_t count, const float *in, float inv_scale, uint
                            void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Host fusion pass: which chains of a graph become one fused launch        */
+/* ---------------------------------------------------------------------- */
+
+/* Operation of a graph node.  The pass fuses a contraction (CONV, MATMUL,
+ * MATMUL_FP8) with the epilogue ops that follow it; every other op is kept. */
+typedef enum {
+    DLF_OP_INPUT = 0,           /* a tensor that no node computes */
+    DLF_OP_CONV = 1,
+    DLF_OP_MATMUL = 2,
+    DLF_OP_MATMUL_FP8 = 3,      /* fp8 codes in, dequantised fp32 out */
+    DLF_OP_BIAS_ADD = 4,
+    DLF_OP_BATCHNORM = 5,
+    DLF_OP_ADD = 6,             /* elementwise, two inputs */
+    DLF_OP_RELU = 7,
+    DLF_OP_GELU_TANH = 8,
+    DLF_OP_GELU_ERF = 9,
+    DLF_OP_QUANT = 10,          /* static e4m3 quantisation */
+    DLF_OP_OTHER = 11           /* anything else (Reshape, Transpose, ...): never fused */
+} dlf_op;
+
+#define DLF_NODE_OUTPUT 1u      /* the node's tensor is a graph output and must reach memory */
+#define DLF_NODE_TRAINING 2u    /* a BatchNorm in training mode (never folded) */
+
+/* One node of a graph in topological order.  inputs[j] < the node's own
+ * index.  shape is the output shape (rank 0..4, extents >= 0); dtype its
+ * storage type; flops the node's arithmetic as the caller counts it (2MNK for
+ * a contraction, a few per element for the rest). */
+typedef struct {
+    int32_t op;                 /* dlf_op */
+    int32_t n_inputs;           /* 0, 1 or 2 */
+    int32_t inputs[2];
+    int32_t dtype;              /* dlf_dtype */
+    uint32_t flags;             /* DLF_NODE_* */
+    int32_t rank;
+    int32_t reserved;           /* 0 */
+    int64_t shape[4];
+    int64_t flops;
+} dlf_graph_node;
+
+/* One fused group: nodes[0] is the contraction, then its epilogue ops in
+ * chain order (at most bias/BN, Add, activation, quantisation). */
+typedef struct {
+    int32_t count;              /* 2..5 */
+    int32_t nodes[5];
+    int64_t saved_bytes;        /* HBM bytes the fusion avoids */
+    double net_benefit;         /* saved_bytes - overhead, in bytes */
+} dlf_fusion_group;
+
+/* Plan the fusions of a graph with the three stages of the CANN
+ * graph-autofusion article ([CANN]):
+ *  1. pattern matching: from every contraction, follow the chain
+ *       contraction [bias_add | batchnorm] [add] [activation] [quant]
+ *     (the fused epilogue's order, [OPPL] §4.3; quant only after MATMUL_FP8,
+ *     which takes no Add).  A value may flow on only when it has exactly one
+ *     reader and is not a graph output ([OPPL] §4.1, §4.2); a BatchNorm must
+ *     be in inference mode ([OPPL] §4.1); the other operand of the Add must
+ *     have the chain's shape and dtype (no broadcast, [OPPL] §4.2); every op
+ *     keeps the contraction's output shape and dtype.  Every prefix of two or
+ *     more ops is a candidate.
+ *  2. benefit: saved_bytes = 2 x the bytes of every tensor inside the chain
+ *     (each would be written once and read back once); overhead =
+ *     overhead_frac x (sum of the group's flops) / ridge, the bytes the HBM
+ *     moves while the chip does that fraction of the group's arithmetic
+ *     (ridge = peak flop/s over peak bytes/s); net = saved - overhead in
+ *     binary64.  Candidates with net <= 0 are dropped.
+ *  3. conflict resolution: greedy by net benefit, largest first (ties: the
+ *     lower first node, then the longer chain); a candidate sharing an op with
+ *     one already taken is dropped.
+ * Groups are written in order of their first node.
+ *   nodes        host, [n_nodes] (NULL when n_nodes == 0)
+ *   ridge        > 0 and finite (MI355X bf16: 2516.6e12 / 8e12)
+ *   overhead_frac  >= 0 and finite (the article's 0.05)
+ *   groups       host, [capacity]; may be NULL when capacity == 0
+ *   n_groups     host, receives the number of groups
+ * Returns DLF_ERR_INVALID_ARG for a malformed graph (bad op, dtype, rank,
+ * negative extent or flops, an input index not below the node's own) and
+ * when capacity is too small (then *n_groups holds the number needed and no
+ * group is written).  Synchronous; touches no GPU. */
+dlf_status dlf_fusion_plan(const dlf_graph_node *nodes, int32_t n_nodes, double ridge,
+                           double overhead_frac, dlf_fusion_group *groups, int32_t capacity,
+                           int32_t *n_groups);
+
+/* ---------------------------------------------------------------------- */
 /* Status                                                                   */
 /* ---------------------------------------------------------------------- */
 
