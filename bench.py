@@ -178,7 +178,10 @@ def run_next_rows(torch, steps: int, warmup: int, eager: bool):
     """The widened rows, each against what it replaces:
     - the Q/K/V projections of a LLaMA-7B layer (4096 tokens, h = 4096) as one GEMM over the
       concatenated [3h, h] weights stored split into Q, K and V, vs three separate GEMMs;
-    - the 4096 x 11008 x 4096 GEMM with the exact (erf) GELU epilogue, vs its unfused chain."""
+    - the 4096 x 11008 x 4096 GEMM with the exact (erf) GELU epilogue, vs its unfused chain;
+    - a ResNet stem (batch 32, 224x224x3, 7x7 stride 2, three input channels) and a two-block
+      ResNet bottleneck stage (batch 32, 56x56x256 -> 28x28x512, strided downsample branch),
+      each run under the host fusion pass's plan vs every op on its own."""
     import dl_fusion_amd as d
     from dl_fusion_amd.layers import make_layer
     timer = time_eager if eager else time_graph
@@ -217,6 +220,25 @@ def run_next_rows(torch, steps: int, warmup: int, eager: bool):
         "ms_unfused_chain": ms_u, "speedup_vs_unfused": ms_u / ms}
     del L, inp
     torch.cuda.empty_cache()
+    from dl_fusion_amd.layers import to_device
+    from dl_fusion_amd.network import Network
+    from workloads import graphs
+    nets = (("f3_resnet_stem", "resnet_stem_bf16_n32_224x224x3_7x7s2_to_112x112x64_bn_relu", graphs.stem_graph(n=32)),
+            ("f3_resnet_stage", "resnet_stage_bf16_n32_56x56x256_to_28x28x512_2_bottlenecks",
+             graphs.resnet_stage_graph()))
+    for key, name, g in nets:
+        params = graphs.draw_params(g, seed=11)
+        fused, plain = Network(g, params, fuse=True), Network(g, params, fuse=False)
+        dev = {j: to_device(workloads.bf16_bits(params[j]["x"]), "bf16") for j in fused.inputs}
+        ms = timer(torch, lambda: fused.forward(dev), steps, warmup)
+        ms_u = timer(torch, lambda: plain.forward(dev), steps, warmup)
+        fl = sum(nd["flops"] for nd in g if nd["op"] == "conv")
+        out[key] = {"workload": name, "conv_gflop": fl / 1e9, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+                    "frac_mfma_peak": fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], "launches": fused.launches,
+                    "hbm_bytes_saved_by_plan": fused.saved_bytes, "ms_unfused": ms_u,
+                    "launches_unfused": plain.launches, "speedup_vs_unfused": ms_u / ms}
+        del fused, plain, dev, params
+        torch.cuda.empty_cache()
     return out
 
 

@@ -24,6 +24,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
 
+# torch's ROCm build carries its own HIP runtime under the same soname as the system one the
+# library links against.  Loading torch first makes the library bind to that runtime, so one
+# HIP runtime serves the process; with the library loaded first, its calls found no device
+# while torch's allocations went on working.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------------------

@@ -151,13 +151,11 @@ dlf_status check_conv(const dlf_conv_desc* d, const void* x, const void* w, cons
     g->M = d->n * g->ho * g->wo;
     g->K = d->kh * d->kw * d->c_in;
     if (d->dtype == DLF_FP8_E4M3) return fail(DLF_ERR_UNSUPPORTED, "fp8 convolution has no fused kernel");
-    if (d->dtype == DLF_BF16 && d->c_in % 8 != 0)
-        return fail(DLF_ERR_UNSUPPORTED, "bf16 convolution needs c_in %% 8 == 0 (got %lld)",
-                    static_cast<long long>(d->c_in));
-    // 32-bit index limits of the kernels
+    // 32-bit index limits of the kernels (the value-by-value gather for c_in % 8 != 0 also
+    // indexes a whole image row, w * c_in, in 32 bits)
     const int64_t lim = int64_t(1) << 30;
     if (d->n * d->h * d->w > lim || g->K > lim || d->c_out > lim || d->h > lim || d->w > lim ||
-        g->ho * g->wo > lim || d->n * (d->h + d->kh) * (d->w + d->kw) > lim)
+        g->ho * g->wo > lim || d->n * (d->h + d->kh) * (d->w + d->kw) > lim || d->w * d->c_in > lim)
         return fail(DLF_ERR_UNSUPPORTED, "tensor too large for 32-bit pixel indexing");
     if (g->M == 0 || d->c_out == 0) return ok();
     if (!y || (g->K > 0 && (!x || !w)))

@@ -16,7 +16,9 @@ hipError_t launch_mma_bf16_conv(const MmaArgs& a, int act, int tile, hipStream_t
     };
     // a 64-byte slice (32 bf16) stays inside one kernel tap when Cin % 32 == 0
     if (a.Cin % 32 == 0) return go(std::integral_constant<int, kConvAligned>{});
-    return go(std::integral_constant<int, kConvGeneric>{});
+    // a 16-byte chunk (8 bf16) stays inside one tap when Cin % 8 == 0; otherwise value by value
+    if (a.Cin % 8 == 0) return go(std::integral_constant<int, kConvGeneric>{});
+    return go(std::integral_constant<int, kConvAnyC>{});
 }
 
 }  // namespace dlf

@@ -50,7 +50,10 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64];
 // Operand A modes: dense rows read through a buffer resource per tile panel (32-bit offsets,
 // rows below 8 MB), dense rows read by 64-bit global addresses (longer rows), or gathered
 // from an NHWC convolution input.
-enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2, kDenseWide = 3 };
+// A operand: dense rows (32-bit buffer offsets, or 64-bit addresses for rows of 8 MB or more),
+// or gathered from an NHWC image: a 64-byte slice inside one kernel tap (Cin % 32 == 0), a
+// 16-byte chunk inside one tap (Cin % 8 == 0), or value by value (any Cin).
+enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2, kDenseWide = 3, kConvAnyC = 4 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1, bool REG_ = false>
 struct TileShape {
@@ -149,7 +152,10 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     constexpr int CE = 16 / ELEM;                 // elements per 16-byte chunk
     constexpr int KE = kRowBytes / ELEM;          // K elements per slice
     constexpr int S = TS::STAGES;
-    constexpr int LOADS = TS::LA + TS::LB;        // vmcnt units per slice per lane
+    // vmcnt units per slice per lane.  The value-by-value gather completes inside the slice's
+    // issue (its values pass through registers into LDS), so it leaves none outstanding.
+    constexpr int LOADS = AMODE == kConvAnyC ? 0 : TS::LA + TS::LB;
+    static_assert(AMODE != kConvAnyC || !TS::REG, "the gather writes LDS itself");
     using F = Frag<ELEM>;
     // the LDS holds the operand ring during the K loop and the rounded output tile after it
     constexpr int STAGED = OUT == kOutF32 ? 0 : TS::BM * TS::BN * (OUT == kOutFp8 ? 1 : 2);
@@ -262,6 +268,53 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
                 const int64_t off = (static_cast<int64_t>(a_pix[j] + r * p.W + s) * p.Cin + ci) * ELEM;
                 sink(j, ok ? static_cast<const void*>(a_bytes + off) : zp, sA + (wave * TS::LA + j) * 1024);
             }
+        } else if constexpr (AMODE == kConvAnyC) {
+            // Any Cin: each of a chunk's 8 values is fetched on its own (zero outside the
+            // image) and the chunk reaches LDS through registers, at the place the LDS-DMA
+            // load would have put it.  Kernel row r covers the contiguous run t in [0, KW*Cin)
+            // of input row a_h + r from column a_w on, so k = r*KW*Cin + t needs one division
+            // per chunk and the column test is a range test on a_w*Cin + t.  The weight rows
+            // (K values, K not a multiple of 8) are not 16-byte aligned either and are read
+            // the same way, with zeros past K and past N.
+            static_assert(ELEM == 2, "bf16 gather");
+            const uint16_t* const xs = static_cast<const uint16_t*>(p.a);
+            const int RK = p.KW * p.Cin, WC = p.W * p.Cin;
+#pragma unroll
+            for (int j = 0; j < TS::LA; ++j) {
+                const int k0 = kbase + a_lchunk[j] * CE;
+                int r = k0 / RK;
+                int t = k0 - r * RK;
+                const int q0 = a_w[j] * p.Cin;
+                uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    const bool ok = a_rowok[j] && k0 + e < K &&
+                                    static_cast<unsigned>(a_h[j] + r) < static_cast<unsigned>(p.H) &&
+                                    static_cast<unsigned>(q0 + t) < static_cast<unsigned>(WC);
+                    uint32_t val = 0u;
+                    if (ok) val = xs[static_cast<int64_t>(a_pix[j] + r * p.W) * p.Cin + t];
+                    v[e >> 1] |= val << (16 * (e & 1));
+                    if (++t == RK) { t = 0; ++r; }
+                }
+                *reinterpret_cast<u32x4_t*>(sA + (wave * TS::LA + j) * 1024 + lane * 16) =
+                    u32x4_t{v[0], v[1], v[2], v[3]};
+            }
+            const uint16_t* const ws = static_cast<const uint16_t*>(p.b);
+#pragma unroll
+            for (int j = 0; j < TS::LB; ++j) {
+                const int n = n0 + (wave * TS::LB + j) * kRowsPerLoad + prow;
+                const int k0 = kbase + b_lchunk[j] * CE;
+                uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    uint32_t val = 0u;
+                    if (n < N && k0 + e < K) val = ws[static_cast<int64_t>(n) * K + k0 + e];
+                    v[e >> 1] |= val << (16 * (e & 1));
+                }
+                *reinterpret_cast<u32x4_t*>(sB + (wave * TS::LB + j) * 1024 + lane * 16) =
+                    u32x4_t{v[0], v[1], v[2], v[3]};
+            }
+            return;
         } else if constexpr (BUF) {
 #pragma unroll
             for (int j = 0; j < TS::LA; ++j) {
@@ -468,7 +521,8 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         constexpr int OB = OUT == kOutFp8 ? 1 : 2;            // output bytes per element
         // gated: columns (2j, 2j+1) are (gate j, up j) and give output column j
         constexpr bool GATED = ACT >= kActSiluMul;
-        static_assert(!GATED || (OUT == kOutBf16 && AMODE != kConvAligned && AMODE != kConvGeneric),
+        static_assert(!GATED || (OUT == kOutBf16 && AMODE != kConvAligned && AMODE != kConvGeneric &&
+                                 AMODE != kConvAnyC),
                       "gated epilogue: dense bf16 output");
         constexpr int SROW = (GATED ? TS::BN / 2 : TS::BN) * OB;   // staging row bytes
         constexpr int CPR = SROW / 16;                        // 16-byte chunks per staged row

@@ -35,9 +35,11 @@
  *    caller runs the unfused chain instead.  Nothing is ever approximated
  *    silently ([OPPL] §4.2 falls back to separate ops when a fused form does
  *    not apply; [RFC] §3.7 falls back to the original graph on a mismatch).
- *  - Device pointers must be 16-byte aligned (vector loads); bf16 inputs need
- *    their contiguous dimension (c_in, or k) to be a multiple of 8, fp8 inputs
- *    a multiple of 16.  Zero-sized outputs are valid and launch nothing.
+ *  - Device pointers must be 16-byte aligned (vector loads); bf16 GEMM inputs
+ *    need k to be a multiple of 8, fp8 inputs a multiple of 16.  A bf16
+ *    convolution takes any c_in (c_in % 8 != 0, such as a 3-channel image,
+ *    gathers its operands value by value: slower, for stems).  Zero-sized
+ *    outputs are valid and launch nothing.
  *  - The output must not overlap any input (DLF_ERR_ALIAS): every input
  *    element is read by many output tiles.
  *  - Thread safety: no global mutable state besides the thread-local error.
@@ -166,7 +168,7 @@ dlf_status dlf_bn_scale_shift(int64_t cout, const float *conv_bias, const float 
  * ([OPPL] §4.2 and §6.2, [INFR] §4.1); the output is rounded once (RNE).
  * Each element of y is written to device memory exactly once.
  *   d        host descriptor; dtype DLF_F32 (fp32 FMA kernel) or DLF_BF16
- *            (bf16 MFMA implicit GEMM, c_in % 8 == 0); DLF_FP8_E4M3 ->
+ *            (bf16 MFMA implicit GEMM, any c_in); DLF_FP8_E4M3 ->
  *            DLF_ERR_UNSUPPORTED
  *   x, w     device, layouts as in dlf_conv_desc, type d->dtype
  *   bias     device [c_out] fp32, or NULL (no bias)

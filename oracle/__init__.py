@@ -59,6 +59,7 @@ def _load():
         "orc_gelu_tanh": (None, [_i64, _dp, _dp]),
         "orc_gelu_erf": (None, [_i64, _dp, _dp]),
         "orc_silu": (None, [_i64, _dp, _dp]),
+        "orc_round_bf16": (None, [_i64, _dp, _dp]),
         "orc_fold_bn": (None, [_i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]),
         "orc_e4m3_to_double": (ctypes.c_double, [ctypes.c_int]),
         "orc_e4m3_from_double": (ctypes.c_int, [ctypes.c_double]),
@@ -214,6 +215,15 @@ def gelu_tanh(u):
     u = _d(u)
     out = np.empty_like(u)
     _load().orc_gelu_tanh(u.size, _ptr(u), _ptr(out))
+    return out
+
+
+def round_bf16(v):
+    """The nearest bfloat16 value of each binary64 value (ties to even), widened back: the
+    storage rounding of a bf16 tensor, taken in one step from binary64."""
+    v = _d(v)
+    out = np.empty_like(v)
+    _load().orc_round_bf16(v.size, _ptr(v), _ptr(out))
     return out
 
 

@@ -298,6 +298,37 @@ void orc_e4m3_encode(int64_t count, const double *v, uint8_t *codes)
         codes[i] = (uint8_t)e4m3_from_double(v[i]);
 }
 
+/* ------------------------------------------------------------------------ */
+/* bfloat16 storage rounding: the nearest bf16 value of a binary64 value,     */
+/* ties to the even significand, in one step (never through binary32, whose  */
+/* first rounding could move a value onto a bf16 tie: the double rounding of */
+/* [OPPL] §6.2).  bf16 keeps binary32's exponent range and 8 significant     */
+/* bits: a value in [2^e, 2^(e+1)) rounds to a multiple of 2^(e-7); below    */
+/* 2^-126 the spacing stays 2^-133 (subnormals); a result of 2^128 or more   */
+/* is infinite.  Returned widened back to binary64.                          */
+/* ------------------------------------------------------------------------ */
+static double bf16_round(double v)
+{
+    if (v == 0.0 || !isfinite(v))
+        return v;
+    int e;
+    frexp(v, &e);                       /* |v| in [2^(e-1), 2^e) */
+    int q = e - 8;                      /* spacing exponent: 8 significant bits */
+    if (q < -133)
+        q = -133;
+    const double r = ldexp(nearbyint(ldexp(v, -q)), q);   /* exact scaling; RNE */
+    if (fabs(r) >= ldexp(1.0, 128))
+        return copysign(INFINITY, v);
+    return r;
+}
+
+void orc_round_bf16(int64_t count, const double *in, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = bf16_round(in[i]);
+}
+
 /* Static output quantisation of fp32 values exactly as an fp32 epilogue takes
  * it: p = fp32(u * inv_scale) (one IEEE binary32 multiply, round to nearest
  * even), then code = Q(p).  [FRT] §3 (static-scale FP8 written by the

@@ -14,6 +14,7 @@ import re
 import numpy as np
 import pytest
 
+import oracle
 from oracle import fusion
 from workloads import graphs
 
@@ -231,3 +232,84 @@ def test_net_benefit_threshold():
     assert saved == 16 and net < 0
     assert fusion.plan(g) == []
     assert [p["nodes"] for p in fusion.plan(g, overhead_frac=0.0)] == [[1, 2]]
+
+
+# ---- the network oracle ----------------------------------------------------------------------
+
+def _identity_block(n=2, h=5, w=6, c=8):
+    g = [dict(op="input", inputs=[], shape=(n, h, w, c), dtype="bf16", flops=0, output=False, training=False,
+              attrs={}),
+         dict(op="conv", inputs=[0], shape=(n, h, w, c), dtype="bf16", flops=2 * n * h * w * c * c, output=False,
+              training=False, attrs=dict(kh=1, kw=1, stride=1, pad=0, cin=c, cout=c)),
+         dict(op="batchnorm", inputs=[1], shape=(n, h, w, c), dtype="bf16", flops=1, output=False, training=False,
+              attrs=dict(eps=0.0)),
+         dict(op="add", inputs=[2, 0], shape=(n, h, w, c), dtype="bf16", flops=1, output=False, training=False,
+              attrs={}),
+         dict(op="relu", inputs=[3], shape=(n, h, w, c), dtype="bf16", flops=1, output=True, training=False,
+              attrs={})]
+    params = {0: {"x": np.random.default_rng(3).standard_normal((n, h, w, c)).astype(np.float32)},
+              1: {"w": np.eye(c, dtype=np.float32).reshape(c, 1, 1, c)},
+              2: {"gamma": np.ones(c, np.float32), "beta": np.zeros(c, np.float32),
+                  "mean": np.zeros(c, np.float32), "var": np.ones(c, np.float32)}}
+    return g, params
+
+
+def test_network_oracle_identity_block_is_exact():
+    """A 1x1 identity conv, an identity BN (gamma 1, beta 0, mean 0, var 1, eps 0) and a
+    residual of the block input: the block computes relu(2 x), exactly in bf16, fused or not."""
+    from oracle import network as onet
+    import workloads as W
+    g, params = _identity_block()
+    bits = W.bf16_bits(params[0]["x"])
+    x = oracle.widen(bits, "bf16")
+    plan = fusion.plan(g)
+    assert [p["nodes"] for p in plan] == [[1, 2, 3, 4]]
+    for pl in (plan, []):
+        out = onet.forward(g, params, {0: bits}, pl)
+        np.testing.assert_array_equal(out[4], np.maximum(2 * x, 0.0))
+    # the fused network keeps only the input and the result in memory
+    assert sorted(onet.forward(g, params, {0: bits}, plan)) == [0, 4]
+
+
+def test_network_oracle_routes_a_resnet_stage_exactly():
+    """Every conv a channel selection at its centre tap (OHWI delta, identity on the first
+    min(cin, cout) channels), every BN the identity: the two-block stage then computes, in
+    exact bf16 arithmetic (values double at most), out1 = relu(S(x', cout) + S(x', cout)) on
+    the selected channels where x' = relu(x)[:, ::2, ::2] for the main branch and x[:, ::2, ::2]
+    for the shortcut, and out2 = relu(2 * out1) on the first cmid channels, out1 elsewhere.
+    Pins the oracle's routing (strides, padding, the shortcut operand, the residual slot),
+    fused and unfused."""
+    from oracle import network as onet
+    import workloads as W
+    n, h, w, cin, cmid, cout = 2, 8, 10, 16, 8, 24
+    g = graphs.resnet_stage_graph(n=n, h=h, w=w, cin=cin, cmid=cmid, cout=cout, stride=2, blocks=2)
+    params = graphs.draw_params(g, seed=4)
+    for i, nd in enumerate(g):
+        if nd["op"] == "conv":
+            a = nd["attrs"]
+            wt = np.zeros((a["cout"], a["kh"], a["kw"], a["cin"]), np.float32)
+            for c in range(min(a["cin"], a["cout"])):
+                wt[c, a["kh"] // 2, a["kw"] // 2, c] = 1.0
+            params[i] = {"w": wt}
+        elif nd["op"] == "batchnorm":
+            c = nd["shape"][-1]
+            nd["attrs"]["eps"] = 0.0
+            params[i] = {"gamma": np.ones(c, np.float32), "beta": np.zeros(c, np.float32),
+                         "mean": np.zeros(c, np.float32), "var": np.ones(c, np.float32)}
+    bits = W.bf16_bits(params[0]["x"])
+    x = oracle.widen(bits, "bf16")
+
+    def sel(t, c):
+        out = np.zeros(t.shape[:-1] + (c,))
+        k = min(c, t.shape[-1])
+        out[..., :k] = t[..., :k]
+        return out
+
+    xs = x[:, ::2, ::2, :]
+    main = sel(sel(np.maximum(sel(x, cmid), 0)[:, ::2, ::2, :], cmid), cout)
+    out1 = np.maximum(main + sel(xs, cout), 0)
+    out2 = np.maximum(sel(sel(np.maximum(sel(out1, cmid), 0), cmid), cout) + out1, 0)
+    for pl in (fusion.plan(g), []):
+        got = onet.forward(g, params, {0: bits}, pl)
+        np.testing.assert_array_equal(got[12], out1)
+        np.testing.assert_array_equal(got[len(g) - 1], out2)

@@ -157,6 +157,46 @@ def test_bf16_conv_ragged_shapes_every_tile(i):
     check_conv(wl, tiles=CONV_TILES, unfused=(i < 3))
 
 
+# Any number of input channels (Cin % 8 != 0): the implicit GEMM gathers both operands value
+# by value.  The stem geometry (7x7, stride 2, pad 3, three channels), a ragged K of 27, one
+# channel, and 5 or 12 channels with a residual and a stride.
+ANYC_BF16 = [
+    dict(n=2, h=23, w=21, cin=3, cout=64, kh=7, kw=7, stride=2, pad=3, act="relu", residual=False),
+    dict(n=3, h=9, w=10, cin=5, cout=40, kh=3, kw=3, stride=1, pad=1, act="gelu_erf", residual=True),
+    dict(n=4, h=6, w=7, cin=1, cout=33, kh=1, kw=1, stride=1, pad=0, act="none", residual=False),
+    dict(n=1, h=13, w=11, cin=12, cout=72, kh=3, kw=3, stride=2, pad=1, act="relu", residual=True),
+    dict(n=2, h=8, w=8, cin=3, cout=129, kh=3, kw=3, stride=1, pad=0, act="gelu_tanh", residual=False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(ANYC_BF16)))
+def test_bf16_conv_any_cin_every_tile(i):
+    wl = workloads.workload(1, conv_bias=bool(i % 2), **ANYC_BF16[i])
+    check_conv(wl, tiles=CONV_TILES, unfused=(i < 2))
+
+
+def test_resnet_stem_full_size_sampled():
+    """The ResNet stem at batch 32: 224x224x3 -> 112x112x64, 7x7 stride 2 pad 3, BN, ReLU; 512
+    sampled output pixels (the four corners among them) against the oracle."""
+    wl = workloads.workload(1, n=32, h=224, w=224, cin=3, cout=64, kh=7, kw=7, stride=2, pad=3,
+                            act="relu", residual=False)
+    inp = workloads.generate(wl)
+    L = layers().make_layer(inp, with_unfused=False)
+    case(f"stem conv_fused {wl}")
+    buf, y = guarded(L.out_shape, torch.bfloat16)
+    L.forward(y=y)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, y.numel())
+    rng = np.random.default_rng(5)
+    pts = np.stack([rng.integers(0, 32, 512), rng.integers(0, 112, 512), rng.integers(0, 112, 512)], 1)
+    pts[:4] = [[0, 0, 0], [31, 111, 111], [0, 0, 111], [31, 111, 0]]
+    ref = oracle.conv_bn_act(inp, pts=pts)
+    got = oracle.widen(host(y, "bf16"), "bf16")[pts[:, 0], pts[:, 1], pts[:, 2], :]
+    err = oracle.rel_error(got, ref)
+    assert err <= TOL["bf16"], err
+    assert np.all(got >= 0)
+
+
 # 3x3 stride-1 pad-1 layers the halo kernel takes: several rows per workgroup with a
 # shorter last row tile, one row per workgroup, 64 / 128 / 256 / 384 input channels,
 # one or two 32-pixel fragments per wave, 48 KB and 96 KB halos.
@@ -661,3 +701,54 @@ def test_unfused_eltwise_passes(dt):
         torch.cuda.synchronize()
         got = oracle.widen(host(out, dt), dt).ravel()[:rows * c - 5]
         assert oracle.rel_error(got, oracle.activation(yw, act).ravel()[:rows * c - 5]) <= tol
+
+
+# ---------------------------------------------------------------------------
+# Networks under the host fusion pass
+# ---------------------------------------------------------------------------
+NETWORKS = [
+    ("stage", dict(n=2, h=14, w=14, cin=64, cmid=32, cout=128, stride=2, blocks=2)),
+    ("stage", dict(n=3, h=9, w=11, cin=24, cmid=16, cout=40, stride=2, blocks=3)),
+    ("stem", dict(n=2, h=32, w=30)),
+]
+
+
+@pytest.mark.parametrize("fuse", [True, False])
+@pytest.mark.parametrize("i", range(len(NETWORKS)))
+def test_network_under_the_fusion_plan(i, fuse):
+    """The library's plan (identical to the oracle's) executed through the C ABI: every
+    tensor the plan keeps in memory against the oracle network evaluated with the same
+    storage roundings (fused chains: folded bf16 weights, one rounding; other ops: a
+    rounding each)."""
+    from oracle import fusion as ofusion, network as onet
+    from workloads import graphs
+    from dl_fusion_amd.network import Network
+    kind, kw = NETWORKS[i]
+    g = graphs.resnet_stage_graph(**kw) if kind == "stage" else graphs.stem_graph(**kw)
+    params = graphs.draw_params(g, seed=7 + i)
+    case(f"network {kind} {kw} fuse={fuse}")
+    net = Network(g, params, fuse=fuse)
+    plan = ofusion.plan(g, net_ridge(), net_frac()) if fuse else []
+    assert [p["nodes"] for p in net.plan] == [p["nodes"] for p in plan]
+    bits = {j: workloads.bf16_bits(params[j]["x"]) for j in net.inputs}
+    dev = {j: layers().to_device(b, "bf16") for j, b in bits.items()}
+    net.forward(dev)
+    torch.cuda.synchronize()
+    ref = onet.forward(g, params, bits, plan)
+    assert sorted(net.bufs) == sorted(k for k in ref if g[k]["op"] != "input")
+    for j, t in net.bufs.items():
+        err = oracle.rel_error(oracle.widen(host(t, "bf16"), "bf16"), ref[j])
+        assert err <= TOL["bf16"], (j, g[j]["op"], err)
+    if fuse:
+        assert net.launches == len(plan) + sum(
+            1 for j, nd in enumerate(g) if nd["op"] != "input" and all(j not in p["nodes"] for p in plan))
+
+
+def net_ridge():
+    from dl_fusion_amd.network import RIDGE_BF16
+    return RIDGE_BF16
+
+
+def net_frac():
+    from dl_fusion_amd.network import OVERHEAD_FRAC
+    return OVERHEAD_FRAC

@@ -175,7 +175,8 @@ def test_conv_validation_statuses():
     A, B, Y = 0x100000, 0x200000, 0x300000      # fake, aligned, disjoint
     d = dlf.conv_desc(1, 8, 8, 16, 16, dtype="bf16")
     assert lib.dlf_conv_fused(None, A, B, None, None, Y, 0) == dlf.DLF_ERR_INVALID_ARG
-    bad = dlf.conv_desc(1, 8, 8, 12, 16, dtype="bf16")                           # c_in % 8 != 0
+    # c_in % 8 != 0 is gathered value by value; an image row of 2^30 values or more is not
+    bad = dlf.conv_desc(1, 1, 1 << 27, 12, 16, kh=1, kw=1, pad=0, dtype="bf16")
     assert lib.dlf_conv_fused(ctypes.byref(bad), A, B, None, None, Y, 0) == dlf.DLF_ERR_UNSUPPORTED
     fp8 = dlf.conv_desc(1, 8, 8, 16, 16, dtype="fp8")
     assert lib.dlf_conv_fused(ctypes.byref(fp8), A, B, None, None, Y, 0) == dlf.DLF_ERR_UNSUPPORTED

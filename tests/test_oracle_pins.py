@@ -458,3 +458,43 @@ def test_metric_floor():
     assert math.isclose(oracle.rel_error(g2, o2), 0.5 / math.sqrt(0.5))
     g3 = o2 + np.array([[0.0, 0.0], [0, 0], [0, 1.0], [0, 0]])
     assert math.isclose(oracle.rel_error(g3, o2), 1.0 / math.sqrt(50.0))
+
+
+def test_round_bf16_single_rounding_ties_and_range():
+    """bf16 storage rounding from binary64: agrees with torch's fp32 -> bf16 cast (round to
+    nearest even) wherever the value is an fp32 value, and with exact rational arithmetic on
+    arbitrary binary64 values; ties go to the even significand; one rounding, not two."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    f32 = np.concatenate([rng.standard_normal(5000), rng.standard_normal(500) * 1e30,
+                          rng.standard_normal(500) * 1e-39, [0.0, -0.0, 1.0, -2.5]]).astype(np.float32)
+    want = torch.from_numpy(f32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(f32.astype(np.float64)), want)
+    # exact: the two bf16 neighbours of v from its binary expansion, the nearer (ties even)
+    v = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000),
+                        1.0 + rng.integers(0, 1 << 10, 200) * 2.0 ** -10])
+    got = oracle.round_bf16(v)
+    for x, gx in zip(v, got):
+        fx = Fraction(float(x))
+        e = abs(fx).numerator.bit_length() - abs(fx).denominator.bit_length()
+        while Fraction(2) ** e > abs(fx):
+            e -= 1
+        while Fraction(2) ** (e + 1) <= abs(fx):
+            e += 1
+        ulp = Fraction(2) ** max(e - 7, -133)
+        lo = (fx / ulp).__floor__()
+        r = fx / ulp - lo
+        k = lo + (1 if r > Fraction(1, 2) or (r == Fraction(1, 2) and lo % 2 == 1) else 0)
+        assert Fraction(float(gx)) == k * ulp, x
+    one = 1.0
+    cases = {one + 2.0 ** -8: one,                            # tie -> even (1.0)
+             one + 3 * 2.0 ** -8: one + 2.0 ** -6,            # tie -> even (mantissa 2)
+             -(one + 2.0 ** -8): -one,
+             one + 2.0 ** -8 + 2.0 ** -30: one + 2.0 ** -7,   # just above the tie: up
+             2.0 ** 128 - 2.0 ** 119 - 2.0 ** 100: 2.0 ** 128 - 2.0 ** 120,   # largest finite
+             2.0 ** 128 - 2.0 ** 119: np.inf,                 # tie at the top goes to 2^128
+             2.0 ** -134: 0.0, 3 * 2.0 ** -134: 2.0 ** -132}  # subnormal ties
+    for x, want in cases.items():
+        assert oracle.round_bf16(np.array([x]))[0] == want, x
+    # one rounding: via fp32, 1 + 2^-8 + 2^-30 would land on the tie and go down to 1.0
+    assert float(np.float32(one + 2.0 ** -8 + 2.0 ** -30)) == one + 2.0 ** -8
