@@ -191,12 +191,26 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
         a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
         return hip_status(dlf::launch_conv_f32(a, act_code(d->act), s), what);
     }
-    // 3x3, stride 1, pad 1: the halo kernels.  DLF_CONV=generic forces the implicit GEMM,
-    // DLF_CONV=stream the halo kernel that streams weights (tests of every route).
+    // 3x3, stride 1, pad 1: the halo kernels; at most four input channels: the small-channel
+    // kernel.  DLF_CONV=generic forces the implicit GEMM, DLF_CONV=stream the halo kernel
+    // that streams weights (tests of every route).
     dlf::HaloPlan plan{};
     const char* force = std::getenv("DLF_CONV");
     const bool generic = force && std::strcmp(force, "generic") == 0;
     const bool stream_only = force && std::strcmp(force, "stream") == 0;
+    dlf::SmallCArgs sc{};
+    if (!generic && g.K > 0 &&
+        dlf::conv_smallc_plan(static_cast<int>(d->n), static_cast<int>(d->h), static_cast<int>(d->w),
+                              static_cast<int>(d->c_in), static_cast<int>(d->c_out), static_cast<int>(d->kh),
+                              static_cast<int>(d->kw), d->stride_h, d->stride_w, d->pad_h, d->pad_w,
+                              static_cast<int>(g.ho), static_cast<int>(g.wo), &sc)) {
+        sc.x = static_cast<const uint16_t*>(x);
+        sc.w = static_cast<const uint16_t*>(w);
+        sc.bias = bias;
+        sc.res = static_cast<const uint16_t*>(residual);
+        sc.y = static_cast<uint16_t*>(y);
+        return hip_status(dlf::launch_conv_smallc(sc, act_code(d->act), s), what);
+    }
     if (!generic && g.K > 0 && d->kh == 3 && d->kw == 3 && d->stride_h == 1 && d->stride_w == 1 &&
         d->pad_h == 1 && d->pad_w == 1 &&
         dlf::conv_halo_plan(static_cast<int>(d->n), static_cast<int>(d->h), static_cast<int>(d->w),
@@ -227,7 +241,10 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     a.H = static_cast<int>(d->h); a.W = static_cast<int>(d->w); a.Cin = static_cast<int>(d->c_in);
     a.Ho = static_cast<int>(g.ho); a.Wo = static_cast<int>(g.wo); a.KW = static_cast<int>(d->kw);
     a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
-    return hip_status(dlf::launch_mma_bf16(a, true, act_code(d->act), pick_tile(g.M, d->c_out, false), s), what);
+    // the value-by-value gather (c_in % 8 != 0) is latency-bound: smaller tiles, more of them
+    const int tile = d->c_in % 8 != 0 && !std::getenv("DLF_TILE") ? static_cast<int>(dlf::kTile128x64)
+                                                                  : pick_tile(g.M, d->c_out, false);
+    return hip_status(dlf::launch_mma_bf16(a, true, act_code(d->act), tile, s), what);
 }
 
 dlf_status check_gemm_common(const dlf_gemm_desc* d, const void* a, const void* b, const void* c) {

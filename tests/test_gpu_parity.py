@@ -175,6 +175,25 @@ def test_bf16_conv_any_cin_every_tile(i):
     check_conv(wl, tiles=CONV_TILES, unfused=(i < 2))
 
 
+# Up to four input channels with whole 16-byte input rows: the small-channel kernel (weights
+# and the input patch re-laid in LDS with 4-channel pixels) by default, the value-by-value
+# implicit GEMM on the forced generic route.  Ragged row tiles, a half channel block
+# (Cout % 64 = 32), residuals, one and two channels, a tall image with many row tiles.
+SMALLC_BF16 = [
+    dict(n=2, h=24, w=16, cin=3, cout=64, kh=7, kw=7, stride=2, pad=3, act="relu", residual=False),
+    dict(n=3, h=10, w=8, cin=4, cout=96, kh=3, kw=3, stride=1, pad=1, act="gelu_erf", residual=True),
+    dict(n=1, h=9, w=16, cin=2, cout=32, kh=5, kw=5, stride=2, pad=2, act="none", residual=True),
+    dict(n=2, h=40, w=40, cin=1, cout=64, kh=3, kw=3, stride=1, pad=0, act="gelu_tanh", residual=False),
+    dict(n=1, h=200, w=64, cin=3, cout=128, kh=7, kw=7, stride=2, pad=3, act="relu", residual=False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALLC_BF16)))
+def test_bf16_conv_small_channel_kernel(i):
+    wl = workloads.workload(1, conv_bias=bool(i % 2), **SMALLC_BF16[i])
+    check_conv(wl, tiles=(4,), unfused=(i < 2))
+
+
 def test_resnet_stem_full_size_sampled():
     """The ResNet stem at batch 32: 224x224x3 -> 112x112x64, 7x7 stride 2 pad 3, BN, ReLU; 512
     sampled output pixels (the four corners among them) against the oracle."""
@@ -709,6 +728,7 @@ def test_unfused_eltwise_passes(dt):
 NETWORKS = [
     ("stage", dict(n=2, h=14, w=14, cin=64, cmid=32, cout=128, stride=2, blocks=2)),
     ("stage", dict(n=3, h=9, w=11, cin=24, cmid=16, cout=40, stride=2, blocks=3)),
+    ("stem", dict(n=2, h=32, w=32)),
     ("stem", dict(n=2, h=32, w=30)),
 ]
 
