@@ -338,6 +338,25 @@ def gemm_gated(inp: dict, gate: str, rows=None):
     return activation(np.ascontiguousarray(y[:, 0::2]), gate) * y[:, 1::2]
 
 
+def ffn(inp: dict, rows=None):
+    """Transformer feed-forward block, FC1 -> activation -> FC2 ([OPPL] §3.2, the FFN fusion:
+    two fully connected layers with an activation between them), with the second layer's
+    bias and the block's residual add in its epilogue ([OPPL] §3.3):
+        y = act(x W1^T + b1) W2^T + b2 [+ residual]
+    in binary64 from the stored bf16 tensors.  rows: optional token indices.  Returns
+    [rows][d_model]."""
+    wl = inp["workload"]
+    x = widen(inp["x"], "bf16")
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    h = activation(bias_add(matmul_nt(x, widen(inp["w1"], "bf16")), inp["b1"]), wl.act)
+    y = bias_add(matmul_nt(h, widen(inp["w2"], "bf16")), inp["b2"])
+    if inp.get("residual") is not None:
+        r = widen(inp["residual"], "bf16")
+        y = add(y, r if rows is None else r[np.asarray(rows)])
+    return y
+
+
 def fp8_gemm_bn_act_quant(inp: dict, act: str = "relu", rows=None):
     """fp8 MatMul with static scales -> BN -> activation -> static e4m3 quantisation.
 

@@ -498,3 +498,32 @@ def test_round_bf16_single_rounding_ties_and_range():
         assert oracle.round_bf16(np.array([x]))[0] == want, x
     # one rounding: via fp32, 1 + 2^-8 + 2^-30 would land on the tie and go down to 1.0
     assert float(np.float32(one + 2.0 ** -8 + 2.0 ** -30)) == one + 2.0 ** -8
+
+
+def test_ffn_against_pure_python_loops():
+    """FC1 -> activation -> FC2 (+ b2, + residual) on a tiny block, against plain Python loops
+    over the definition (no numpy, no oracle kernels): h_f = act(sum_d x_d W1[f][d] + b1_f),
+    y_j = sum_f h_f W2[j][f] + b2_j + r_j; with ReLU and with the tanh GELU."""
+    for act in ("relu", "gelu_tanh"):
+        wl = workloads.FfnWorkload("tiny", m=3, d_model=5, d_ff=7, act=act, residual=True, seed=9)
+        inp = workloads.generate(wl)
+        got = oracle.ffn(inp)
+        x = oracle.widen(inp["x"], "bf16").tolist()
+        w1 = oracle.widen(inp["w1"], "bf16").tolist()
+        w2 = oracle.widen(inp["w2"], "bf16").tolist()
+        r = oracle.widen(inp["residual"], "bf16").tolist()
+        b1 = [float(v) for v in inp["b1"]]
+        b2 = [float(v) for v in inp["b2"]]
+        for t in range(3):
+            h = []
+            for f in range(7):
+                u = sum(x[t][d] * w1[f][d] for d in range(5)) + b1[f]
+                if act == "relu":
+                    h.append(max(u, 0.0))
+                else:
+                    h.append(0.5 * u * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3))))
+            for j in range(5):
+                want = sum(h[f] * w2[j][f] for f in range(7)) + b2[j] + r[t][j]
+                assert abs(got[t][j] - want) <= 1e-12 * (1.0 + abs(want))
+        # rows select tokens
+        np.testing.assert_array_equal(oracle.ffn(inp, rows=[2, 0]), got[[2, 0]])

@@ -24,7 +24,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "ConvWorkload", "GemmWorkload", "Fp8GemmWorkload", "WORKLOADS",
+    "ConvWorkload", "GemmWorkload", "Fp8GemmWorkload", "FfnWorkload", "FFN_BERT_BASE", "WORKLOADS",
     "generate", "bf16_bits", "e4m3_codes", "workload",
 ]
 
@@ -113,6 +113,32 @@ class Fp8GemmWorkload:
         return "fp8"
 
 
+@dataclass(frozen=True)
+class FfnWorkload:
+    """Transformer feed-forward block: y = act(x W1^T + b1) W2^T + b2 [+ residual]; bf16
+    tensors, fp32 biases.  W1 is [d_ff][d_model], W2 is [d_model][d_ff] (the [out][in] layout
+    of a linear layer)."""
+    name: str
+    m: int
+    d_model: int
+    d_ff: int
+    act: str = "gelu_tanh"
+    residual: bool = True
+    seed: int = 5
+
+    @property
+    def kind(self) -> str:
+        return "ffn"
+
+    @property
+    def dtype(self) -> str:
+        return "bf16"
+
+
+# BERT-base's feed-forward block (d_model 768, d_ff 3072) over 64 sequences of 128 tokens
+FFN_BERT_BASE = FfnWorkload("ffn_bf16_8192x768x3072_bias_gelu_tanh_residual", 8192, 768, 3072)
+
+
 WORKLOADS = {
     0: ConvWorkload("conv3x3_f32_n1_32x32_16to32_bias_bn_relu", "f32", 1, 32, 32, 16, 32,
                     conv_bias=True, eps=1e-5, act="relu", seed=0),
@@ -199,6 +225,14 @@ def generate(wl) -> dict:
         wq = e4m3_codes((w.astype(np.float64) / float(s_w)).astype(np.float32))
         out.update(x=xq, w=wq, s_x=float(s_x), s_w=float(s_w), gamma=gamma, beta=beta, mean=mean,
                    var=var, eps=float(wl.eps), conv_bias=None, s_y=float(np.float32(wl.out_scale)))
+    elif isinstance(wl, FfnWorkload):
+        x = rng.standard_normal((wl.m, wl.d_model)).astype(np.float32)
+        w1 = rng.normal(0.0, 1.0 / np.sqrt(max(wl.d_model, 1)), (wl.d_ff, wl.d_model)).astype(np.float32)
+        b1 = rng.normal(0.0, 0.02, wl.d_ff).astype(np.float32)
+        w2 = rng.normal(0.0, 1.0 / np.sqrt(max(wl.d_ff, 1)), (wl.d_model, wl.d_ff)).astype(np.float32)
+        b2 = rng.normal(0.0, 0.02, wl.d_model).astype(np.float32)
+        res = bf16_bits(rng.standard_normal((wl.m, wl.d_model)).astype(np.float32)) if wl.residual else None
+        out.update(x=bf16_bits(x), w1=bf16_bits(w1), b1=b1, w2=bf16_bits(w2), b2=b2, residual=res)
     else:
         raise TypeError(f"unknown workload type {type(wl)!r}")
     return out
