@@ -238,6 +238,11 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     a.K = static_cast<int>(g.K);
     a.out_inv_scale = 1.0f;
     a.dequant = 1.0f;
+    // a 1x1, stride-1, unpadded conv is the GEMM of the [n*h*w][c_in] pixel matrix: the dense
+    // kernel reads it with buffer loads and no gather arithmetic
+    if (!generic && d->kh == 1 && d->kw == 1 && d->stride_h == 1 && d->stride_w == 1 && d->pad_h == 0 &&
+        d->pad_w == 0 && d->c_in % 8 == 0)
+        return hip_status(dlf::launch_mma_bf16(a, false, act_code(d->act), pick_tile(g.M, d->c_out, true), s), what);
     a.H = static_cast<int>(d->h); a.W = static_cast<int>(d->w); a.Cin = static_cast<int>(d->c_in);
     a.Ho = static_cast<int>(g.ho); a.Wo = static_cast<int>(g.wo); a.KW = static_cast<int>(d->kw);
     a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
