@@ -75,6 +75,15 @@ DLF_OP_OTHER = 11
 DLF_NODE_OUTPUT, DLF_NODE_TRAINING = 1, 2
 
 
+class dlf_ffn_desc(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("dtype", ctypes.c_int), ("act", ctypes.c_int)]
+
+
+def ffn_desc(m, d_model, d_ff, act="gelu_tanh", dtype="bf16"):
+    return dlf_ffn_desc(m, d_model, d_ff, DTYPES.get(dtype, dtype), ACTS.get(act, act))
+
+
 class dlf_graph_node(ctypes.Structure):
     _fields_ = [("op", ctypes.c_int32), ("n_inputs", ctypes.c_int32), ("inputs", ctypes.c_int32 * 2),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("rank", ctypes.c_int32),
@@ -104,6 +113,8 @@ _SIGS = {
     "dlf_add": [_i64, ctypes.c_int, _vp, _vp, _vp, _vp],
     "dlf_act_apply": [_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp],
     "dlf_quant_apply": [_i64, _vp, ctypes.c_float, _vp, _vp],
+    "dlf_ffn_pack": [_i64, _i64, _vp, _vp],
+    "dlf_ffn_fused": [ctypes.POINTER(dlf_ffn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "dlf_fusion_plan": [ctypes.POINTER(dlf_graph_node), ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                         ctypes.POINTER(dlf_fusion_group), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
@@ -255,6 +266,21 @@ def dlf_act_apply(count, dt, act, x, out, stream=None):
 def dlf_quant_apply(count, x, inv_scale, codes, stream=None):
     _check(_lib.dlf_quant_apply(count, _dev(x), float(inv_scale), _dev(codes), _stream(stream)),
            "dlf_quant_apply")
+
+
+def dlf_ffn_pack(w_bits):
+    """Host: a [rows][k] bf16 weight (uint16 bit patterns) packed in the fused FFN kernel's
+    fragment order; returns a new uint16 array of the same shape."""
+    w, _ = _host(w_bits, np.uint16)
+    out = np.empty_like(w)
+    rows, k = w.shape
+    _check(_lib.dlf_ffn_pack(rows, k, w.ctypes.data, out.ctypes.data), "dlf_ffn_pack")
+    return out
+
+
+def dlf_ffn_fused(desc, x, w1_packed, b1, w2_packed, b2, residual, y, stream=None):
+    _check(_lib.dlf_ffn_fused(ctypes.byref(desc), _dev(x), _dev(w1_packed), _dev(b1), _dev(w2_packed), _dev(b2),
+                              _dev(residual), _dev(y), _stream(stream)), "dlf_ffn_fused")
 
 
 def graph_nodes(graph):

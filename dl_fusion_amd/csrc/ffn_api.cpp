@@ -1,0 +1,92 @@
+// C ABI of the fused feed-forward block: the load-time weight packing (host) and the one-
+// kernel FC1 -> activation -> FC2 launch.  Every check happens before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/dlfusion.h"
+#include "device_common.h"
+#include "kernels.h"
+#include "status.h"
+
+namespace {
+
+using dlf::fail;
+using dlf::ok;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+extern "C" dlf_status dlf_ffn_pack(int64_t rows, int64_t k, const uint16_t* w, uint16_t* packed) {
+    if (rows < 0 || k < 0) return fail(DLF_ERR_INVALID_ARG, "negative dimension");
+    if (rows % 32 != 0 || k % 16 != 0)
+        return fail(DLF_ERR_INVALID_ARG, "rows must be a multiple of 32 and k of 16");
+    if (rows == 0 || k == 0) return ok();
+    if (!w || !packed) return fail(DLF_ERR_INVALID_ARG, "w and packed must be non-NULL");
+    if (overlaps(w, static_cast<size_t>(rows * k) * 2, packed, static_cast<size_t>(rows * k) * 2))
+        return fail(DLF_ERR_ALIAS, "packed overlaps w");
+    const int64_t ks = k / 16;
+    for (int64_t rb = 0; rb < rows / 32; ++rb)
+        for (int64_t s = 0; s < ks; ++s)
+            for (int lane = 0; lane < 64; ++lane) {
+                const uint16_t* src = w + (32 * rb + lane % 32) * k + 16 * s + 8 * (lane / 32);
+                std::memcpy(packed + ((rb * ks + s) * 64 + lane) * 8, src, 16);
+            }
+    return ok();
+}
+
+extern "C" dlf_status dlf_ffn_fused(const dlf_ffn_desc* d, const void* x, const void* w1_packed,
+                                    const float* b1, const void* w2_packed, const float* b2,
+                                    const void* residual, void* y, void* stream) {
+    if (!d) return fail(DLF_ERR_INVALID_ARG, "ffn descriptor is NULL");
+    if (d->m < 0 || d->d_model < 0 || d->d_ff < 0) return fail(DLF_ERR_INVALID_ARG, "negative dimension");
+    if (d->act != DLF_ACT_NONE && d->act != DLF_ACT_RELU && d->act != DLF_ACT_GELU_TANH &&
+        d->act != DLF_ACT_GELU_ERF)
+        return fail(DLF_ERR_INVALID_ARG, "unknown activation %d", static_cast<int>(d->act));
+    if (d->dtype != DLF_BF16) {
+        if (d->dtype != DLF_F32 && d->dtype != DLF_FP8_E4M3) return fail(DLF_ERR_INVALID_ARG, "unknown dtype");
+        return fail(DLF_ERR_UNSUPPORTED, "the fused feed-forward block is bf16 only");
+    }
+    if (d->d_model != 256 && d->d_model != 512 && d->d_model != 768 && d->d_model != 1024)
+        return fail(DLF_ERR_UNSUPPORTED, "d_model must be 256, 512, 768 or 1024 (got %lld)",
+                    static_cast<long long>(d->d_model));
+    if (d->d_ff <= 0 || d->d_ff % 256 != 0 || d->d_ff > (int64_t(1) << 24))
+        return fail(DLF_ERR_UNSUPPORTED, "d_ff must be a positive multiple of 256 below 2^24");
+    if (d->m > (int64_t(1) << 36)) return fail(DLF_ERR_UNSUPPORTED, "too many tokens");
+    if (d->m == 0) return ok();
+    if (!x || !w1_packed || !w2_packed || !y) return fail(DLF_ERR_INVALID_ARG, "x, weights and y must be non-NULL");
+    if (!aligned16(x) || !aligned16(w1_packed) || !aligned16(w2_packed) || !aligned16(y) ||
+        (b1 && !aligned16(b1)) || (b2 && !aligned16(b2)) || (residual && !aligned16(residual)))
+        return fail(DLF_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const size_t act_bytes = static_cast<size_t>(d->m * d->d_model) * 2;
+    const size_t w_bytes = static_cast<size_t>(d->d_ff * d->d_model) * 2;
+    if (overlaps(y, act_bytes, x, act_bytes) || overlaps(y, act_bytes, w1_packed, w_bytes) ||
+        overlaps(y, act_bytes, w2_packed, w_bytes) || overlaps(y, act_bytes, b1, static_cast<size_t>(d->d_ff) * 4) ||
+        overlaps(y, act_bytes, b2, static_cast<size_t>(d->d_model) * 4) || overlaps(y, act_bytes, residual, act_bytes))
+        return fail(DLF_ERR_ALIAS, "output overlaps an input");
+    dlf::FfnArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.w1p = static_cast<const uint16_t*>(w1_packed);
+    a.b1 = b1;
+    a.w2p = static_cast<const uint16_t*>(w2_packed);
+    a.b2 = b2;
+    a.res = static_cast<const uint16_t*>(residual);
+    a.y = static_cast<uint16_t*>(y);
+    a.M = d->m;
+    a.D = static_cast<int>(d->d_model);
+    a.F = static_cast<int>(d->d_ff);
+    const int act = d->act == DLF_ACT_RELU ? dlf::kActRelu
+                  : d->act == DLF_ACT_GELU_TANH ? dlf::kActGelu
+                  : d->act == DLF_ACT_GELU_ERF ? dlf::kActGeluErf : dlf::kActNone;
+    const hipError_t e = dlf::launch_ffn(a, act, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DLF_ERR_HIP, "dlf_ffn_fused: %s", hipGetErrorString(e));
+    return ok();
+}

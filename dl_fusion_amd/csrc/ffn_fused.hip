@@ -1,0 +1,198 @@
+// Transformer feed-forward block in one kernel, FC1 -> activation -> FC2, with the activated
+// intermediate kept on chip (the FFN fusion of "OpenPPL算子融合深度解析" §3.2; the second
+// layer's bias and the block's residual add ride in its epilogue, §3.3):
+//     y = act(x W1^T + b1) W2^T + b2 [+ residual]
+//
+// A workgroup owns 32 tokens and every one of the d_model output columns, so no partial sum
+// leaves the chip.  It walks d_ff in chunks of 256:
+//   FC1: wave w computes h[32 tokens][32 features] = act(x W1[f]^T + b1) for the chunk's
+//        features 32w .. 32w+31 over all of d_model (x resident in LDS), rounds it to bf16
+//        and puts it in LDS (double-buffered, one barrier per chunk);
+//   FC2: wave w accumulates its d_model/8 output columns over the chunk's 256 features.
+// The 32 x d_model fp32 accumulator stays in registers for the whole walk.  The weights are
+// streamed from L2/HBM in MFMA fragment order (packed once at load time, see dlf_ffn_pack):
+// each wave's fragment of a 32x32x16 MFMA is one contiguous kilobyte, fetched eight
+// fragments ahead into a register ring.  Every weight byte is read once per 32 tokens.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "mma_common.h"
+
+namespace dlf {
+namespace {
+
+constexpr int kTok = 32;           // tokens per workgroup
+constexpr int kChunk = 256;        // d_ff features per chunk (8 waves x 32)
+constexpr int kRing = 8;           // weight fragments in flight per wave
+constexpr int kMaxD = 1024;
+constexpr int kXPitch = kMaxD * 2 + 16;        // bytes per token row of x in LDS (padded)
+constexpr int kHPitch = kChunk * 2 + 16;       // bytes per token row of h in LDS (padded)
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), unrolled at compile time
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for_from(Fn&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    static_for_from<0, N>(f);
+}
+
+// DB: 32-column output blocks per wave (d_model = 256 DB)
+template <int ACT, int DB>
+__global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[kTok * kXPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t hs[2][kTok * kHPitch];
+    constexpr int D = 256 * DB;
+    constexpr int KS1 = D / 16;                 // FC1 k-steps (over d_model)
+    constexpr int KS2 = kChunk / 16;            // FC2 k-steps per chunk (over d_ff)
+    constexpr int QN = KS1 + KS2 * DB;          // weight fragments per wave per chunk
+    static_assert(QN % kRing == 0, "the ring index repeats from chunk to chunk");
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, tok = lane & 31;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kTok;
+    const int F = p.F;
+    const int nchunks = F / kChunk;
+
+    // ---- x rows m0 .. m0+31 into LDS (zero past M) ----
+    for (int i = tid; i < kTok * (D / 8); i += 512) {
+        const int t = i / (D / 8), c = i - t * (D / 8);
+        u32x4_t v{0u, 0u, 0u, 0u};
+        if (m0 + t < p.M) v = *reinterpret_cast<const u32x4_t*>(p.x + (m0 + t) * D + 8 * c);
+        *reinterpret_cast<u32x4_t*>(xs + t * kXPitch + 16 * c) = v;
+    }
+
+    // weight fragment q of chunk c for this wave: q < KS1 is FC1 step q of feature block
+    // 8c + wave; then FC2 step (q - KS1) / DB of output block wave*DB + (q - KS1) % DB
+    const int ks_f = F / 16;
+    auto frag = [&](int c, int q) -> const u32x4_t* {
+        int64_t idx;
+        if (q < KS1) {
+            idx = (static_cast<int64_t>(8 * c + wave) * KS1 + q) * 64 + lane;
+            return reinterpret_cast<const u32x4_t*>(p.w1p) + idx;
+        }
+        const int s = (q - KS1) / DB, b = (q - KS1) - s * DB;
+        idx = (static_cast<int64_t>(wave * DB + b) * ks_f + c * KS2 + s) * 64 + lane;
+        return reinterpret_cast<const u32x4_t*>(p.w2p) + idx;
+    };
+    u32x4_t ring[kRing];
+#pragma unroll
+    for (int q = 0; q < kRing; ++q) ring[q] = *frag(0, q);
+
+    f32x16_t acc2[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc2[b][e] = 0.0f;
+    __syncthreads();
+
+    const uint8_t* const xrow = xs + tok * kXPitch + 16 * half;
+    for (int c = 0; c < nchunks; ++c) {
+        uint8_t* const hbuf = hs[c & 1];
+        const uint8_t* const hrow = hbuf + tok * kHPitch + 16 * half;
+        f32x16_t acc1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc1[e] = 0.0f;
+        // weight fragment q is consumed from ring slot q % kRing, which is then refilled with
+        // fragment q + kRing (the next chunk's first ones near the end)
+        auto take = [&](auto q_c) -> bf16x8_t {
+            constexpr int q = decltype(q_c)::value;
+            const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, ring[q % kRing]);
+            if constexpr (q + kRing < QN) {
+                ring[q % kRing] = *frag(c, q + kRing);
+            } else {
+                if (c + 1 < nchunks) ring[q % kRing] = *frag(c + 1, q + kRing - QN);
+            }
+            return wv;
+        };
+        static_for<KS1>([&](auto q_c) {
+            constexpr int q = decltype(q_c)::value;
+            const bf16x8_t wv = take(q_c);
+            const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(xrow + 32 * q);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xv, acc1, 0, 0, 0);
+        });
+        // FC1 epilogue: lane holds token `tok`, features 32 wave + 8 g + 4 half .. +3
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int fl = 32 * wave + 8 * g + 4 * half;
+            f32x4_t bv{0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.b1) bv = *reinterpret_cast<const f32x4_t*>(p.b1 + c * kChunk + fl);
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(acc1[4 * g + e] + bv[e]);
+            *reinterpret_cast<uint2*>(hbuf + tok * kHPitch + 2 * fl) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+        // this wave's h writes are done; after the barrier every wave's are
+        wait_vm_lgkm<63, 0>();
+        barrier();
+        static_for<KS2 * DB>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int st = i / DB, b = i % DB;
+            const bf16x8_t wv = take(std::integral_constant<int, KS1 + i>{});
+            const bf16x8_t hv = *reinterpret_cast<const bf16x8_t*>(hrow + 32 * st);
+            acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, hv, acc2[b], 0, 0, 0);
+        });
+    }
+
+    // ---- FC2 epilogue: token m0 + tok, columns 32 (wave DB + b) + 8 g + 4 half .. +3 ----
+    const int64_t m = m0 + tok;
+    if (m >= p.M) return;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int col = 32 * (wave * DB + b) + 8 * g + 4 * half;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc2[b][4 * g + e];
+            if (p.b2) {
+                const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.b2 + col);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bv[e];
+            }
+            const int64_t off = m * D + col;
+            if (p.res) {
+                const uint2 rv = *reinterpret_cast<const uint2*>(p.res + off);
+                v[0] += __uint_as_float(rv.x << 16);
+                v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
+                v[2] += __uint_as_float(rv.y << 16);
+                v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
+            }
+            *reinterpret_cast<uint2*>(p.y + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+}
+
+template <int ACT>
+hipError_t launch_d(const FfnArgs& a, dim3 grid, hipStream_t s) {
+    switch (a.D) {
+        case 256: hipLaunchKernelGGL((ffn_kernel<ACT, 1>), grid, dim3(512), 0, s, a); break;
+        case 512: hipLaunchKernelGGL((ffn_kernel<ACT, 2>), grid, dim3(512), 0, s, a); break;
+        case 768: hipLaunchKernelGGL((ffn_kernel<ACT, 3>), grid, dim3(512), 0, s, a); break;
+        case 1024: hipLaunchKernelGGL((ffn_kernel<ACT, 4>), grid, dim3(512), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn(const FfnArgs& a, int act, hipStream_t s) {
+    if (a.M <= 0) return hipSuccess;
+    const int64_t blocks = (static_cast<int64_t>(a.M) + kTok - 1) / kTok;
+    if (blocks > 0x7FFFFFFF || a.F <= 0 || a.F % kChunk != 0) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    switch (act) {
+        case kActNone: return launch_d<kActNone>(a, grid, s);
+        case kActRelu: return launch_d<kActRelu>(a, grid, s);
+        case kActGelu: return launch_d<kActGelu>(a, grid, s);
+        case kActGeluErf: return launch_d<kActGeluErf>(a, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dlf

@@ -127,6 +127,21 @@ bool conv_smallc_plan(int N, int H, int W, int Cin, int Cout, int KH, int KW, in
                       int Ho, int Wo, SmallCArgs* args);
 hipError_t launch_conv_smallc(const SmallCArgs& args, int act, hipStream_t stream);
 
+// Feed-forward block FC1 -> act -> FC2 (+ b2, + residual) in one kernel; weights packed in
+// MFMA fragment order (dlf_ffn_pack).
+struct FfnArgs {
+    const uint16_t* x;      // [M][D]
+    const uint16_t* w1p;    // W1 [F][D], packed
+    const float* b1;        // [F] or nullptr
+    const uint16_t* w2p;    // W2 [D][F], packed
+    const float* b2;        // [D] or nullptr
+    const uint16_t* res;    // [M][D] or nullptr
+    uint16_t* y;            // [M][D]
+    int64_t M;
+    int D, F;               // D in {256, 512, 768, 1024}; F a positive multiple of 256
+};
+hipError_t launch_ffn(const FfnArgs& args, int act, hipStream_t stream);
+
 // Elementwise passes of the unfused chain.  dt: 0 fp32, 1 bf16.
 hipError_t launch_bn_apply(int64_t rows, int64_t c, int dt, const void* y, const float* gamma,
                            const float* beta, const float* mean, const float* var, float eps,

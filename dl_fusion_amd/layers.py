@@ -18,6 +18,7 @@ import numpy as np
 import torch
 
 from . import (dlf_act_apply, dlf_add, dlf_bn_apply, dlf_bn_scale_shift, dlf_conv_fused, dlf_conv_plain,
+               dlf_ffn_fused, dlf_ffn_pack, ffn_desc,
                dlf_fold_bn, dlf_gemm_fused, dlf_gemm_plain, dlf_quant_apply, dlf_scale_shift_apply,
                conv_desc, gemm_desc)
 
@@ -187,10 +188,48 @@ class Fp8LinearBNReluQuant:
         return self.y_unfused
 
 
+class FusedFFN:
+    """Transformer feed-forward block: one dlf_ffn_fused launch (weights packed once at load
+    by dlf_ffn_pack); the unfused form is FC1 (+ b1, act) and FC2 (+ b2, + residual) as two
+    GEMMs with their own register epilogues, the intermediate going through HBM."""
+
+    def __init__(self, inp: dict, device="cuda", with_unfused=True):
+        wl = inp["workload"]
+        self.wl = wl
+        self.desc = ffn_desc(wl.m, wl.d_model, wl.d_ff, wl.act)
+        self.x = to_device(inp["x"], "bf16", device)
+        self.w1p = to_device(dlf_ffn_pack(inp["w1"]), "bf16", device)
+        self.w2p = to_device(dlf_ffn_pack(inp["w2"]), "bf16", device)
+        self.b1 = torch.from_numpy(inp["b1"]).to(device)
+        self.b2 = torch.from_numpy(inp["b2"]).to(device)
+        self.res = to_device(inp.get("residual"), "bf16", device)
+        self.y = torch.empty((wl.m, wl.d_model), dtype=torch.bfloat16, device=device)
+        self.with_unfused = with_unfused
+        if with_unfused:
+            self.w1 = to_device(inp["w1"], "bf16", device)
+            self.w2 = to_device(inp["w2"], "bf16", device)
+            self.desc1 = gemm_desc(wl.m, wl.d_ff, wl.d_model, "bf16", "bf16", wl.act)
+            self.desc2 = gemm_desc(wl.m, wl.d_model, wl.d_ff, "bf16", "bf16", "none")
+            self.h = torch.empty((wl.m, wl.d_ff), dtype=torch.bfloat16, device=device)
+            self.y_unfused = torch.empty_like(self.y)
+
+    def forward(self, stream=None, y=None):
+        out = self.y if y is None else y
+        dlf_ffn_fused(self.desc, self.x, self.w1p, self.b1, self.w2p, self.b2, self.res, out, stream)
+        return out
+
+    def forward_unfused(self, stream=None):
+        dlf_gemm_fused(self.desc1, self.x, self.w1, None, self.b1, None, self.h, stream)
+        dlf_gemm_fused(self.desc2, self.h, self.w2, None, self.b2, self.res, self.y_unfused, stream)
+        return self.y_unfused
+
+
 def make_layer(inp: dict, device="cuda", with_unfused=True):
     kind = inp["workload"].kind
     if kind == "conv":
         return FusedConvBNAct(inp, device, with_unfused)
     if kind == "gemm":
         return FusedLinearAct(inp, device, with_unfused)
+    if kind == "ffn":
+        return FusedFFN(inp, device, with_unfused)
     return Fp8LinearBNReluQuant(inp, device, with_unfused)

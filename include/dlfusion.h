@@ -280,6 +280,52 @@ dlf_status dlf_quant_apply(int64_t count, const float *in, float inv_scale, uint
                            void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Feed-forward block in one kernel: FC1 -> activation -> FC2               */
+/* ---------------------------------------------------------------------- */
+
+/* A transformer feed-forward block ([OPPL] §3.2: the two fully connected
+ * layers and the activation between them fused into one kernel, the
+ * activated intermediate kept on chip; the block's residual add rides in the
+ * second layer's epilogue, [OPPL] §3.3):
+ *     y = act(x W1^T + b1) W2^T + b2 [+ residual]
+ * x, residual, y: [m][d_model]; W1: [d_ff][d_model]; W2: [d_model][d_ff]
+ * (the [out][in] layout of a linear layer); biases fp32. */
+typedef struct {
+    int64_t m, d_model, d_ff;
+    dlf_dtype dtype;            /* DLF_BF16 (else DLF_ERR_UNSUPPORTED) */
+    dlf_act act;
+} dlf_ffn_desc;
+
+/* Load-time packing of one weight matrix W [rows][k] (bf16 bit patterns) into
+ * the order the fused kernel streams it: for each block of 32 rows rb and
+ * each 16-wide k step s, 64 runs of 8 values,
+ *     packed[((rb * (k/16) + s) * 64 + l) * 8 + e]
+ *         = W[32 rb + l % 32][16 s + 8 (l / 32) + e],
+ * i.e. one MFMA operand fragment of a wave per contiguous kilobyte.  Host
+ * memory, synchronous; rows % 32 == 0 and k % 16 == 0 (else
+ * DLF_ERR_INVALID_ARG); packed must not overlap w (DLF_ERR_ALIAS). */
+dlf_status dlf_ffn_pack(int64_t rows, int64_t k, const uint16_t *w, uint16_t *packed);
+
+/* The fused block.  A workgroup owns 32 tokens and all d_model outputs: it
+ * walks d_ff in chunks of 256, computes each chunk of act(x W1^T + b1) into
+ * LDS (rounded to bf16, the operand type of the second product) and
+ * accumulates the chunk's contribution to y in fp32 registers; y is rounded
+ * once (RNE) and written once.
+ *   d          host; d_model in {256, 512, 768, 1024}, d_ff a positive
+ *              multiple of 256 (else DLF_ERR_UNSUPPORTED: run the two GEMMs)
+ *   x          device [m][d_model] bf16
+ *   w1_packed  device, dlf_ffn_pack of W1 (rows d_ff, k d_model)
+ *   b1         device [d_ff] fp32 or NULL
+ *   w2_packed  device, dlf_ffn_pack of W2 (rows d_model, k d_ff)
+ *   b2         device [d_model] fp32 or NULL
+ *   residual   device [m][d_model] bf16 or NULL
+ *   y          device [m][d_model] bf16, not overlapping any input
+ *   stream     hipStream_t or NULL */
+dlf_status dlf_ffn_fused(const dlf_ffn_desc *d, const void *x, const void *w1_packed,
+                         const float *b1, const void *w2_packed, const float *b2,
+                         const void *residual, void *y, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Host fusion pass: which chains of a graph become one fused launch        */
 /* ---------------------------------------------------------------------- */
 

@@ -286,3 +286,43 @@ def test_eltwise_validation_statuses():
     assert lib.dlf_quant_apply(64, A, ctypes.c_float(-1.0), C, 0) == dlf.DLF_ERR_INVALID_ARG
     assert lib.dlf_quant_apply(64, A, ctypes.c_float(1.0), A + 32, 0) == dlf.DLF_ERR_ALIAS
     assert lib.dlf_quant_apply(64, A + 4, ctypes.c_float(1.0), C, 0) == dlf.DLF_ERR_INVALID_ARG
+
+
+def test_ffn_pack_layout_and_checks():
+    """dlf_ffn_pack writes W[32 rb + l % 32][16 s + 8 (l / 32) + e] at
+    ((rb * k/16 + s) * 64 + l) * 8 + e: checked element by element on a random matrix."""
+    rng = np.random.default_rng(8)
+    rows, k = 64, 48
+    w = rng.integers(0, 1 << 16, (rows, k), dtype=np.uint16)
+    p = dlf.dlf_ffn_pack(w).reshape(-1)
+    ks = k // 16
+    for rb in range(rows // 32):
+        for s in range(ks):
+            for lane in range(64):
+                for e in range(8):
+                    assert p[((rb * ks + s) * 64 + lane) * 8 + e] == w[32 * rb + lane % 32, 16 * s + 8 * (lane // 32) + e]
+    lib = dlf.raw()
+    buf = np.zeros(64 * 48, np.uint16)
+    assert lib.dlf_ffn_pack(48, 48, buf.ctypes.data, buf.ctypes.data) == dlf.DLF_ERR_INVALID_ARG   # rows % 32
+    assert lib.dlf_ffn_pack(64, 40, buf.ctypes.data, buf.ctypes.data) == dlf.DLF_ERR_INVALID_ARG   # k % 16
+    assert lib.dlf_ffn_pack(64, 48, buf.ctypes.data, buf.ctypes.data) == dlf.DLF_ERR_ALIAS
+    assert lib.dlf_ffn_pack(64, 48, None, buf.ctypes.data) == dlf.DLF_ERR_INVALID_ARG
+    assert lib.dlf_ffn_pack(0, 48, None, None) == dlf.DLF_OK
+
+
+@fake_pointers
+def test_ffn_validation_statuses():
+    lib = dlf.raw()
+    X, W1, W2, Y = 0x100000, 0x200000, 0x400000, 0x600000
+    fused = lambda d, **kw: lib.dlf_ffn_fused(ctypes.byref(d), kw.get("x", X), W1, None, W2, None,
+                                              kw.get("r", None), kw.get("y", Y), 0)
+    assert fused(dlf.ffn_desc(64, 640, 3072)) == dlf.DLF_ERR_UNSUPPORTED          # d_model
+    assert fused(dlf.ffn_desc(64, 768, 3000)) == dlf.DLF_ERR_UNSUPPORTED          # d_ff % 256
+    assert fused(dlf.ffn_desc(64, 768, 3072, dtype="f32")) == dlf.DLF_ERR_UNSUPPORTED
+    assert fused(dlf.ffn_desc(64, 768, 3072, act=9)) == dlf.DLF_ERR_INVALID_ARG
+    assert fused(dlf.ffn_desc(-1, 768, 3072)) == dlf.DLF_ERR_INVALID_ARG
+    assert fused(dlf.ffn_desc(64, 768, 3072), x=X + 8) == dlf.DLF_ERR_INVALID_ARG  # misaligned
+    assert fused(dlf.ffn_desc(64, 768, 3072), y=X + 64) == dlf.DLF_ERR_ALIAS       # y inside x
+    assert fused(dlf.ffn_desc(64, 768, 3072), r=Y) == dlf.DLF_ERR_ALIAS            # residual == y
+    assert fused(dlf.ffn_desc(0, 768, 3072)) == dlf.DLF_OK                         # empty: no launch
+    assert lib.dlf_ffn_fused(None, X, W1, None, W2, None, None, Y, 0) == dlf.DLF_ERR_INVALID_ARG
