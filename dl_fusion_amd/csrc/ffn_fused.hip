@@ -3,16 +3,18 @@
 // layer's bias and the block's residual add ride in its epilogue, §3.3):
 //     y = act(x W1^T + b1) W2^T + b2 [+ residual]
 //
-// A workgroup owns 32 tokens and every one of the d_model output columns, so no partial sum
-// leaves the chip.  It walks d_ff in chunks of 256:
+// A workgroup owns 32 or 64 tokens and every one of the d_model output columns, so no partial
+// sum leaves the chip.  It walks d_ff in chunks of 256:
 //   FC1: wave w computes h[32 tokens][32 features] = act(x W1[f]^T + b1) for the chunk's
 //        features 32w .. 32w+31 over all of d_model (x resident in LDS), rounds it to bf16
 //        and puts it in LDS (double-buffered, one barrier per chunk);
 //   FC2: wave w accumulates its d_model/8 output columns over the chunk's 256 features.
-// The 32 x d_model fp32 accumulator stays in registers for the whole walk.  The weights are
+// The tokens x d_model fp32 accumulator stays in registers for the whole walk.  The weights are
 // streamed from L2/HBM in MFMA fragment order (packed once at load time, see dlf_ffn_pack):
-// each wave's fragment of a 32x32x16 MFMA is one contiguous kilobyte, fetched eight
-// fragments ahead into a register ring.  Every weight byte is read once per 32 tokens.
+// each wave's fragment of a 32x32x16 MFMA is one contiguous kilobyte, fetched many
+// (16 or 32) fragments ahead into a register ring.  Every weight byte is read once per workgroup, so the
+// weight traffic through L2 falls with the tokens a workgroup owns.
+#include <cstdlib>
 #include <type_traits>
 
 #include "device_common.h"
@@ -22,11 +24,7 @@
 namespace dlf {
 namespace {
 
-constexpr int kTok = 32;           // tokens per workgroup
 constexpr int kChunk = 256;        // d_ff features per chunk (8 waves x 32)
-constexpr int kRing = 8;           // weight fragments in flight per wave
-constexpr int kMaxD = 1024;
-constexpr int kXPitch = kMaxD * 2 + 16;        // bytes per token row of x in LDS (padded)
 constexpr int kHPitch = kChunk * 2 + 16;       // bytes per token row of h in LDS (padded)
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), unrolled at compile time
@@ -42,28 +40,36 @@ __device__ __forceinline__ void static_for(Fn&& f) {
     static_for_from<0, N>(f);
 }
 
-// DB: 32-column output blocks per wave (d_model = 256 DB)
-template <int ACT, int DB>
+// DB: 32-column output blocks per wave (d_model = 256 DB); FT: 32-token fragments per
+// workgroup.  With FT = 2 the weights are read once per 64 tokens (half the L2 traffic of
+// FT = 1) and the h buffer is single (LDS), which costs a second barrier per chunk.
+template <int ACT, int DB, int FT>
 __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[kTok * kXPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t hs[2][kTok * kHPitch];
+    // weight fragments in flight per wave: the stream is latency-bound, so as many as the
+    // registers allow (4 a fragment beside the FT x DB accumulators)
+    constexpr int kRing = FT == 1 && DB <= 3 ? 32 : 16;
     constexpr int D = 256 * DB;
+    constexpr int TOK = 32 * FT;
+    constexpr int XP = D * 2 + 16;              // bytes per token row of x in LDS (padded)
+    constexpr int NB = FT == 1 ? 2 : 1;         // h buffers
+    __shared__ __attribute__((aligned(16))) uint8_t xs[TOK * XP];
+    __shared__ __attribute__((aligned(16))) uint8_t hs[NB][TOK * kHPitch];
     constexpr int KS1 = D / 16;                 // FC1 k-steps (over d_model)
     constexpr int KS2 = kChunk / 16;            // FC2 k-steps per chunk (over d_ff)
     constexpr int QN = KS1 + KS2 * DB;          // weight fragments per wave per chunk
     static_assert(QN % kRing == 0, "the ring index repeats from chunk to chunk");
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, tok = lane & 31;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kTok;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * TOK;
     const int F = p.F;
     const int nchunks = F / kChunk;
 
-    // ---- x rows m0 .. m0+31 into LDS (zero past M) ----
-    for (int i = tid; i < kTok * (D / 8); i += 512) {
+    // ---- x rows m0 .. m0+TOK-1 into LDS (zero past M) ----
+    for (int i = tid; i < TOK * (D / 8); i += 512) {
         const int t = i / (D / 8), c = i - t * (D / 8);
         u32x4_t v{0u, 0u, 0u, 0u};
         if (m0 + t < p.M) v = *reinterpret_cast<const u32x4_t*>(p.x + (m0 + t) * D + 8 * c);
-        *reinterpret_cast<u32x4_t*>(xs + t * kXPitch + 16 * c) = v;
+        *reinterpret_cast<u32x4_t*>(xs + t * XP + 16 * c) = v;
     }
 
     // weight fragment q of chunk c for this wave: q < KS1 is FC1 step q of feature block
@@ -83,20 +89,22 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
 #pragma unroll
     for (int q = 0; q < kRing; ++q) ring[q] = *frag(0, q);
 
-    f32x16_t acc2[DB];
+    f32x16_t acc2[DB][FT];
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc2[b][e] = 0.0f;
+        for (int f = 0; f < FT; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc2[b][f][e] = 0.0f;
     __syncthreads();
 
-    const uint8_t* const xrow = xs + tok * kXPitch + 16 * half;
     for (int c = 0; c < nchunks; ++c) {
-        uint8_t* const hbuf = hs[c & 1];
-        const uint8_t* const hrow = hbuf + tok * kHPitch + 16 * half;
-        f32x16_t acc1;
+        uint8_t* const hbuf = hs[NB == 2 ? (c & 1) : 0];
+        f32x16_t acc1[FT];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc1[e] = 0.0f;
+        for (int f = 0; f < FT; ++f)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc1[f][e] = 0.0f;
         // weight fragment q is consumed from ring slot q % kRing, which is then refilled with
         // fragment q + kRing (the next chunk's first ones near the end)
         auto take = [&](auto q_c) -> bf16x8_t {
@@ -112,20 +120,33 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
         static_for<KS1>([&](auto q_c) {
             constexpr int q = decltype(q_c)::value;
             const bf16x8_t wv = take(q_c);
-            const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(xrow + 32 * q);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xv, acc1, 0, 0, 0);
+#pragma unroll
+            for (int f = 0; f < FT; ++f) {
+                const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(xs + (32 * f + tok) * XP + 16 * half + 32 * q);
+                acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xv, acc1[f], 0, 0, 0);
+            }
         });
-        // FC1 epilogue: lane holds token `tok`, features 32 wave + 8 g + 4 half .. +3
+        if constexpr (NB == 1) {
+            // one h buffer: every wave must be done reading the previous chunk's h
+            if (c > 0) {
+                wait_vm_lgkm<63, 0>();
+                barrier();
+            }
+        }
+        // FC1 epilogue: lane holds token 32 f + tok, features 32 wave + 8 g + 4 half .. +3
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int fl = 32 * wave + 8 * g + 4 * half;
             f32x4_t bv{0.0f, 0.0f, 0.0f, 0.0f};
             if (p.b1) bv = *reinterpret_cast<const f32x4_t*>(p.b1 + c * kChunk + fl);
-            float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(acc1[4 * g + e] + bv[e]);
-            *reinterpret_cast<uint2*>(hbuf + tok * kHPitch + 2 * fl) =
-                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            for (int f = 0; f < FT; ++f) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(acc1[f][4 * g + e] + bv[e]);
+                *reinterpret_cast<uint2*>(hbuf + (32 * f + tok) * kHPitch + 2 * fl) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
         }
         // this wave's h writes are done; after the barrier every wave's are
         wait_vm_lgkm<63, 0>();
@@ -134,63 +155,89 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
             constexpr int i = decltype(i_c)::value;
             constexpr int st = i / DB, b = i % DB;
             const bf16x8_t wv = take(std::integral_constant<int, KS1 + i>{});
-            const bf16x8_t hv = *reinterpret_cast<const bf16x8_t*>(hrow + 32 * st);
-            acc2[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, hv, acc2[b], 0, 0, 0);
+#pragma unroll
+            for (int f = 0; f < FT; ++f) {
+                const bf16x8_t hv = *reinterpret_cast<const bf16x8_t*>(hbuf + (32 * f + tok) * kHPitch + 16 * half + 32 * st);
+                acc2[b][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, hv, acc2[b][f], 0, 0, 0);
+            }
         });
     }
 
-    // ---- FC2 epilogue: token m0 + tok, columns 32 (wave DB + b) + 8 g + 4 half .. +3 ----
-    const int64_t m = m0 + tok;
-    if (m >= p.M) return;
+    // ---- FC2 epilogue: token m0 + 32 f + tok, columns 32 (wave DB + b) + 8 g + 4 half .. +3 ----
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int f = 0; f < FT; ++f) {
+        const int64_t m = m0 + 32 * f + tok;
+        if (m >= p.M) continue;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int col = 32 * (wave * DB + b) + 8 * g + 4 * half;
-            float v[4];
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc2[b][4 * g + e];
-            if (p.b2) {
-                const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.b2 + col);
+            for (int g = 0; g < 4; ++g) {
+                const int col = 32 * (wave * DB + b) + 8 * g + 4 * half;
+                float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                for (int e = 0; e < 4; ++e) v[e] = acc2[b][f][4 * g + e];
+                if (p.b2) {
+                    const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.b2 + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                }
+                const int64_t off = m * D + col;
+                if (p.res) {
+                    const uint2 rv = *reinterpret_cast<const uint2*>(p.res + off);
+                    v[0] += __uint_as_float(rv.x << 16);
+                    v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
+                    v[2] += __uint_as_float(rv.y << 16);
+                    v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
+                }
+                *reinterpret_cast<uint2*>(p.y + off) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
-            const int64_t off = m * D + col;
-            if (p.res) {
-                const uint2 rv = *reinterpret_cast<const uint2*>(p.res + off);
-                v[0] += __uint_as_float(rv.x << 16);
-                v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
-                v[2] += __uint_as_float(rv.y << 16);
-                v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
-            }
-            *reinterpret_cast<uint2*>(p.y + off) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
+    }
 }
 
-template <int ACT>
-hipError_t launch_d(const FfnArgs& a, dim3 grid, hipStream_t s) {
+template <int ACT, int FT>
+hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.M + 32 * FT - 1) / (32 * FT);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks));
     switch (a.D) {
-        case 256: hipLaunchKernelGGL((ffn_kernel<ACT, 1>), grid, dim3(512), 0, s, a); break;
-        case 512: hipLaunchKernelGGL((ffn_kernel<ACT, 2>), grid, dim3(512), 0, s, a); break;
-        case 768: hipLaunchKernelGGL((ffn_kernel<ACT, 3>), grid, dim3(512), 0, s, a); break;
-        case 1024: hipLaunchKernelGGL((ffn_kernel<ACT, 4>), grid, dim3(512), 0, s, a); break;
+        case 256: hipLaunchKernelGGL((ffn_kernel<ACT, 1, FT>), grid, dim3(512), 0, s, a); break;
+        case 512: hipLaunchKernelGGL((ffn_kernel<ACT, 2, FT>), grid, dim3(512), 0, s, a); break;
+        case 768: hipLaunchKernelGGL((ffn_kernel<ACT, 3, FT>), grid, dim3(512), 0, s, a); break;
+        case 1024:
+            if constexpr (FT == 1) {   // 64 tokens of 1024 columns do not fit LDS beside h
+                hipLaunchKernelGGL((ffn_kernel<ACT, 4, FT>), grid, dim3(512), 0, s, a);
+                break;
+            } else {
+                return hipErrorInvalidValue;
+            }
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// 64 tokens per workgroup (half the weight traffic) once that still gives a workgroup per CU
+// (256 of them), else 32; d_model 1024 always takes 32.  DLF_FFN_TOK=32|64 forces one (tests).
+template <int ACT>
+hipError_t launch_act(const FfnArgs& a, hipStream_t s) {
+    int tok = a.M >= 64 * 256 && a.D <= 768 ? 64 : 32;
+    if (const char* env = std::getenv("DLF_FFN_TOK")) {
+        const int t = std::atoi(env);
+        if (t == 32 || (t == 64 && a.D <= 768)) tok = t;
+    }
+    return tok == 64 ? launch_d<ACT, 2>(a, s) : launch_d<ACT, 1>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_ffn(const FfnArgs& a, int act, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
-    const int64_t blocks = (static_cast<int64_t>(a.M) + kTok - 1) / kTok;
-    if (blocks > 0x7FFFFFFF || a.F <= 0 || a.F % kChunk != 0) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(blocks));
+    if (a.F <= 0 || a.F % kChunk != 0) return hipErrorInvalidValue;
     switch (act) {
-        case kActNone: return launch_d<kActNone>(a, grid, s);
-        case kActRelu: return launch_d<kActRelu>(a, grid, s);
-        case kActGelu: return launch_d<kActGelu>(a, grid, s);
-        case kActGeluErf: return launch_d<kActGeluErf>(a, grid, s);
+        case kActNone: return launch_act<kActNone>(a, s);
+        case kActRelu: return launch_act<kActRelu>(a, s);
+        case kActGelu: return launch_act<kActGelu>(a, s);
+        case kActGeluErf: return launch_act<kActGeluErf>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -811,6 +811,29 @@ def test_ffn_fused_against_oracle(i):
         assert err <= TOL["bf16"], ("unfused", err)
 
 
+@pytest.mark.parametrize("tok", ["32", "64"])
+def test_ffn_token_blocks(tok):
+    """Both workgroup sizes (32 and 64 tokens) on ragged token counts, forced."""
+    for i, kw in enumerate([dict(m=150, d_model=768, d_ff=512, act="gelu_tanh", residual=True),
+                            dict(m=65, d_model=256, d_ff=768, act="relu", residual=False),
+                            dict(m=64, d_model=512, d_ff=256, act="gelu_erf", residual=True)]):
+        wl = workloads.FfnWorkload(f"ffn_tok{tok}_{i}", seed=70 + i, **kw)
+        inp = workloads.generate(wl)
+        ref = oracle.ffn(inp)
+        L = layers().make_layer(inp, with_unfused=False)
+        case(f"ffn fused tok={tok} {wl}")
+        os.environ["DLF_FFN_TOK"] = tok
+        try:
+            buf, y = guarded((wl.m, wl.d_model), torch.bfloat16)
+            L.forward(y=y)
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("DLF_FFN_TOK", None)
+        assert guard_intact(buf, y.numel())
+        err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+        assert err <= TOL["bf16"], (tok, i, err)
+
+
 def test_ffn_bert_base_full_size_sampled():
     """BERT-base's block at 8192 tokens: 256 sampled tokens (first and last among them)."""
     wl = workloads.FFN_BERT_BASE
