@@ -182,8 +182,8 @@ def run_next_rows(torch, steps: int, warmup: int, eager: bool):
     - a ResNet stem (batch 32, 224x224x3, 7x7 stride 2, three input channels) and a two-block
       ResNet bottleneck stage (batch 32, 56x56x256 -> 28x28x512, strided downsample branch),
       each run under the host fusion pass's plan vs every op on its own;
-    - BERT-base's feed-forward block (8192 tokens, 768 -> 3072 -> 768, GELU, residual) in one
-      kernel vs two GEMMs with their epilogues and the intermediate in HBM."""
+    - BERT-base's feed-forward block (8192 and 16384 tokens, 768 -> 3072 -> 768, GELU,
+      residual) in one kernel vs two GEMMs with their epilogues and the intermediate in HBM."""
     import dl_fusion_amd as d
     from dl_fusion_amd.layers import make_layer
     timer = time_eager if eager else time_graph
@@ -222,18 +222,20 @@ def run_next_rows(torch, steps: int, warmup: int, eager: bool):
         "ms_unfused_chain": ms_u, "speedup_vs_unfused": ms_u / ms}
     del L, inp
     torch.cuda.empty_cache()
-    wl = workloads.FFN_BERT_BASE
-    inp = workloads.generate(wl)
-    L = make_layer(inp, with_unfused=True)
-    ms = timer(torch, L.forward, steps, warmup)
-    ms_u = timer(torch, L.forward_unfused, steps, warmup)
-    fl = 4 * wl.m * wl.d_model * wl.d_ff
-    out["f4_ffn_back_to_back"] = {
-        "workload": wl.name, "m_dmodel_dff": [wl.m, wl.d_model, wl.d_ff], "ms": ms,
-        "tflops": fl / (ms * 1e-3) / 1e12, "frac_mfma_peak": fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
-        "hbm_bytes_saved": 2 * wl.m * wl.d_ff * 2, "ms_two_gemms": ms_u, "speedup_vs_two_gemms": ms_u / ms}
-    del L, inp
-    torch.cuda.empty_cache()
+    for key, wl in (("f4_ffn_back_to_back", workloads.FFN_BERT_BASE),
+                    ("f4_ffn_back_to_back_16k", dataclasses.replace(
+                        workloads.FFN_BERT_BASE, name="ffn_bf16_16384x768x3072_bias_gelu_tanh_residual", m=16384))):
+        inp = workloads.generate(wl)
+        L = make_layer(inp, with_unfused=True)
+        ms = timer(torch, L.forward, steps, warmup)
+        ms_u = timer(torch, L.forward_unfused, steps, warmup)
+        fl = 4 * wl.m * wl.d_model * wl.d_ff
+        out[key] = {
+            "workload": wl.name, "m_dmodel_dff": [wl.m, wl.d_model, wl.d_ff], "ms": ms,
+            "tflops": fl / (ms * 1e-3) / 1e12, "frac_mfma_peak": fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+            "hbm_bytes_saved": 2 * wl.m * wl.d_ff * 2, "ms_two_gemms": ms_u, "speedup_vs_two_gemms": ms_u / ms}
+        del L, inp
+        torch.cuda.empty_cache()
     from dl_fusion_amd.layers import to_device
     from dl_fusion_amd.network import Network
     from workloads import graphs

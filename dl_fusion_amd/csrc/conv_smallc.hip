@@ -45,27 +45,47 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
         *reinterpret_cast<u32x4_t*>(smem + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
 
-    // ---- weights of channels co0 .. co0+nco-1: one contiguous block of nco*K values ----
+    // ---- weights of channels co0 .. co0+nco-1: one contiguous block of nco*K values.  Four
+    //      16-byte loads per lane go out before their values are scattered; the (co, r, s, ci)
+    //      position of a chunk's first value is divided out once, the next seven step on. ----
     const int K = p.KH * p.KW * p.Cin;
-    const int RK = p.KW * p.Cin;
     {
         const uint8_t* const src = reinterpret_cast<const uint8_t*>(p.w) + static_cast<int64_t>(co0) * K * 2;
         const int chunks = nco * K / 8;                     // whole: nco % 8 == 0
-        for (int c = tid; c < chunks; c += 256) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + 16 * c);
+        for (int c0 = tid; c0 < chunks; c0 += 4 * 256) {
+            u32x4_t v[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = 8 * c + e;
-                const int co = idx / K, k = idx - co * K;
-                const int r = k / RK, rem = k - r * RK;
-                const int s = rem / p.Cin, ci = rem - s * p.Cin;
-                const uint32_t word = v[e >> 1];
-                const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-                *reinterpret_cast<uint16_t*>(sw + (((co * p.KH + r) * p.kwp + s) * 4 + ci) * 2) = val;
+            for (int u = 0; u < 4; ++u)
+                if (c0 + 256 * u < chunks) v[u] = *reinterpret_cast<const u32x4_t*>(src + 16 * (c0 + 256 * u));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + 256 * u;
+                if (c >= chunks) break;
+                const int idx = 8 * c;
+                int co = idx / K, k = idx - co * K;
+                int r = k / (p.KW * p.Cin), rem = k - r * p.KW * p.Cin;
+                int sx_ = rem / p.Cin, ci = rem - sx_ * p.Cin;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t word = v[u][e >> 1];
+                    const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+                    *reinterpret_cast<uint16_t*>(sw + (((co * p.KH + r) * p.kwp + sx_) * 4 + ci) * 2) = val;
+                    if (++ci == p.Cin) {
+                        ci = 0;
+                        if (++sx_ == p.KW) {
+                            sx_ = 0;
+                            if (++r == p.KH) {
+                                r = 0;
+                                ++co;
+                            }
+                        }
+                    }
+                }
             }
         }
     }
-    // ---- input rows hi0 .. hi0+prows-1 of this image, whole rows (W*Cin values each) ----
+    // ---- input rows hi0 .. hi0+prows-1 of this image, whole rows (W*Cin values each), four
+    //      loads per lane in flight as above ----
     const int hi0 = ho0 * p.SH - p.PH;
     const int prows = (rows - 1) * p.SH + p.KH;
     const int row_vals = p.W * p.Cin;
@@ -73,68 +93,102 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
     {
         const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x) + static_cast<int64_t>(img) * p.H * row_vals * 2;
         const int total = prows * row_chunks;
-        for (int c = tid; c < total; c += 256) {
-            const int pr = c / row_chunks, rc = c - pr * row_chunks;
-            const int hi = hi0 + pr;
-            if (static_cast<unsigned>(hi) >= static_cast<unsigned>(p.H)) continue;   // stays zero
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xb + (static_cast<int64_t>(hi) * row_vals + 8 * rc) * 2);
+        for (int c0 = tid; c0 < total; c0 += 4 * 256) {
+            u32x4_t v[4];
+            int pr[4], rc[4];
+            bool ok[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = 8 * rc + e;
-                const int wi = idx / p.Cin, ci = idx - wi * p.Cin;
-                const uint32_t word = v[e >> 1];
-                const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-                *reinterpret_cast<uint16_t*>(sx + ((pr * p.pw + wi + p.PW) * 4 + ci) * 2) = val;
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + 256 * u;
+                pr[u] = c / row_chunks;
+                rc[u] = c - pr[u] * row_chunks;
+                const int hi = hi0 + pr[u];
+                ok[u] = c < total && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H);   // else stays zero
+                if (ok[u]) v[u] = *reinterpret_cast<const u32x4_t*>(xb + (static_cast<int64_t>(hi) * row_vals + 8 * rc[u]) * 2);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!ok[u]) continue;
+                const int idx = 8 * rc[u];
+                int wi = idx / p.Cin, ci = idx - wi * p.Cin;
+                uint8_t* const rowp = sx + (pr[u] * p.pw + p.PW) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t word = v[u][e >> 1];
+                    const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+                    *reinterpret_cast<uint16_t*>(rowp + (wi * 4 + ci) * 2) = val;
+                    if (++ci == p.Cin) {
+                        ci = 0;
+                        ++wi;
+                    }
+                }
             }
         }
     }
     __syncthreads();
 
-    // ---- 32-pixel fragments, dealt round-robin to the four waves ----
+    // ---- 32-pixel fragments, two at a time per wave (fragments f and f + 4), so that four
+    //      accumulator chains interleave on the matrix pipe ----
     const int npx = rows * p.Wo;
     const int nfrag = (npx + 31) / 32;
-    const int ksteps = p.kwp / 4;
+    const int ksteps = p.kwp / 4;                           // 1 .. 4 (the host bounds KH * kwp)
     const int nj = nco / 32;
     uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
-    for (int f = wave; f < nfrag; f += 4) {
-        const int pl = f * 32 + (lane & 31);
-        const bool pv = pl < npx;
-        const int plc = pv ? pl : 0;
-        const int hl = plc / p.Wo, wo = plc - hl * p.Wo;
-        const uint8_t* const abase = sx + ((hl * p.SH) * p.pw + wo * p.SW + 2 * half) * 8;
-        const uint8_t* const bbase = sw + (((lane & 31) * p.KH) * p.kwp + 2 * half) * 8;
-        f32x16_t acc0, acc1;
+    const uint8_t* const bbase = sw + (((lane & 31) * p.KH) * p.kwp + 2 * half) * 8;
+    const int bstep_j = 32 * wgroup * 8;
+    for (int f0 = wave; f0 < nfrag; f0 += 8) {
+        int hl[2], wo[2];
+        bool pv[2];
+        const uint8_t* abase[2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            acc0[e] = 0.0f;
-            acc1[e] = 0.0f;
+        for (int u = 0; u < 2; ++u) {
+            const int pl = (f0 + 4 * u) * 32 + (lane & 31);
+            pv[u] = pl < npx;
+            const int plc = pv[u] ? pl : 0;
+            hl[u] = plc / p.Wo;
+            wo[u] = plc - hl[u] * p.Wo;
+            abase[u] = sx + ((hl[u] * p.SH) * p.pw + wo[u] * p.SW + 2 * half) * 8;
         }
+        f32x16_t acc[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[u][j][e] = 0.0f;
         for (int r = 0; r < p.KH; ++r) {
-            for (int ks = 0; ks < ksteps; ++ks) {
-                const uint8_t* const a = abase + (r * p.pw + 4 * ks) * 8;
-                const uint2 a0 = *reinterpret_cast<const uint2*>(a);
-                const uint2 a1 = *reinterpret_cast<const uint2*>(a + 8);
-                const u32x4_t au{a0.x, a0.y, a1.x, a1.y};
-                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, au);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks >= ksteps) break;
+                bf16x8_t av[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint8_t* const a = abase[u] + (r * p.pw + 4 * ks) * 8;
+                    const uint2 a0 = *reinterpret_cast<const uint2*>(a);
+                    const uint2 a1 = *reinterpret_cast<const uint2*>(a + 8);
+                    av[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
+                }
                 const uint8_t* const b = bbase + (r * p.kwp + 4 * ks) * 8;
                 const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(b);
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av, acc0, 0, 0, 0);
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[0], acc[0][0], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[1], acc[1][0], 0, 0, 0);
                 if (nj > 1) {
-                    const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b + 32 * wgroup * 8);
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av, acc1, 0, 0, 0);
+                    const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b + bstep_j);
+                    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[0], acc[0][1], 0, 0, 0);
+                    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[1], acc[1][1], 0, 0, 0);
                 }
             }
         }
-        if (!pv) continue;
-        // lane: pixel pl; register group g of fragment j holds channels 32 j + 8 g + 4 half .. +3
-        const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hl) * p.Wo + wo;
-        auto store = [&](const f32x16_t& acc, int j) {
+        // lane: pixel of fragment f0 + 4u; register group g of channel fragment j holds
+        // channels 32 j + 8 g + 4 half .. +3
+        auto store = [&](const f32x16_t& accv, int u, int j) {
+            const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hl[u]) * p.Wo + wo[u];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int co = co0 + 32 * j + 8 * g + 4 * half;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[4 * g + e];
+                for (int e = 0; e < 4; ++e) v[e] = accv[4 * g + e];
                 if (p.bias) {
                     const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + co);
 #pragma unroll
@@ -160,8 +214,12 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
                 *reinterpret_cast<uint2*>(yb + off * 2) = make_uint2(lo, hi);
             }
         };
-        store(acc0, 0);
-        if (nj > 1) store(acc1, 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (!pv[u]) continue;
+            store(acc[u][0], u, 0);
+            if (nj > 1) store(acc[u][1], u, 1);
+        }
     }
 }
 
@@ -182,6 +240,7 @@ bool conv_smallc_plan(int N, int H, int W, int Cin, int Cout, int KH, int KW, in
         return false;
     if ((W * Cin) % 8 != 0) return false;                 // whole 16-byte chunks per input row
     const int kwp = (KW + 3) / 4 * 4;
+    if (kwp > 16) return false;                            // at most four MFMA steps per kernel row
     const int wbytes = 64 * KH * kwp * 8;
     if (wbytes > kSmallLds / 2) return false;
     // patch columns: every input column (filled) and every column a fragment reads, padded

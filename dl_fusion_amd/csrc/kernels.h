@@ -121,8 +121,8 @@ struct SmallCArgs {
     int co_blocks;          // ceil(Cout / 64)
 };
 // False when the shape does not qualify (Cin <= 4, Cout a multiple of 32, W*Cin a multiple
-// of 8, the weights of 64 channels within 32 KB and the patch of one output row within the
-// rest of 64 KB); fills everything but the pointers.
+// of 8, KW <= 16, the weights of 64 channels within 32 KB and the patch of one output row
+// within the rest of 64 KB); fills everything but the pointers.
 bool conv_smallc_plan(int N, int H, int W, int Cin, int Cout, int KH, int KW, int SH, int SW, int PH, int PW,
                       int Ho, int Wo, SmallCArgs* args);
 hipError_t launch_conv_smallc(const SmallCArgs& args, int act, hipStream_t stream);
