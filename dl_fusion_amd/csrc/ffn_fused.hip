@@ -47,7 +47,7 @@ template <int ACT, int DB, int FT>
 __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     // weight fragments in flight per wave: the stream is latency-bound, so as many as the
     // registers allow (4 a fragment beside the FT x DB accumulators)
-    constexpr int kRing = FT == 1 && DB <= 3 ? 32 : 16;
+    constexpr int kRing = FT == 1 && (DB == 1 || DB == 3) ? 32 : 16;
     constexpr int D = 256 * DB;
     constexpr int TOK = 32 * FT;
     constexpr int XP = D * 2 + 16;              // bytes per token row of x in LDS (padded)
@@ -100,11 +100,16 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
 
     for (int c = 0; c < nchunks; ++c) {
         uint8_t* const hbuf = hs[NB == 2 ? (c & 1) : 0];
-        f32x16_t acc1[FT];
+        // FC1 accumulators: FT token fragments, each split over even and odd k-steps when there
+        // is only one, so that two independent chains keep the matrix pipe busy
+        constexpr int SPLIT = FT == 1 ? 2 : 1;
+        f32x16_t acc1[FT][SPLIT];
 #pragma unroll
         for (int f = 0; f < FT; ++f)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc1[f][e] = 0.0f;
+            for (int h = 0; h < SPLIT; ++h)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc1[f][h][e] = 0.0f;
         // weight fragment q is consumed from ring slot q % kRing, which is then refilled with
         // fragment q + kRing (the next chunk's first ones near the end)
         auto take = [&](auto q_c) -> bf16x8_t {
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
 #pragma unroll
             for (int f = 0; f < FT; ++f) {
                 const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(xs + (32 * f + tok) * XP + 16 * half + 32 * q);
-                acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xv, acc1[f], 0, 0, 0);
+                acc1[f][q % SPLIT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xv, acc1[f][q % SPLIT], 0, 0, 0);
             }
         });
         if constexpr (NB == 1) {
@@ -143,7 +148,11 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
             for (int f = 0; f < FT; ++f) {
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(acc1[f][4 * g + e] + bv[e]);
+                for (int e = 0; e < 4; ++e) {
+                    float a = acc1[f][0][4 * g + e];
+                    if constexpr (SPLIT == 2) a += acc1[f][SPLIT - 1][4 * g + e];
+                    v[e] = activate<ACT>(a + bv[e]);
+                }
                 *reinterpret_cast<uint2*>(hbuf + (32 * f + tok) * kHPitch + 2 * fl) =
                     make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
