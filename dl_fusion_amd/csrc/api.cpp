@@ -79,19 +79,22 @@ int pick_tile(int64_t M, int64_t N, bool dense) {
         const int t = std::atoi(env);
         if (t >= 0 && t < dlf::kTileCount) return t;
     }
-    const int cands[] = {dlf::kTile256x256, dlf::kTile256x128, dlf::kTile128x128, dlf::kTile256x64,
-                         dlf::kTile128x64, dlf::kTile64x64};
-    const double eff[] = {1.0, 0.9, 0.8, 0.8, 0.65, 0.5};
+    // Measured on MI355X: the four-wave 256x128 and 256x64 tiles lost to 128x128 / 128x64 on
+    // every shape swept (memory-bound 1x1 layers, FFN projections, square GEMMs), and the
+    // four-wave 256x256 tile of the implicit GEMM to 128x128; the dense 256x256 tile is the
+    // eight-wave pipeline.
+    const int cands[] = {dlf::kTile256x256, dlf::kTile128x128, dlf::kTile128x64, dlf::kTile64x64};
+    const double eff[] = {1.0, 0.8, 0.65, 0.5};
     int best = dlf::kTile64x64;
     double best_cost = 0;
-    for (int i = 0; i < 6; ++i) {
+    for (int i = dense ? 0 : 1; i < 4; ++i) {
         const int t = cands[i];
         const int64_t bm = dlf::mma_tile_rows(t), bn = dlf::mma_tile_cols(t);
         if (bn > 64 && N <= bn / 2) continue;   // mostly-empty columns
         const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
         const int64_t rounds = (tiles + 255) / 256;
         const double cost = static_cast<double>(rounds) * static_cast<double>(bm * bn) / eff[i];
-        if (i == 0 || best_cost == 0 || cost < best_cost) {
+        if (best_cost == 0 || cost < best_cost) {
             best = t;
             best_cost = cost;
         }
