@@ -48,6 +48,8 @@ class Network:
                 raise NotImplementedError(f"node {i}: the network runner executes bf16 graphs")
             if nd["op"] not in ("input", "conv", "batchnorm", "add") and nd["op"] not in _ACTS:
                 raise NotImplementedError(f"node {i}: op {nd['op']} is not executed here")
+            if nd["op"] == "batchnorm" and nd.get("training", False):
+                raise NotImplementedError(f"node {i}: a BatchNorm in training mode (batch statistics) is not executed here")
         self.graph = graph
         self.plan = dlf_fusion_plan(graph, ridge, overhead_frac) if fuse else []
         self.saved_bytes = sum(g["saved"] for g in self.plan)

@@ -86,3 +86,32 @@ def test_validation():
     assert dlf.raw().dlf_fusion_plan(None, 3, RIDGE, FRAC, None, 0, ctypes.byref(ctypes.c_int32())) \
         == dlf.DLF_ERR_INVALID_ARG
     assert dlf.raw().dlf_fusion_plan(arr, n, RIDGE, FRAC, None, 0, None) == dlf.DLF_ERR_INVALID_ARG
+
+
+def test_network_runner_plan_and_launches_on_the_host():
+    """The runner's load-time work (plan, fold, buffers) without a GPU: the plan is the
+    library's, one launch per chosen chain plus one per op outside a chain, and buffers only
+    for the tensors the plan keeps in memory."""
+    torch = pytest.importorskip("torch")
+    from dl_fusion_amd.network import Network, OVERHEAD_FRAC, RIDGE_BF16
+    g = graphs.resnet_stage_graph(n=2, h=8, w=8, cin=16, cmid=8, cout=32, stride=2, blocks=2)
+    params = graphs.draw_params(g, seed=3)
+    net = Network(g, params, fuse=True, device="cpu")
+    plan = fusion.plan(g, RIDGE_BF16, OVERHEAD_FRAC)
+    assert [p["nodes"] for p in net.plan] == [p["nodes"] for p in plan]
+    inside = {i for p in plan for i in p["nodes"]}
+    loose = [i for i, nd in enumerate(g) if nd["op"] != "input" and i not in inside]
+    assert net.launches == len(plan) + len(loose)
+    assert sorted(net.bufs) == sorted([p["nodes"][-1] for p in plan] + loose)
+    assert net.saved_bytes == sum(p["saved"] for p in plan)
+    plain = Network(g, params, fuse=False, device="cpu")
+    assert plain.launches == sum(1 for nd in g if nd["op"] != "input") and plain.plan == []
+    # what the runner refuses
+    bad = [dict(nd) for nd in g]
+    bad[2] = dict(bad[2], training=True)
+    with pytest.raises(NotImplementedError):
+        Network(bad, params, device="cpu")
+    bad = [dict(nd) for nd in g]
+    bad[1] = dict(bad[1], dtype="f32")
+    with pytest.raises(NotImplementedError):
+        Network(bad, params, device="cpu")
