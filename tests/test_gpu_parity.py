@@ -726,6 +726,8 @@ def test_unfused_eltwise_passes(dt):
 # Networks under the host fusion pass
 # ---------------------------------------------------------------------------
 NETWORKS = [
+    # the benchmarked stage's widths and resolution (56x56x256 -> 28x28x512), 4 of its 32 images
+    ("stage", dict(n=4, h=56, w=56, cin=256, cmid=128, cout=512, stride=2, blocks=2)),
     ("stage", dict(n=2, h=14, w=14, cin=64, cmid=32, cout=128, stride=2, blocks=2)),
     ("stage", dict(n=3, h=9, w=11, cin=24, cmid=16, cout=40, stride=2, blocks=3)),
     ("stem", dict(n=2, h=32, w=32)),
@@ -739,7 +741,13 @@ def test_network_under_the_fusion_plan(i, fuse):
     """The library's plan (identical to the oracle's) executed through the C ABI: every
     tensor the plan keeps in memory against the oracle network evaluated with the same
     storage roundings (fused chains: folded bf16 weights, one rounding; other ops: a
-    rounding each)."""
+    rounding each).
+
+    A stored tensor that d roundings separate from the inputs (a fused chain counts once,
+    every unfused op once) is held to 1e-2 * max(2, d): each layer adds at most about two
+    bf16 units of the last place of its own (summation order, fp32 vs binary64), and a
+    difference in its input passes through a BN-normalised layer without growing, so the
+    differences add along the longest path.  d <= 2 is the single-layer bf16 bar."""
     from oracle import fusion as ofusion, network as onet
     from workloads import graphs
     from dl_fusion_amd.network import Network
@@ -756,9 +764,22 @@ def test_network_under_the_fusion_plan(i, fuse):
     torch.cuda.synchronize()
     ref = onet.forward(g, params, bits, plan)
     assert sorted(net.bufs) == sorted(k for k in ref if g[k]["op"] != "input")
+    # roundings between the inputs and each stored tensor, along the longest path
+    chain_of = {j: p["nodes"] for p in plan for j in p["nodes"]}
+    depth = {}
+    for j, nd in enumerate(g):
+        if nd["op"] == "input":
+            depth[j] = 0
+        elif j in chain_of:
+            nodes = chain_of[j]
+            if nodes[-1] == j:
+                srcs = {s for k in nodes for s in g[k]["inputs"] if s not in nodes}
+                depth[j] = 1 + max(depth[s] for s in srcs)
+        else:
+            depth[j] = 1 + max(depth[s] for s in nd["inputs"])
     for j, t in net.bufs.items():
         err = oracle.rel_error(oracle.widen(host(t, "bf16"), "bf16"), ref[j])
-        assert err <= TOL["bf16"], (j, g[j]["op"], err)
+        assert err <= 1e-2 * max(2, depth[j]), (j, g[j]["op"], depth[j], err)
     if fuse:
         assert net.launches == len(plan) + sum(
             1 for j, nd in enumerate(g) if nd["op"] != "input" and all(j not in p["nodes"] for p in plan))
