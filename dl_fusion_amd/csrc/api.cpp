@@ -74,6 +74,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // dense GEMM, the eight-wave 256 x 256 variant with one barrier per two K slices
 // runs instead: measured 7-10% faster on the 4096 x 11008 x 4096 bf16 and
 // 8192 x 4096 x 4096 fp8 GEMMs.
+// Memory-bound GEMMs (many rows, short K, narrow N) take the streaming kernel unless a tile
+// is forced (DLF_TILE) or DLF_GEMM=tiled asks for the tiled kernel; DLF_GEMM=stream takes it
+// wherever it applies (tests of both routes).
+bool stream_gemm(const dlf::MmaArgs& a) {
+    if (std::getenv("DLF_TILE")) return false;
+    const char* g = std::getenv("DLF_GEMM");
+    if (g && std::strcmp(g, "tiled") == 0) return false;
+    if (g && std::strcmp(g, "stream") == 0) return dlf::gemm_stream_ok(a);
+    return dlf::gemm_stream_pays(a);
+}
+
 int pick_tile(int64_t M, int64_t N, bool dense) {
     if (const char* env = std::getenv("DLF_TILE")) {
         const int t = std::atoi(env);
@@ -244,8 +255,10 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     // a 1x1, stride-1, unpadded conv is the GEMM of the [n*h*w][c_in] pixel matrix: the dense
     // kernel reads it with buffer loads and no gather arithmetic
     if (!generic && d->kh == 1 && d->kw == 1 && d->stride_h == 1 && d->stride_w == 1 && d->pad_h == 0 &&
-        d->pad_w == 0 && d->c_in % 8 == 0)
+        d->pad_w == 0 && d->c_in % 8 == 0) {
+        if (stream_gemm(a)) return hip_status(dlf::launch_gemm_stream(a, act_code(d->act), s), what);
         return hip_status(dlf::launch_mma_bf16(a, false, act_code(d->act), pick_tile(g.M, d->c_out, true), s), what);
+    }
     a.H = static_cast<int>(d->h); a.W = static_cast<int>(d->w); a.Cin = static_cast<int>(d->c_in);
     a.Ho = static_cast<int>(g.ho); a.Wo = static_cast<int>(g.wo); a.KW = static_cast<int>(d->kw);
     a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
@@ -438,6 +451,7 @@ dlf_status gemm_fused_impl(const dlf_gemm_desc* d, const void* a, const void* b,
     x.out_inv_scale = d->out_inv_scale;
     x.dequant = 1.0f;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (bf16_path && stream_gemm(x)) return hip_status(dlf::launch_gemm_stream(x, act_code(d->act), s), what);
     const int tile = pick_tile(d->m, d->n, true);
     if (bf16_path) return hip_status(dlf::launch_mma_bf16(x, false, act_code(d->act), tile, s), what);
     const int out = d->out_dtype == DLF_FP8_E4M3 ? dlf::kOutFp8 : dlf::kOutBf16;

@@ -1,0 +1,258 @@
+// Streaming GEMM for memory-bound shapes: C = act(A B^T + bias [+ residual]) with a short
+// reduction (K of 128 to 512) and a narrow output (N of 128 to 512), as in the 1x1
+// convolutions of a ResNet bottleneck (the GEMM of the [n h w][c_in] pixel matrix).  The
+// work is reading A (and the residual) once and writing C once; the tiled kernel reaches
+// half the HBM bandwidth there, because each workgroup has only its own few K slices in
+// flight and its tiles do not overlap their loads with the previous tile's epilogue.
+//
+// Here a workgroup of four waves is persistent over tiles of 32 rows of A, dealt to the
+// workgroups in turn.  B is loaded once into registers (wave w holds the MFMA fragments of
+// its N/4 columns for all of K).  The tiles stream through an LDS ring of R slots, each
+// holding one tile's A rows and, with a residual, its residual rows, by LDS-DMA buffer
+// loads that every wave shares; R tiles are in flight at a time.  Per tile a wave runs
+// K/16 x N/128 MFMAs out of LDS and then its epilogue, whose stores go out after the next
+// tile's loads.  Loads past the last tile or row read zeros and stores past them are
+// dropped (out-of-range buffer offsets), so every wave issues the same loads and stores
+// each iteration and the memory-counter waits are constants.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "mma_common.h"
+
+namespace dlf {
+namespace {
+
+constexpr int kSRows = 32;             // rows of A per tile
+constexpr int kSLds = 128 * 1024;      // the ring
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// f(integral_constant<int, I>) ... f(integral_constant<int, N-1>), unrolled at compile time
+template <int I, int N, class Fn>
+__device__ __forceinline__ void unrolled(Fn&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        unrolled<I + 1, N>(f);
+    }
+}
+
+// CPW: 32-column output blocks per wave (N = 128 CPW); KS: 16-wide K steps (K = 16 KS)
+template <int CPW, int KS, int ACT, bool RES>
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, const int tiles) {
+    constexpr int N = 128 * CPW, K = 16 * KS;
+    constexpr int ABYTES = kSRows * K * 2, RBYTES = RES ? kSRows * N * 2 : 0;
+    constexpr int SLOT = ABYTES + RBYTES;
+    constexpr int LPW = SLOT / 4096;                           // 1 KB loads per wave per tile
+    constexpr int ALOADS = ABYTES / 1024;                      // the A part: loads 0 .. ALOADS-1
+    constexpr int ST = 4 * CPW;                                // stores per wave per tile
+    constexpr int CA = K / 8, CR = N / 8;                      // 16-byte chunks per row
+    // tiles in flight: what the ring holds, at most 8, and few enough that the loads of R-1
+    // tiles and the stores of R tiles fit the 6-bit memory counter (stores count in it too)
+    constexpr int R0 = kSLds / SLOT > 8 ? 8 : kSLds / SLOT;
+    constexpr int R1 = (63 + LPW) / (LPW + ST);
+    constexpr int R = R0 < R1 ? R0 : R1;
+    static_assert(SLOT % 4096 == 0 && R >= 2, "whole kilobyte loads, two tiles in flight");
+    static_assert(LPW * (R - 1) + ST * R < 64, "vmcnt range");
+    static_assert(CA >= 16 && CR >= 16, "the chunk swizzle spans 16 chunks");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[R * SLOT];
+
+    const int tid = static_cast<int>(threadIdx.x);
+    // the wave index in a scalar register: the LDS-DMA destination (M0) must be uniform
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), half = lane >> 5, row = lane & 31;
+    const int G = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
+    const int64_t M = p.M;
+    const __amdgpu_buffer_rsrc_t ar =
+        buffer_rsrc(p.a, static_cast<uint32_t>(M * K * 2));
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(RES ? static_cast<const void*>(p.res) : p.a,
+                                                  static_cast<uint32_t>(RES ? M * N * 2 : 0));
+    const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(p.c, static_cast<uint32_t>(M * N * 2));
+
+    // B fragments of this wave's columns 32 (CPW wave + j) + lane % 32, chunk 2 s + half
+    bf16x8_t bf[CPW][KS];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const uint16_t* const brow = static_cast<const uint16_t*>(p.b) +
+                                     static_cast<int64_t>(32 * (CPW * wave + j) + row) * K + 8 * half;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) bf[j][s] = *reinterpret_cast<const bf16x8_t*>(brow + 16 * s);
+    }
+
+    // load j of this wave fills slot bytes [(wave LPW + j) KB, +1 KB): lane's 16-byte chunk
+    // q = 64 (wave LPW + j) + lane sits at row q / CA, physical chunk q % CA, which holds
+    // logical chunk (q % CA) ^ (row % 16) (same for the residual part with CR chunks a row).
+    // Offsets are tile-independent up to the tile's first row.
+    uint32_t rel[LPW];
+    int lrow[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int lj = wave * LPW + j;
+        if (lj < ALOADS) {
+            const int q = 64 * lj + lane, r = q / CA, pc = q % CA;
+            lrow[j] = r;
+            rel[j] = static_cast<uint32_t>((r * K + 8 * (pc ^ (r & 15))) * 2);
+        } else {
+            const int q = 64 * (lj - ALOADS) + lane, r = q / CR, pc = q % CR;
+            lrow[j] = r;
+            rel[j] = static_cast<uint32_t>((r * N + 8 * (pc ^ (r & 15))) * 2);
+        }
+    }
+    auto issue = [&](int i) {   // the loads of this workgroup's tile i into slot i % R
+        const int t = wg + G * i;
+        uint8_t* const slot = ring + (i % R) * SLOT;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int lj = wave * LPW + j;
+            const int64_t m = static_cast<int64_t>(t) * kSRows + lrow[j];
+            const bool ok = t < tiles && m < M;
+            if (lj < ALOADS) {
+                const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * K * 2) + rel[j];
+                load_lds16_buf(ar, ok ? off : kOutOfRange, slot + lj * 1024);
+            } else {
+                const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * N * 2) + rel[j];
+                load_lds16_buf(rr, ok ? off : kOutOfRange, slot + lj * 1024);
+            }
+        }
+    };
+
+    // bias of this lane's output columns 32 (CPW wave + j) + 8 g + 4 half .. +3
+    f32x4_t bias[CPW][4];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bias[j][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.shift) bias[j][g] = *reinterpret_cast<const f32x4_t*>(p.shift + 32 * (CPW * wave + j) + 8 * g + 4 * half);
+        }
+
+    const int iters = wg < tiles ? (tiles - wg + G - 1) / G : 0;
+    wait_vmcnt<0>();   // B and the bias are in registers before the ring's loads go out
+#pragma unroll
+    for (int i = 0; i < R; ++i) issue(i);
+    for (int i = 0; i < iters; ++i) {
+        // tile i has landed for this wave once at most the memory operations issued after its
+        // loads are outstanding: the loads of tiles i+1 .. i+R-1 and the stores of tiles
+        // max(0, i-R) .. i-1 (the stores of tile k go out right after the loads of tile k+R)
+        if (i >= R) {
+            wait_vmcnt<LPW * (R - 1) + ST * R>();
+        } else {
+            unrolled<0, R>([&](auto c) {
+                if (i == decltype(c)::value) wait_vmcnt<LPW * (R - 1) + ST * decltype(c)::value>();
+            });
+        }
+        barrier();
+        const uint8_t* const slot = ring + (i % R) * SLOT;
+        f32x16_t acc[CPW];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8_t av =
+                *reinterpret_cast<const bf16x8_t*>(slot + row * K * 2 + 16 * ((2 * s + half) ^ (row & 15)));
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j][s], av, acc[j], 0, 0, 0);
+        }
+        // the residual of this lane's outputs, out of the slot before it is refilled
+        uint2 rv[CPW][4];
+        if constexpr (RES) {
+#pragma unroll
+            for (int j = 0; j < CPW; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = 32 * (CPW * wave + j) + 8 * g + 4 * half;   // 4 columns: half a chunk
+                    rv[j][g] = *reinterpret_cast<const uint2*>(slot + ABYTES + row * N * 2 +
+                                                              16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7));
+                }
+        }
+        wait_vm_lgkm<63, 0>();   // this wave's reads of the slot are done
+        barrier();               // and every wave's: the slot takes tile i + R
+        issue(i + R);
+        // epilogue: row 32 t + lane % 32, columns as the bias
+        const int64_t m = static_cast<int64_t>(wg + G * i) * kSRows + row;
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = 32 * (CPW * wave + j) + 8 * g + 4 * half;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[j][4 * g + e] + bias[j][g][e];
+                if constexpr (RES) {
+                    v[0] += __uint_as_float(rv[j][g].x << 16);
+                    v[1] += __uint_as_float(rv[j][g].x & 0xFFFF0000u);
+                    v[2] += __uint_as_float(rv[j][g].y << 16);
+                    v[3] += __uint_as_float(rv[j][g].y & 0xFFFF0000u);
+                }
+                if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                }
+                uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                if constexpr (ACT == kActRelu) {
+                    lo = relu_bf16x2(lo);
+                    hi = relu_bf16x2(hi);
+                }
+                const uint32_t off = m < M ? static_cast<uint32_t>((m * N + col) * 2) : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, cr, off, 0, 0);
+            }
+    }
+    wait_vmcnt<0>();   // the dummy loads of the ring's last slots land before the workgroup ends
+}
+
+template <int CPW, int KS, int ACT>
+hipError_t launch3(const MmaArgs& a, int tiles, dim3 grid, hipStream_t s) {
+    if (a.res)
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, ACT, true>), grid, dim3(256), 0, s, a, tiles);
+    else
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, ACT, false>), grid, dim3(256), 0, s, a, tiles);
+    return hipGetLastError();
+}
+
+template <int CPW, int KS>
+hipError_t launch2(const MmaArgs& a, int act, int tiles, dim3 grid, hipStream_t s) {
+    switch (act) {
+        case kActNone: return launch3<CPW, KS, kActNone>(a, tiles, grid, s);
+        case kActRelu: return launch3<CPW, KS, kActRelu>(a, tiles, grid, s);
+        case kActGelu: return launch3<CPW, KS, kActGelu>(a, tiles, grid, s);
+        case kActGeluErf: return launch3<CPW, KS, kActGeluErf>(a, tiles, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool gemm_stream_ok(const MmaArgs& a) {
+    if (a.scale || a.parts > 1 || a.M <= 0) return false;
+    if (a.N % 128 != 0 || a.N < 128 || a.N > 512) return false;
+    if (a.K != 128 && a.K != 256 && a.K != 512) return false;
+    if (static_cast<int64_t>(a.N) * a.K > 65536) return false;    // B fragments: at most 128 registers a lane
+    const int64_t lim = int64_t(1) << 31;
+    return a.M * a.K * 2 < lim && a.M * a.N * 2 < lim;
+}
+
+bool gemm_stream_pays(const MmaArgs& a) {
+    // measured on MI355X against the tiled kernel: 1.12-1.38x faster from 32768 rows with
+    // K <= 256 and N <= 384; level below that; 0.86-0.95x with K = 512, N = 512 or N K = 65536
+    return gemm_stream_ok(a) && a.M >= 32768 && a.K <= 256 && a.N <= 384;
+}
+
+hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
+    const int64_t tiles64 = (a.M + kSRows - 1) / kSRows;
+    const int tiles = static_cast<int>(tiles64);
+    const dim3 grid(static_cast<unsigned>(tiles < 256 ? tiles : 256));
+    const int cpw = a.N / 128, ks = a.K / 16;
+    switch (cpw * 100 + ks) {
+        case 108: return launch2<1, 8>(a, act, tiles, grid, s);
+        case 116: return launch2<1, 16>(a, act, tiles, grid, s);
+        case 132: return launch2<1, 32>(a, act, tiles, grid, s);
+        case 208: return launch2<2, 8>(a, act, tiles, grid, s);
+        case 216: return launch2<2, 16>(a, act, tiles, grid, s);
+        case 308: return launch2<3, 8>(a, act, tiles, grid, s);
+        case 408: return launch2<4, 8>(a, act, tiles, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dlf

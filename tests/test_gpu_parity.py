@@ -359,6 +359,51 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
         assert oracle.rel_error(oracle.widen(host(yu, "bf16"), "bf16"), ref) <= TOL_UNFUSED["bf16"]
 
 
+# Memory-bound shapes take the streaming kernel (B in registers, A and the residual through
+# an LDS ring of whole tiles): every (N, K) it is built for, ragged row counts (one row, a
+# partial last tile, fewer tiles than workgroups, many tiles per workgroup), every
+# activation, with and without residual and bias; forced onto it (DLF_GEMM=stream), onto the
+# tiled kernel, and on the library's own choice, each against the oracle.
+STREAM_GEMM = [
+    dict(m=100, n=128, k=256, act="relu", bias=True),
+    dict(m=1, n=128, k=128, act="gelu_tanh", bias=True),
+    dict(m=9000, n=128, k=512, act="none", bias=False),
+    dict(m=777, n=256, k=128, act="gelu_erf", bias=True),
+    dict(m=33, n=256, k=256, act="relu", bias=True),
+    dict(m=12345, n=384, k=128, act="gelu_tanh", bias=True),
+    dict(m=4100, n=512, k=128, act="relu", bias=True),
+    dict(m=40000, n=128, k=256, act="relu", bias=True),        # the library's own choice takes it
+]
+
+
+@pytest.mark.parametrize("res", [False, True])
+@pytest.mark.parametrize("i", range(len(STREAM_GEMM)))
+def test_bf16_gemm_streaming_route(i, res):
+    wl = workloads.workload(3, **STREAM_GEMM[i])
+    inp = workloads.generate(wl)
+    r = None
+    if res:
+        r = workloads.bf16_bits(np.random.default_rng(90 + i).standard_normal((wl.m, wl.n)).astype(np.float32))
+    ref = gemm_reference(inp, np.arange(wl.m), r)
+    L = layers().make_layer(inp, with_unfused=False)
+    r_d = layers().to_device(r, "bf16") if r is not None else None
+    try:
+        for route in ("stream", "tiled", None):
+            if route is None:
+                os.environ.pop("DLF_GEMM", None)
+            else:
+                os.environ["DLF_GEMM"] = route
+            case(f"gemm_fused {wl} route={route} residual={res}")
+            buf, y = guarded((wl.m, wl.n), torch.bfloat16)
+            L.forward(y=y, residual=r_d)
+            torch.cuda.synchronize()
+            assert guard_intact(buf, y.numel())
+            err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+            assert err <= TOL["bf16"], (wl, route, err)
+    finally:
+        os.environ.pop("DLF_GEMM", None)
+
+
 # Rows of 8 MB or more are past the 32-bit offsets of the buffer-resource loads: the library
 # reads them with 64-bit global addresses and the basic tiles (a tuned tile falls back to
 # 256 x 256).  One K just past that limit per input type, on the default, a tuned and a small
