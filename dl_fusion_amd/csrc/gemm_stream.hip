@@ -225,17 +225,17 @@ hipError_t launch2(const MmaArgs& a, int act, int tiles, dim3 grid, hipStream_t 
 
 bool gemm_stream_ok(const MmaArgs& a) {
     if (a.scale || a.parts > 1 || a.M <= 0) return false;
-    if (a.N % 128 != 0 || a.N < 128 || a.N > 512) return false;
-    if (a.K != 128 && a.K != 256 && a.K != 512) return false;
+    if (a.N % 128 != 0 || a.N < 128 || a.N > 384) return false;
+    if (a.K != 128 && a.K != 256) return false;
     if (static_cast<int64_t>(a.N) * a.K > 65536) return false;    // B fragments: at most 128 registers a lane
     const int64_t lim = int64_t(1) << 31;
     return a.M * a.K * 2 < lim && a.M * a.N * 2 < lim;
 }
 
 bool gemm_stream_pays(const MmaArgs& a) {
-    // measured on MI355X against the tiled kernel: 1.12-1.38x faster from 32768 rows with
-    // K <= 256 and N <= 384; level below that; 0.86-0.95x with K = 512, N = 512 or N K = 65536
-    return gemm_stream_ok(a) && a.M >= 32768 && a.K <= 256 && a.N <= 384;
+    // measured on MI355X against the tiled kernel: 1.12-1.40x faster from 32768 rows (level
+    // with N = K = 256); level below that.  K = 512 and N = 512 were slower and are not built.
+    return gemm_stream_ok(a) && a.M >= 32768;
 }
 
 hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
@@ -246,11 +246,9 @@ hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
     switch (cpw * 100 + ks) {
         case 108: return launch2<1, 8>(a, act, tiles, grid, s);
         case 116: return launch2<1, 16>(a, act, tiles, grid, s);
-        case 132: return launch2<1, 32>(a, act, tiles, grid, s);
         case 208: return launch2<2, 8>(a, act, tiles, grid, s);
         case 216: return launch2<2, 16>(a, act, tiles, grid, s);
         case 308: return launch2<3, 8>(a, act, tiles, grid, s);
-        case 408: return launch2<4, 8>(a, act, tiles, grid, s);
         default: return hipErrorInvalidValue;
     }
 }

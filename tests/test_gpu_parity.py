@@ -367,11 +367,11 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
 STREAM_GEMM = [
     dict(m=100, n=128, k=256, act="relu", bias=True),
     dict(m=1, n=128, k=128, act="gelu_tanh", bias=True),
-    dict(m=9000, n=128, k=512, act="none", bias=False),
+    dict(m=9000, n=128, k=256, act="none", bias=False),
     dict(m=777, n=256, k=128, act="gelu_erf", bias=True),
     dict(m=33, n=256, k=256, act="relu", bias=True),
     dict(m=12345, n=384, k=128, act="gelu_tanh", bias=True),
-    dict(m=4100, n=512, k=128, act="relu", bias=True),
+    dict(m=4100, n=384, k=128, act="relu", bias=True),
     dict(m=40000, n=128, k=256, act="relu", bias=True),        # the library's own choice takes it
 ]
 
