@@ -45,7 +45,11 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
     constexpr int SLOT = ABYTES + RBYTES;
     constexpr int LPW = SLOT / 4096;                           // 1 KB loads per wave per tile
     constexpr int ALOADS = ABYTES / 1024;                      // the A part: loads 0 .. ALOADS-1
-    constexpr int ST = 4 * CPW;                                // stores per wave per tile
+    // output rows of 256 bytes or more go out staged, as whole rows of 16-byte stores (2 CPW
+    // of 1 KB per wave); with N = 128 each lane's 8-byte pieces go out directly (4 CPW a
+    // wave): measured faster each way
+    constexpr bool STAGED = CPW >= 2;
+    constexpr int ST = STAGED ? 2 * CPW : 4 * CPW;             // stores per wave per tile
     constexpr int CA = K / 8, CR = N / 8;                      // 16-byte chunks per row
     // tiles in flight: what the ring holds, at most 8, and few enough that the loads of R-1
     // tiles and the stores of R tiles fit the 6-bit memory counter (stores count in it too)
@@ -56,6 +60,9 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
     static_assert(LPW * (R - 1) + ST * R < 64, "vmcnt range");
     static_assert(CA >= 16 && CR >= 16, "the chunk swizzle spans 16 chunks");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[R * SLOT];
+    // the finished tile, rows of N values (chunks swizzled like the ring's), written out as
+    // whole rows with 16-byte stores
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[STAGED ? kSRows * N * 2 : 16];
 
     const int tid = static_cast<int>(threadIdx.x);
     // the wave index in a scalar register: the LDS-DMA destination (M0) must be uniform
@@ -166,16 +173,12 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
                                                               16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7));
                 }
         }
-        wait_vm_lgkm<63, 0>();   // this wave's reads of the slot are done
-        barrier();               // and every wave's: the slot takes tile i + R
-        issue(i + R);
-        // epilogue: row 32 t + lane % 32, columns as the bias
-        const int64_t m = static_cast<int64_t>(wg + G * i) * kSRows + row;
+        // epilogue: row lane % 32 of the tile, columns as the bias, bf16
+        u32x2_t outv[CPW][4];
 #pragma unroll
         for (int j = 0; j < CPW; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = 32 * (CPW * wave + j) + 8 * g + 4 * half;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[j][4 * g + e] + bias[j][g][e];
@@ -194,9 +197,38 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
                     lo = relu_bf16x2(lo);
                     hi = relu_bf16x2(hi);
                 }
-                const uint32_t off = m < M ? static_cast<uint32_t>((m * N + col) * 2) : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, cr, off, 0, 0);
+                outv[j][g] = u32x2_t{lo, hi};
+                if constexpr (STAGED) {
+                    const int col = 32 * (CPW * wave + j) + 8 * g + 4 * half;
+                    *reinterpret_cast<u32x2_t*>(stage + row * N * 2 + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7)) =
+                        outv[j][g];
+                }
             }
+        wait_vm_lgkm<63, 0>();   // this wave's slot reads (and staging writes) are done
+        barrier();               // and every wave's: the slot takes tile i + R (the tile is staged)
+        issue(i + R);
+        const int64_t t0 = static_cast<int64_t>(wg + G * i) * kSRows;
+        if constexpr (STAGED) {
+            // wave w writes rows 8 w .. 8 w + 7 of the tile, 1 KB (1024 / (2 N) rows) a store
+#pragma unroll
+            for (int u = 0; u < ST; ++u) {
+                const int q = 64 * u + lane, r = 8 * wave + q / CR, c = q % CR;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * N * 2 + 16 * (c ^ (r & 15)));
+                const int64_t m = t0 + r;
+                const uint32_t off = m < M ? static_cast<uint32_t>((m * N + 8 * c) * 2) : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b128(v, cr, off, 0, 0);
+            }
+        } else {
+            const int64_t m = t0 + row;
+#pragma unroll
+            for (int j = 0; j < CPW; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = 32 * (CPW * wave + j) + 8 * g + 4 * half;
+                    const uint32_t off = m < M ? static_cast<uint32_t>((m * N + col) * 2) : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b64(outv[j][g], cr, off, 0, 0);
+                }
+        }
     }
     wait_vmcnt<0>();   // the dummy loads of the ring's last slots land before the workgroup ends
 }
@@ -233,9 +265,9 @@ bool gemm_stream_ok(const MmaArgs& a) {
 }
 
 bool gemm_stream_pays(const MmaArgs& a) {
-    // measured on MI355X against the tiled kernel: 1.12-1.40x faster from 32768 rows (level
-    // with N = K = 256); level below that.  K = 512 and N = 512 were slower and are not built.
-    return gemm_stream_ok(a) && a.M >= 32768;
+    // measured on MI355X against the tiled kernel: 1.1-1.4x faster from 32768 rows, level
+    // below that, 0.96x with N = K = 256.  K = 512 and N = 512 were slower and are not built.
+    return gemm_stream_ok(a) && a.M >= 32768 && static_cast<int64_t>(a.N) * a.K < 65536;
 }
 
 hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
