@@ -24,7 +24,6 @@ namespace dlf {
 namespace {
 
 constexpr int kSRows = 32;             // rows of A per tile
-constexpr int kSLds = 128 * 1024;      // the ring
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -37,10 +36,12 @@ __device__ __forceinline__ void unrolled(Fn&& f) {
     }
 }
 
-// CPW: 32-column output blocks per wave (N = 128 CPW); KS: 16-wide K steps (K = 16 KS)
-template <int CPW, int KS, int ACT, bool RES>
-__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, const int tiles) {
+// CPW: 32-column output blocks per wave (N = 128 CPW); KS: 16-wide K steps (K = 16 KS);
+// OCC: workgroups a CU (the ring takes 128 KB of LDS over OCC)
+template <int CPW, int KS, int OCC, int ACT, bool RES>
+__global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, const int tiles) {
     constexpr int N = 128 * CPW, K = 16 * KS;
+    constexpr int kSLds = 128 * 1024 / OCC;
     constexpr int ABYTES = kSRows * K * 2, RBYTES = RES ? kSRows * N * 2 : 0;
     constexpr int SLOT = ABYTES + RBYTES;
     constexpr int LPW = SLOT / 4096;                           // 1 KB loads per wave per tile
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
     static_assert(SLOT % 4096 == 0 && R >= 2, "whole kilobyte loads, two tiles in flight");
     static_assert(LPW * (R - 1) + ST * R < 64, "vmcnt range");
     static_assert(CA >= 16 && CR >= 16, "the chunk swizzle spans 16 chunks");
+    static_assert(OCC * (R * SLOT + (STAGED ? kSRows * N * 2 : 0)) <= 160 * 1024, "LDS per CU");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[R * SLOT];
     // the finished tile, rows of N values (chunks swizzled like the ring's), written out as
     // whole rows with 16-byte stores
@@ -74,16 +76,6 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
     const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(RES ? static_cast<const void*>(p.res) : p.a,
                                                   static_cast<uint32_t>(RES ? M * N * 2 : 0));
     const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(p.c, static_cast<uint32_t>(M * N * 2));
-
-    // B fragments of this wave's columns 32 (CPW wave + j) + lane % 32, chunk 2 s + half
-    bf16x8_t bf[CPW][KS];
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-        const uint16_t* const brow = static_cast<const uint16_t*>(p.b) +
-                                     static_cast<int64_t>(32 * (CPW * wave + j) + row) * K + 8 * half;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) bf[j][s] = *reinterpret_cast<const bf16x8_t*>(brow + 16 * s);
-    }
 
     // load j of this wave fills slot bytes [(wave LPW + j) KB, +1 KB): lane's 16-byte chunk
     // q = 64 (wave LPW + j) + lane sits at row q / CA, physical chunk q % CA, which holds
@@ -122,6 +114,20 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
         }
     };
 
+    const int iters = wg < tiles ? (tiles - wg + G - 1) / G : 0;
+    // the first tile's loads go out ahead of B and the bias, the other R-1 tiles' behind them:
+    // B's latency overlaps the first tile's, and the wait for tile 0 below covers B too
+    issue(0);
+    // B fragments of this wave's columns 32 (CPW wave + j) + lane % 32, chunk 2 s + half
+    bf16x8_t bf[CPW][KS];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const uint16_t* const brow = static_cast<const uint16_t*>(p.b) +
+                                     static_cast<int64_t>(32 * (CPW * wave + j) + row) * K + 8 * half;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) bf[j][s] = *reinterpret_cast<const bf16x8_t*>(brow + 16 * s);
+    }
+
     // bias of this lane's output columns 32 (CPW wave + j) + 8 g + 4 half .. +3
     f32x4_t bias[CPW][4];
 #pragma unroll
@@ -132,10 +138,8 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
             if (p.shift) bias[j][g] = *reinterpret_cast<const f32x4_t*>(p.shift + 32 * (CPW * wave + j) + 8 * g + 4 * half);
         }
 
-    const int iters = wg < tiles ? (tiles - wg + G - 1) / G : 0;
-    wait_vmcnt<0>();   // B and the bias are in registers before the ring's loads go out
 #pragma unroll
-    for (int i = 0; i < R; ++i) issue(i);
+    for (int i = 1; i < R; ++i) issue(i);
     for (int i = 0; i < iters; ++i) {
         // tile i has landed for this wave once at most the memory operations issued after its
         // loads are outstanding: the loads of tiles i+1 .. i+R-1 and the stores of tiles
@@ -233,22 +237,23 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(const MmaArgs p, co
     wait_vmcnt<0>();   // the dummy loads of the ring's last slots land before the workgroup ends
 }
 
-template <int CPW, int KS, int ACT>
-hipError_t launch3(const MmaArgs& a, int tiles, dim3 grid, hipStream_t s) {
+template <int CPW, int KS, int OCC, int ACT>
+hipError_t launch3(const MmaArgs& a, int tiles, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(tiles < 256 * OCC ? tiles : 256 * OCC));
     if (a.res)
-        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, ACT, true>), grid, dim3(256), 0, s, a, tiles);
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, true>), grid, dim3(256), 0, s, a, tiles);
     else
-        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, ACT, false>), grid, dim3(256), 0, s, a, tiles);
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, false>), grid, dim3(256), 0, s, a, tiles);
     return hipGetLastError();
 }
 
-template <int CPW, int KS>
-hipError_t launch2(const MmaArgs& a, int act, int tiles, dim3 grid, hipStream_t s) {
+template <int CPW, int KS, int OCC>
+hipError_t launch2(const MmaArgs& a, int act, int tiles, hipStream_t s) {
     switch (act) {
-        case kActNone: return launch3<CPW, KS, kActNone>(a, tiles, grid, s);
-        case kActRelu: return launch3<CPW, KS, kActRelu>(a, tiles, grid, s);
-        case kActGelu: return launch3<CPW, KS, kActGelu>(a, tiles, grid, s);
-        case kActGeluErf: return launch3<CPW, KS, kActGeluErf>(a, tiles, grid, s);
+        case kActNone: return launch3<CPW, KS, OCC, kActNone>(a, tiles, s);
+        case kActRelu: return launch3<CPW, KS, OCC, kActRelu>(a, tiles, s);
+        case kActGelu: return launch3<CPW, KS, OCC, kActGelu>(a, tiles, s);
+        case kActGeluErf: return launch3<CPW, KS, OCC, kActGeluErf>(a, tiles, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -273,14 +278,20 @@ bool gemm_stream_pays(const MmaArgs& a) {
 hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
     const int64_t tiles64 = (a.M + kSRows - 1) / kSRows;
     const int tiles = static_cast<int>(tiles64);
-    const dim3 grid(static_cast<unsigned>(tiles < 256 ? tiles : 256));
     const int cpw = a.N / 128, ks = a.K / 16;
-    switch (cpw * 100 + ks) {
-        case 108: return launch2<1, 8>(a, act, tiles, grid, s);
-        case 116: return launch2<1, 16>(a, act, tiles, grid, s);
-        case 208: return launch2<2, 8>(a, act, tiles, grid, s);
-        case 216: return launch2<2, 16>(a, act, tiles, grid, s);
-        case 308: return launch2<3, 8>(a, act, tiles, grid, s);
+    // two workgroups a CU (half the ring each) where N K = 32768, from 2048 tiles: measured
+    // 1.05-1.2x faster there, 0.95x at 1250 tiles.  With N = K = 128 two were level to 4%
+    // slower; N = 384 has no room for two (its staging area), and N = K = 256 needs more
+    // than 256 registers for its B fragments and accumulators.
+    const bool two = cpw * ks == 16 && tiles >= 2048;
+    switch (cpw * 1000 + ks * 10 + (two ? 2 : 1)) {
+        case 1081: return launch2<1, 8, 1>(a, act, tiles, s);
+        case 1161: return launch2<1, 16, 1>(a, act, tiles, s);
+        case 1162: return launch2<1, 16, 2>(a, act, tiles, s);
+        case 2081: return launch2<2, 8, 1>(a, act, tiles, s);
+        case 2082: return launch2<2, 8, 2>(a, act, tiles, s);
+        case 2161: return launch2<2, 16, 1>(a, act, tiles, s);
+        case 3081: return launch2<3, 8, 1>(a, act, tiles, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -360,10 +360,11 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
 
 
 # Memory-bound shapes take the streaming kernel (B in registers, A and the residual through
-# an LDS ring of whole tiles): every (N, K) it is built for, ragged row counts (one row, a
-# partial last tile, fewer tiles than workgroups, many tiles per workgroup), every
-# activation, with and without residual and bias; forced onto it (DLF_GEMM=stream), onto the
-# tiled kernel, and on the library's own choice, each against the oracle.
+# an LDS ring of whole tiles): every (N, K) it is built for, at one and two workgroups a CU,
+# ragged row counts (one row, a partial last tile, fewer tiles than workgroups, many tiles
+# per workgroup), every activation, with and without residual and bias; forced onto it
+# (DLF_GEMM=stream), onto the tiled kernel, and on the library's own choice, each against the
+# oracle.
 STREAM_GEMM = [
     dict(m=100, n=128, k=256, act="relu", bias=True),
     dict(m=1, n=128, k=128, act="gelu_tanh", bias=True),
@@ -373,6 +374,9 @@ STREAM_GEMM = [
     dict(m=12345, n=384, k=128, act="gelu_tanh", bias=True),
     dict(m=4100, n=384, k=128, act="relu", bias=True),
     dict(m=40000, n=128, k=256, act="relu", bias=True),        # the library's own choice takes it
+    # N K = 32768 from 2048 tiles: two workgroups a CU (half the ring each)
+    dict(m=70001, n=128, k=256, act="gelu_erf", bias=True),
+    dict(m=66000, n=256, k=128, act="relu", bias=False),
 ]
 
 
