@@ -1,19 +1,21 @@
 // Streaming GEMM for memory-bound shapes: C = act(A B^T + bias [+ residual]) with a short
-// reduction (K of 128 to 512) and a narrow output (N of 128 to 512), as in the 1x1
-// convolutions of a ResNet bottleneck (the GEMM of the [n h w][c_in] pixel matrix).  The
-// work is reading A (and the residual) once and writing C once; the tiled kernel reaches
-// half the HBM bandwidth there, because each workgroup has only its own few K slices in
-// flight and its tiles do not overlap their loads with the previous tile's epilogue.
+// reduction (K of 128 or 256), as in the 1x1 convolutions of a ResNet bottleneck (the GEMM of
+// the [n h w][c_in] pixel matrix).  The work is reading A (and the residual) once and
+// writing C once; the tiled kernel reaches half the HBM bandwidth there, because each
+// workgroup has only its own few K slices in flight and its tiles do not overlap their loads
+// with the previous tile's epilogue.
 //
-// Here a workgroup of four waves is persistent over tiles of 32 rows of A, dealt to the
-// workgroups in turn.  B is loaded once into registers (wave w holds the MFMA fragments of
-// its N/4 columns for all of K).  The tiles stream through an LDS ring of R slots, each
-// holding one tile's A rows and, with a residual, its residual rows, by LDS-DMA buffer
-// loads that every wave shares; R tiles are in flight at a time.  Per tile a wave runs
-// K/16 x N/128 MFMAs out of LDS and then its epilogue, whose stores go out after the next
-// tile's loads.  Loads past the last tile or row read zeros and stores past them are
-// dropped (out-of-range buffer offsets), so every wave issues the same loads and stores
-// each iteration and the memory-counter waits are constants.
+// Here a workgroup of four waves owns a block of 128 to 384 output columns and is persistent
+// over tiles of 32 rows of A, dealt to the workgroups of its block in turn.  B's block is
+// loaded once into registers (wave w holds the MFMA fragments of a quarter of the block's
+// columns for all of K).  The tiles stream through an LDS ring of R slots, each holding one
+// tile's A rows and, with a residual, its residual rows, by LDS-DMA buffer loads that every
+// wave shares; R tiles are in flight at a time.  Per tile a wave runs K/16 x N/128 MFMAs out
+// of LDS and then its epilogue, whose stores go out after the next tile's loads.  Loads past
+// the last tile or row read zeros and stores past them are dropped (out-of-range buffer
+// offsets), so every wave issues the same loads and stores each iteration and the
+// memory-counter waits are constants.
+#include <cstdlib>
 #include <type_traits>
 
 #include "device_common.h"
@@ -36,8 +38,11 @@ __device__ __forceinline__ void unrolled(Fn&& f) {
     }
 }
 
-// CPW: 32-column output blocks per wave (N = 128 CPW); KS: 16-wide K steps (K = 16 KS);
-// OCC: workgroups a CU (the ring takes 128 KB of LDS over OCC)
+// CPW: 32-column output blocks per wave (a workgroup's column block is N = 128 CPW wide);
+// KS: 16-wide K steps (K = 16 KS); OCC: workgroups a CU (the ring takes 128 KB of LDS over
+// OCC).  The output is p.N = N nblk columns wide: workgroup b owns column block cb and walks
+// the row tiles gt, gt + Gt, ... (Gt workgroups a block), with the workgroups of one row tile
+// on one XCD, so that all but the first read of the tile's A rows hit its L2.
 template <int CPW, int KS, int OCC, int ACT, bool RES>
 __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, const int tiles) {
     constexpr int N = 128 * CPW, K = 16 * KS;
@@ -69,13 +74,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
     const int tid = static_cast<int>(threadIdx.x);
     // the wave index in a scalar register: the LDS-DMA destination (M0) must be uniform
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), half = lane >> 5, row = lane & 31;
-    const int G = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
-    const int64_t M = p.M;
+    const int nblk = p.N / N, b = static_cast<int>(blockIdx.x);
+    const int G = static_cast<int>(gridDim.x) / nblk;                // Gt: a multiple of 8
+    const int cb = (b >> 3) % nblk, wg = ((b >> 3) / nblk) * 8 + (b & 7);
+    const int n0 = cb * N;                                            // first output column
+    const int64_t M = p.M, LD = p.N;
     const __amdgpu_buffer_rsrc_t ar =
         buffer_rsrc(p.a, static_cast<uint32_t>(M * K * 2));
     const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(RES ? static_cast<const void*>(p.res) : p.a,
-                                                  static_cast<uint32_t>(RES ? M * N * 2 : 0));
-    const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(p.c, static_cast<uint32_t>(M * N * 2));
+                                                  static_cast<uint32_t>(RES ? M * LD * 2 : 0));
+    const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(p.c, static_cast<uint32_t>(M * LD * 2));
 
     // load j of this wave fills slot bytes [(wave LPW + j) KB, +1 KB): lane's 16-byte chunk
     // q = 64 (wave LPW + j) + lane sits at row q / CA, physical chunk q % CA, which holds
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
         } else {
             const int q = 64 * (lj - ALOADS) + lane, r = q / CR, pc = q % CR;
             lrow[j] = r;
-            rel[j] = static_cast<uint32_t>((r * N + 8 * (pc ^ (r & 15))) * 2);
+            rel[j] = static_cast<uint32_t>((r * LD + n0 + 8 * (pc ^ (r & 15))) * 2);
         }
     }
     auto issue = [&](int i) {   // the loads of this workgroup's tile i into slot i % R
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
                 const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * K * 2) + rel[j];
                 load_lds16_buf(ar, ok ? off : kOutOfRange, slot + lj * 1024);
             } else {
-                const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * N * 2) + rel[j];
+                const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * LD * 2) + rel[j];
                 load_lds16_buf(rr, ok ? off : kOutOfRange, slot + lj * 1024);
             }
         }
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
         const uint16_t* const brow = static_cast<const uint16_t*>(p.b) +
-                                     static_cast<int64_t>(32 * (CPW * wave + j) + row) * K + 8 * half;
+                                     static_cast<int64_t>(n0 + 32 * (CPW * wave + j) + row) * K + 8 * half;
 #pragma unroll
         for (int s = 0; s < KS; ++s) bf[j][s] = *reinterpret_cast<const bf16x8_t*>(brow + 16 * s);
     }
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             bias[j][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.shift) bias[j][g] = *reinterpret_cast<const f32x4_t*>(p.shift + 32 * (CPW * wave + j) + 8 * g + 4 * half);
+            if (p.shift) bias[j][g] = *reinterpret_cast<const f32x4_t*>(p.shift + n0 + 32 * (CPW * wave + j) + 8 * g + 4 * half);
         }
 
 #pragma unroll
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
                 const int q = 64 * u + lane, r = 8 * wave + q / CR, c = q % CR;
                 const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * N * 2 + 16 * (c ^ (r & 15)));
                 const int64_t m = t0 + r;
-                const uint32_t off = m < M ? static_cast<uint32_t>((m * N + 8 * c) * 2) : kOutOfRange;
+                const uint32_t off = m < M ? static_cast<uint32_t>((m * LD + n0 + 8 * c) * 2) : kOutOfRange;
                 __builtin_amdgcn_raw_buffer_store_b128(v, cr, off, 0, 0);
             }
         } else {
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int col = 32 * (CPW * wave + j) + 8 * g + 4 * half;
-                    const uint32_t off = m < M ? static_cast<uint32_t>((m * N + col) * 2) : kOutOfRange;
+                    const uint32_t off = m < M ? static_cast<uint32_t>((m * LD + n0 + col) * 2) : kOutOfRange;
                     __builtin_amdgcn_raw_buffer_store_b64(outv[j][g], cr, off, 0, 0);
                 }
         }
@@ -239,7 +247,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
 
 template <int CPW, int KS, int OCC, int ACT>
 hipError_t launch3(const MmaArgs& a, int tiles, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(tiles < 256 * OCC ? tiles : 256 * OCC));
+    // Gt workgroups a column block, a multiple of 8 (the tile-to-XCD mapping), at most the
+    // CUs' OCC slots
+    const int nblk = a.N / (128 * CPW);
+    const int cap = (256 * OCC / nblk) / 8 * 8, want = (tiles + 7) / 8 * 8;
+    const dim3 grid(static_cast<unsigned>((want < cap ? want : cap) * nblk));
     if (a.res)
         hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, true>), grid, dim3(256), 0, s, a, tiles);
     else
@@ -258,32 +270,52 @@ hipError_t launch2(const MmaArgs& a, int act, int tiles, hipStream_t s) {
     }
 }
 
+// built column blocks: 128, 256 and 384 wide for K = 128, 128 and 256 for K = 256 (B's
+// fragments take N K / 512 registers a lane, at most 128)
+bool built(int64_t nb, int64_t k) { return (k == 128 && nb <= 384) || (k == 256 && nb <= 256); }
+
+// a workgroup's column block: the widest built one that divides N, or what DLF_STREAM_NB
+// asks for where that is built and divides N (tuning only); 0 if none
+int64_t block_cols(int64_t n, int64_t k) {
+    if (const char* env = std::getenv("DLF_STREAM_NB")) {
+        const int64_t nb = std::atoll(env);
+        if ((nb == 128 || nb == 256 || nb == 384) && n % nb == 0 && built(nb, k)) return nb;
+    }
+    for (const int64_t nb : {384, 256, 128})
+        if (n % nb == 0 && built(nb, k)) return nb;
+    return 0;
+}
+
 }  // namespace
 
 bool gemm_stream_ok(const MmaArgs& a) {
-    if (a.scale || a.parts > 1 || a.M <= 0) return false;
-    if (a.N % 128 != 0 || a.N < 128 || a.N > 384) return false;
+    if (a.scale || a.parts > 1 || a.M <= 0 || a.N <= 0) return false;
     if (a.K != 128 && a.K != 256) return false;
-    if (static_cast<int64_t>(a.N) * a.K > 65536) return false;    // B fragments: at most 128 registers a lane
+    const int64_t nb = block_cols(a.N, a.K);
+    if (nb == 0 || a.N / nb > 32) return false;                   // at least 8 workgroups a block
     const int64_t lim = int64_t(1) << 31;
     return a.M * a.K * 2 < lim && a.M * a.N * 2 < lim;
 }
 
 bool gemm_stream_pays(const MmaArgs& a) {
-    // measured on MI355X against the tiled kernel: 1.1-1.4x faster from 32768 rows, level
-    // below that, 0.96x with N = K = 256.  K = 512 and N = 512 were slower and are not built.
-    return gemm_stream_ok(a) && a.M >= 32768 && static_cast<int64_t>(a.N) * a.K < 65536;
+    // measured on MI355X against the tiled kernel: 1.1-1.4x faster from 4M outputs with
+    // N = 128 to 384 (32768 rows of 128, 25088 rows of 256 or 384), 1.1-2.2x with N = 512 to
+    // 1024 in column blocks, 0.97x at 25088 rows of 128.  A variant with B blocks of K = 512
+    // (and so N = 128) was slower and is not built.
+    return gemm_stream_ok(a) && a.M * a.N >= (int64_t(1) << 22);
 }
 
 hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
     const int64_t tiles64 = (a.M + kSRows - 1) / kSRows;
     const int tiles = static_cast<int>(tiles64);
-    const int cpw = a.N / 128, ks = a.K / 16;
-    // two workgroups a CU (half the ring each) where N K = 32768, from 2048 tiles: measured
-    // 1.05-1.2x faster there, 0.95x at 1250 tiles.  With N = K = 128 two were level to 4%
-    // slower; N = 384 has no room for two (its staging area), and N = K = 256 needs more
-    // than 256 registers for its B fragments and accumulators.
-    const bool two = cpw * ks == 16 && tiles >= 2048;
+    const int64_t nb = block_cols(a.N, a.K);
+    const int cpw = static_cast<int>(nb / 128), ks = static_cast<int>(a.K / 16);
+    // two workgroups a CU (half the ring each) where the block's N K = 32768, from 2048 units
+    // of a row tile and a column block: measured 1.05-1.2x faster there, 0.95x at 1250.  With
+    // N = K = 128 two were level to 4% slower; N = 384 has no room for two (its staging
+    // area), and N = K = 256 needs more than 256 registers for its B fragments and
+    // accumulators.
+    const bool two = cpw * ks == 16 && tiles64 * (a.N / nb) >= 2048;
     switch (cpw * 1000 + ks * 10 + (two ? 2 : 1)) {
         case 1081: return launch2<1, 8, 1>(a, act, tiles, s);
         case 1161: return launch2<1, 16, 1>(a, act, tiles, s);

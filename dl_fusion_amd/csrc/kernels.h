@@ -58,10 +58,10 @@ int mma_tile_cols(int tile);
 // out: kOutBf16 / kOutFp8 / kOutF32; act: kActNone / kActRelu / kActGelu.
 hipError_t launch_mma_bf16(const MmaArgs& args, bool conv, int act, int tile, hipStream_t stream);
 hipError_t launch_mma_fp8(const MmaArgs& args, int act, int out, int tile, hipStream_t stream);
-// Streaming GEMM for memory-bound shapes (bf16, no scale, one output): N of 128, 256 or 384,
-// K of 128 or 256, N K <= 65536, A and C below 2 GB.
+// Streaming GEMM for memory-bound shapes (bf16, no scale, one output): K of 128 or 256, N a
+// multiple of 128 (column blocks of 128 to 384, at most 32 of them), A and C below 2 GB.
 bool gemm_stream_ok(const MmaArgs& args);
-// ... and where it is faster than the tiled kernel (at least 32768 rows)
+// ... and where it is faster than the tiled kernel (from 4M outputs)
 bool gemm_stream_pays(const MmaArgs& args);
 hipError_t launch_gemm_stream(const MmaArgs& args, int act, hipStream_t stream);
 // instantiation groups of the MFMA kernel (one translation unit each); wide: rows of 8 MB or

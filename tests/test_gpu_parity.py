@@ -373,10 +373,17 @@ STREAM_GEMM = [
     dict(m=33, n=256, k=256, act="relu", bias=True),
     dict(m=12345, n=384, k=128, act="gelu_tanh", bias=True),
     dict(m=4100, n=384, k=128, act="relu", bias=True),
-    dict(m=40000, n=128, k=256, act="relu", bias=True),        # the library's own choice takes it
+    dict(m=40000, n=128, k=256, act="relu", bias=True),        # the library's own choice takes
+    dict(m=20000, n=256, k=128, act="gelu_tanh", bias=True),   # these two (4M outputs or more)
     # N K = 32768 from 2048 tiles: two workgroups a CU (half the ring each)
     dict(m=70001, n=128, k=256, act="gelu_erf", bias=True),
     dict(m=66000, n=256, k=128, act="relu", bias=False),
+    # wider outputs in column blocks, several workgroups a row tile: 2 x 256, 5 x 128 (a
+    # block count that is no power of two), 3 x 256 at K = 256, and 2 x 256 at two a CU
+    dict(m=5000, n=512, k=128, act="relu", bias=True),
+    dict(m=3001, n=640, k=128, act="gelu_tanh", bias=True),
+    dict(m=2500, n=768, k=256, act="none", bias=True),
+    dict(m=70001, n=512, k=128, act="gelu_erf", bias=False),
 ]
 
 
@@ -407,6 +414,30 @@ def test_bf16_gemm_streaming_route(i, res):
     finally:
         os.environ.pop("DLF_GEMM", None)
 
+
+
+@pytest.mark.parametrize("nb,n,k", [(128, 512, 128), (128, 768, 256), (256, 768, 128)])
+def test_bf16_gemm_streaming_forced_block_width(nb, n, k):
+    """Column blocks narrower than the widest that divides N (DLF_STREAM_NB), with residual."""
+    wl = workloads.workload(3, m=4097, n=n, k=k, act="relu", bias=True)
+    inp = workloads.generate(wl)
+    r = workloads.bf16_bits(np.random.default_rng(7).standard_normal((wl.m, wl.n)).astype(np.float32))
+    ref = gemm_reference(inp, np.arange(wl.m), r)
+    L = layers().make_layer(inp, with_unfused=False)
+    r_d = layers().to_device(r, "bf16")
+    os.environ["DLF_GEMM"] = "stream"
+    os.environ["DLF_STREAM_NB"] = str(nb)
+    try:
+        case(f"gemm_fused {wl} route=stream block={nb} residual=True")
+        buf, y = guarded((wl.m, wl.n), torch.bfloat16)
+        L.forward(y=y, residual=r_d)
+        torch.cuda.synchronize()
+        assert guard_intact(buf, y.numel())
+        err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+        assert err <= TOL["bf16"], (wl, nb, err)
+    finally:
+        os.environ.pop("DLF_GEMM", None)
+        os.environ.pop("DLF_STREAM_NB", None)
 
 # Rows of 8 MB or more are past the 32-bit offsets of the buffer-resource loads: the library
 # reads them with 64-bit global addresses and the basic tiles (a tuned tile falls back to
