@@ -262,6 +262,10 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     a.H = static_cast<int>(d->h); a.W = static_cast<int>(d->w); a.Cin = static_cast<int>(d->c_in);
     a.Ho = static_cast<int>(g.ho); a.Wo = static_cast<int>(g.wo); a.KW = static_cast<int>(d->kw);
     a.SH = d->stride_h; a.SW = d->stride_w; a.PH = d->pad_h; a.PW = d->pad_w;
+    // a strided, unpadded 1x1 conv (a ResNet downsample) reads every SH-th row and SW-th pixel:
+    // the streaming kernel gathers those rows into its ring
+    if (!generic && d->kh == 1 && d->kw == 1 && d->pad_h == 0 && d->pad_w == 0 && stream_gemm(a))
+        return hip_status(dlf::launch_gemm_stream(a, act_code(d->act), s), what);
     // the value-by-value gather (c_in % 8 != 0) is latency-bound: smaller tiles, more of them
     const int tile = d->c_in % 8 != 0 && !std::getenv("DLF_TILE") ? static_cast<int>(dlf::kTile128x64)
                                                                   : pick_tile(g.M, d->c_out, false);

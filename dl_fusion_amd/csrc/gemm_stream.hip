@@ -43,7 +43,9 @@ __device__ __forceinline__ void unrolled(Fn&& f) {
 // OCC).  The output is p.N = N nblk columns wide: workgroup b owns column block cb and walks
 // the row tiles gt, gt + Gt, ... (Gt workgroups a block), with the workgroups of one row tile
 // on one XCD, so that all but the first read of the tile's A rows hit its L2.
-template <int CPW, int KS, int OCC, int ACT, bool RES>
+// GATHER: A's row m is output pixel m = (img, ho, wo) of an unpadded 1x1 convolution with
+// strides SH, SW, read from input pixel (img, SH ho, SW wo) of the NHWC input (c_in = K).
+template <int CPW, int KS, int OCC, int ACT, bool RES, bool GATHER>
 __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, const int tiles) {
     constexpr int N = 128 * CPW, K = 16 * KS;
     constexpr int kSLds = 128 * 1024 / OCC;
@@ -79,8 +81,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
     const int cb = (b >> 3) % nblk, wg = ((b >> 3) / nblk) * 8 + (b & 7);
     const int n0 = cb * N;                                            // first output column
     const int64_t M = p.M, LD = p.N;
-    const __amdgpu_buffer_rsrc_t ar =
-        buffer_rsrc(p.a, static_cast<uint32_t>(M * K * 2));
+    const uint32_t ho = static_cast<uint32_t>(p.Ho), wo = static_cast<uint32_t>(p.Wo);
+    const int64_t a_bytes = GATHER ? M / (int64_t(ho) * wo) * p.H * p.W * K * 2 : M * K * 2;
+    const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(p.a, static_cast<uint32_t>(a_bytes));
     const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(RES ? static_cast<const void*>(p.res) : p.a,
                                                   static_cast<uint32_t>(RES ? M * LD * 2 : 0));
     const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(p.c, static_cast<uint32_t>(M * LD * 2));
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
         if (lj < ALOADS) {
             const int q = 64 * lj + lane, r = q / CA, pc = q % CA;
             lrow[j] = r;
-            rel[j] = static_cast<uint32_t>((r * K + 8 * (pc ^ (r & 15))) * 2);
+            rel[j] = static_cast<uint32_t>(((GATHER ? 0 : r * K) + 8 * (pc ^ (r & 15))) * 2);
         } else {
             const int q = 64 * (lj - ALOADS) + lane, r = q / CR, pc = q % CR;
             lrow[j] = r;
@@ -113,7 +116,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_stream_kernel(const MmaArgs p, 
             const int64_t m = static_cast<int64_t>(t) * kSRows + lrow[j];
             const bool ok = t < tiles && m < M;
             if (lj < ALOADS) {
-                const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * K * 2) + rel[j];
+                uint32_t off;
+                if constexpr (GATHER) {
+                    const uint32_t mm = static_cast<uint32_t>(m), q = mm / wo, x = mm - q * wo;
+                    const uint32_t img = q / ho, y = q - img * ho;
+                    const uint32_t pix = (img * static_cast<uint32_t>(p.H) + y * static_cast<uint32_t>(p.SH)) *
+                                             static_cast<uint32_t>(p.W) + x * static_cast<uint32_t>(p.SW);
+                    off = pix * static_cast<uint32_t>(K * 2) + rel[j];
+                } else {
+                    off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * K * 2) + rel[j];
+                }
                 load_lds16_buf(ar, ok ? off : kOutOfRange, slot + lj * 1024);
             } else {
                 const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(t) * kSRows * LD * 2) + rel[j];
@@ -252,10 +264,12 @@ hipError_t launch3(const MmaArgs& a, int tiles, hipStream_t s) {
     const int nblk = a.N / (128 * CPW);
     const int cap = (256 * OCC / nblk) / 8 * 8, want = (tiles + 7) / 8 * 8;
     const dim3 grid(static_cast<unsigned>((want < cap ? want : cap) * nblk));
-    if (a.res)
-        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, true>), grid, dim3(256), 0, s, a, tiles);
+    if (a.Wo > 0)   // the strided 1x1 convolution: no residual (gemm_stream_ok)
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, false, true>), grid, dim3(256), 0, s, a, tiles);
+    else if (a.res)
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, true, false>), grid, dim3(256), 0, s, a, tiles);
     else
-        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, false>), grid, dim3(256), 0, s, a, tiles);
+        hipLaunchKernelGGL((gemm_stream_kernel<CPW, KS, OCC, ACT, false, false>), grid, dim3(256), 0, s, a, tiles);
     return hipGetLastError();
 }
 
@@ -274,13 +288,16 @@ hipError_t launch2(const MmaArgs& a, int act, int tiles, hipStream_t s) {
 // fragments take N K / 512 registers a lane, at most 128)
 bool built(int64_t nb, int64_t k) { return (k == 128 && nb <= 384) || (k == 256 && nb <= 256); }
 
-// a workgroup's column block: the widest built one that divides N, or what DLF_STREAM_NB
-// asks for where that is built and divides N (tuning only); 0 if none
-int64_t block_cols(int64_t n, int64_t k) {
+// a workgroup's column block: the widest built one that divides N (128 for gathered rows:
+// measured 1.2x faster than 256 on the strided 1x1 56x56x256 -> 28x28x512, where B's 128 KB
+// a workgroup cost more than the fourfold reads of A), or what DLF_STREAM_NB asks for where
+// that is built and divides N (tuning only); 0 if none
+int64_t block_cols(int64_t n, int64_t k, bool gather) {
     if (const char* env = std::getenv("DLF_STREAM_NB")) {
         const int64_t nb = std::atoll(env);
         if ((nb == 128 || nb == 256 || nb == 384) && n % nb == 0 && built(nb, k)) return nb;
     }
+    if (gather) return n % 128 == 0 ? 128 : 0;
     for (const int64_t nb : {384, 256, 128})
         if (n % nb == 0 && built(nb, k)) return nb;
     return 0;
@@ -291,9 +308,16 @@ int64_t block_cols(int64_t n, int64_t k) {
 bool gemm_stream_ok(const MmaArgs& a) {
     if (a.scale || a.parts > 1 || a.M <= 0 || a.N <= 0) return false;
     if (a.K != 128 && a.K != 256) return false;
-    const int64_t nb = block_cols(a.N, a.K);
+    const int64_t nb = block_cols(a.N, a.K, a.Wo > 0);
     if (nb == 0 || a.N / nb > 32) return false;                   // at least 8 workgroups a block
     const int64_t lim = int64_t(1) << 31;
+    if (a.Wo > 0) {   // gathered rows: an unpadded 1x1 convolution, without residual
+        if (a.res || a.KW != 1 || a.PH != 0 || a.PW != 0 || a.Cin != a.K || a.Ho <= 0 || a.SH <= 0 || a.SW <= 0)
+            return false;
+        const int64_t px = int64_t(a.Ho) * a.Wo;
+        if (a.M % px != 0 || int64_t(a.SH) * (a.Ho - 1) >= a.H || int64_t(a.SW) * (a.Wo - 1) >= a.W) return false;
+        if (a.M / px * a.H * a.W * a.K * 2 >= lim) return false;
+    }
     return a.M * a.K * 2 < lim && a.M * a.N * 2 < lim;
 }
 
@@ -302,13 +326,17 @@ bool gemm_stream_pays(const MmaArgs& a) {
     // N = 128 to 384 (32768 rows of 128, 25088 rows of 256 or 384), 1.1-2.2x with N = 512 to
     // 1024 in column blocks, 0.97x at 25088 rows of 128.  A variant with B blocks of K = 512
     // (and so N = 128) was slower and is not built.
+    // Gathered rows (strided 1x1 convolutions) pay from N = 512 only: 1.23x at 56x56x256 ->
+    // 28x28x512 (stride 2), 0.75x at 56x56x256 -> 28x28x256, where the implicit GEMM's
+    // tiles read the strided rows faster.
+    if (a.Wo > 0 && a.N < 512) return false;
     return gemm_stream_ok(a) && a.M * a.N >= (int64_t(1) << 22);
 }
 
 hipError_t launch_gemm_stream(const MmaArgs& a, int act, hipStream_t s) {
     const int64_t tiles64 = (a.M + kSRows - 1) / kSRows;
     const int tiles = static_cast<int>(tiles64);
-    const int64_t nb = block_cols(a.N, a.K);
+    const int64_t nb = block_cols(a.N, a.K, a.Wo > 0);
     const int cpw = static_cast<int>(nb / 128), ks = static_cast<int>(a.K / 16);
     // two workgroups a CU (half the ring each) where the block's N K = 32768, from 2048 units
     // of a row tile and a column block: measured 1.05-1.2x faster there, 0.95x at 1250.  With

@@ -157,6 +157,48 @@ def test_bf16_conv_ragged_shapes_every_tile(i):
     check_conv(wl, tiles=CONV_TILES, unfused=(i < 3))
 
 
+
+# Unpadded strided 1x1 convolutions (a ResNet downsample) stream with their rows gathered:
+# strides 2 and 3, odd and even image sides, one to three column blocks, K of 128 and 256,
+# with and without activation and conv bias; forced onto the streaming kernel (DLF_GEMM=
+# stream; its 128-wide column blocks, and 256-wide ones where they divide c_out), onto the
+# implicit GEMM (DLF_GEMM=tiled, DLF_CONV=generic), and on the library's own choice (the last
+# case is large enough for it to stream), each against the oracle.
+STRIDED_1X1 = [
+    dict(n=3, h=15, w=13, cin=256, cout=512, kh=1, kw=1, stride=2, pad=0, act="none", residual=False),
+    dict(n=2, h=12, w=12, cin=128, cout=384, kh=1, kw=1, stride=2, pad=0, act="relu", residual=False),
+    dict(n=1, h=17, w=20, cin=256, cout=256, kh=1, kw=1, stride=3, pad=0, act="gelu_erf", residual=False),
+    dict(n=12, h=56, w=56, cin=256, cout=512, kh=1, kw=1, stride=2, pad=0, act="none", residual=False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(STRIDED_1X1)))
+def test_bf16_strided_1x1_streaming_route(i):
+    wl = workloads.workload(1, conv_bias=bool(i % 2), **STRIDED_1X1[i])
+    inp = workloads.generate(wl)
+    ref = oracle.conv_bn_act(inp)
+    L = layers().make_layer(inp, with_unfused=False)
+    routes = [("stream", None, None), ("tiled", None, None), (None, "generic", None), (None, None, None)]
+    if wl.cout % 256 == 0:
+        routes.append(("stream", None, "256"))
+    try:
+        for gemm, conv, nb in routes:
+            for key, val in (("DLF_GEMM", gemm), ("DLF_CONV", conv), ("DLF_STREAM_NB", nb)):
+                if val is None:
+                    os.environ.pop(key, None)
+                else:
+                    os.environ[key] = val
+            case(f"conv_fused {wl} gemm={gemm} conv={conv} block={nb}")
+            buf, y = guarded(L.out_shape, torch.bfloat16)
+            L.forward(y=y)
+            torch.cuda.synchronize()
+            assert guard_intact(buf, y.numel()), "store beyond the output"
+            err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+            assert err <= TOL["bf16"], (wl, gemm, conv, nb, err)
+    finally:
+        for key in ("DLF_GEMM", "DLF_CONV", "DLF_STREAM_NB"):
+            os.environ.pop(key, None)
+
 # Any number of input channels (Cin % 8 != 0): the implicit GEMM gathers both operands value
 # by value.  The stem geometry (7x7, stride 2, pad 3, three channels), a ragged K of 27, one
 # channel, and 5 or 12 channels with a residual and a stride.
