@@ -21,10 +21,19 @@ namespace dlf {
 namespace {
 
 constexpr int kSmallLds = 65536;   // bytes: weights first, then the patch
+constexpr int kSmallStage = 4096;  // bytes a wave: one finished 32-pixel fragment
+
+// bytes between two output channels' weights: KH kwp 8, plus 16 where that is an even number
+// of 16-byte chunks, so that the 32 lanes' fragment reads (one channel each) fall in distinct
+// LDS banks
+__host__ __device__ inline int smallc_wstride(int kh, int kwp) {
+    const int b = kh * kwp * 8;
+    return (b / 16) % 2 == 0 ? b + 16 : b;
+}
 
 template <int ACT, bool RES>
 __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmallLds];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmallLds + 4 * kSmallStage];
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     int bid = static_cast<int>(blockIdx.x);
@@ -36,9 +45,9 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
     const int nco = min(64, p.Cout - co0);                  // 32 or 64
     const int ho0 = rt * p.th;
     const int rows = min(p.th, p.Ho - ho0);
-    const int wgroup = p.KH * p.kwp;                       // 8-byte groups per output channel
+    const int wstride = smallc_wstride(p.KH, p.kwp);
     uint8_t* const sw = smem;
-    uint8_t* const sx = smem + 64 * wgroup * 8;
+    uint8_t* const sx = smem + 64 * wstride;
 
     // ---- zero both regions (padding taps, the fourth channel, rows and columns outside) ----
     for (int i = tid; i < kSmallLds / 16; i += 256)
@@ -69,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t word = v[u][e >> 1];
                     const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-                    *reinterpret_cast<uint16_t*>(sw + (((co * p.KH + r) * p.kwp + sx_) * 4 + ci) * 2) = val;
+                    *reinterpret_cast<uint16_t*>(sw + co * wstride + ((r * p.kwp + sx_) * 4 + ci) * 2) = val;
                     if (++ci == p.Cin) {
                         ci = 0;
                         if (++sx_ == p.KW) {
@@ -134,8 +143,10 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
     const int ksteps = p.kwp / 4;                           // 1 .. 4 (the host bounds KH * kwp)
     const int nj = nco / 32;
     uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
-    const uint8_t* const bbase = sw + (((lane & 31) * p.KH) * p.kwp + 2 * half) * 8;
-    const int bstep_j = 32 * wgroup * 8;
+    const uint8_t* const bbase = sw + (lane & 31) * wstride + 2 * half * 8;
+    const int bstep_j = 32 * wstride;
+    uint8_t* const stg = smem + kSmallLds + wave * kSmallStage;
+    const int cpr = nco / 8;                                // 16-byte chunks of a staged row
     for (int f0 = wave; f0 < nfrag; f0 += 8) {
         int hl[2], wo[2];
         bool pv[2];
@@ -180,45 +191,64 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
             }
         }
         // lane: pixel of fragment f0 + 4u; register group g of channel fragment j holds
-        // channels 32 j + 8 g + 4 half .. +3
-        auto store = [&](const f32x16_t& accv, int u, int j) {
-            const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hl[u]) * p.Wo + wo[u];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int co = co0 + 32 * j + 8 * g + 4 * half;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = accv[4 * g + e];
-                if (p.bias) {
-                    const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + co);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += bv[e];
-                }
-                const int64_t off = pix * p.Cout + co;
-                if constexpr (RES) {
-                    const uint2 rv = *reinterpret_cast<const uint2*>(p.res + off);
-                    v[0] += __uint_as_float(rv.x << 16);
-                    v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
-                    v[2] += __uint_as_float(rv.y << 16);
-                    v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
-                }
-                if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
-                }
-                uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-                if constexpr (ACT == kActRelu) {
-                    lo = relu_bf16x2(lo);
-                    hi = relu_bf16x2(hi);
-                }
-                *reinterpret_cast<uint2*>(yb + off * 2) = make_uint2(lo, hi);
-            }
-        };
+        // channels 32 j + 8 g + 4 half .. +3.  The finished fragment goes through this wave's
+        // staging area, 32 rows of 128 bytes with chunk c of row m at c ^ ((m >> 1) & 7), and
+        // out as whole rows of 16-byte stores.
+        const int m = lane & 31, swz = (m >> 1) & 7;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            if (!pv[u]) continue;
-            store(acc[u][0], u, 0);
-            if (nj > 1) store(acc[u][1], u, 1);
+            const int f = f0 + 4 * u;
+            if (f >= nfrag) break;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (j >= nj) break;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int co = co0 + 32 * j + 8 * g + 4 * half;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[u][j][4 * g + e];
+                    if (p.bias) {
+                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + co);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                    }
+                    if constexpr (RES) {
+                        if (pv[u]) {
+                            const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hl[u]) * p.Wo + wo[u];
+                            const uint2 rv = *reinterpret_cast<const uint2*>(p.res + pix * p.Cout + co);
+                            v[0] += __uint_as_float(rv.x << 16);
+                            v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
+                            v[2] += __uint_as_float(rv.y << 16);
+                            v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
+                        }
+                    }
+                    if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                    }
+                    uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                    if constexpr (ACT == kActRelu) {
+                        lo = relu_bf16x2(lo);
+                        hi = relu_bf16x2(hi);
+                    }
+                    *reinterpret_cast<uint2*>(stg + m * 128 + (((4 * j + g) ^ swz) << 4) + 8 * half) = make_uint2(lo, hi);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's staging writes are done
+            __builtin_amdgcn_wave_barrier();
+            // rows of the fragment: pixel f 32 + r of the tile, cpr chunks each
+            for (int q = lane; q < 32 * cpr; q += 64) {
+                const int r = q / cpr, c = q - r * cpr;
+                const int pl = f * 32 + r;
+                if (pl >= npx) continue;
+                const int hr = pl / p.Wo, wr = pl - hr * p.Wo;
+                const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hr) * p.Wo + wr;
+                const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+                *reinterpret_cast<u32x4_t*>(yb + (pix * p.Cout + co0 + 8 * c) * 2) = val;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // the staging reads are done before the next writes
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -241,7 +271,7 @@ bool conv_smallc_plan(int N, int H, int W, int Cin, int Cout, int KH, int KW, in
     if ((W * Cin) % 8 != 0) return false;                 // whole 16-byte chunks per input row
     const int kwp = (KW + 3) / 4 * 4;
     if (kwp > 16) return false;                            // at most four MFMA steps per kernel row
-    const int wbytes = 64 * KH * kwp * 8;
+    const int wbytes = 64 * smallc_wstride(KH, kwp);
     if (wbytes > kSmallLds / 2) return false;
     // patch columns: every input column (filled) and every column a fragment reads, padded
     // taps included
