@@ -115,6 +115,9 @@ _SIGS = {
     "dlf_quant_apply": [_i64, _vp, ctypes.c_float, _vp, _vp],
     "dlf_ffn_pack": [_i64, _i64, _vp, _vp],
     "dlf_ffn_fused": [ctypes.POINTER(dlf_ffn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "dlf_ffn_workspace_bytes": [ctypes.POINTER(dlf_ffn_desc), ctypes.POINTER(ctypes.c_size_t)],
+    "dlf_ffn_fused_ws": [ctypes.POINTER(dlf_ffn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                         _vp],
     "dlf_fusion_plan": [ctypes.POINTER(dlf_graph_node), ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                         ctypes.POINTER(dlf_fusion_group), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
@@ -281,6 +284,18 @@ def dlf_ffn_pack(w_bits):
 def dlf_ffn_fused(desc, x, w1_packed, b1, w2_packed, b2, residual, y, stream=None):
     _check(_lib.dlf_ffn_fused(ctypes.byref(desc), _dev(x), _dev(w1_packed), _dev(b1), _dev(w2_packed), _dev(b2),
                               _dev(residual), _dev(y), _stream(stream)), "dlf_ffn_fused")
+
+
+def dlf_ffn_workspace_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(_lib.dlf_ffn_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "dlf_ffn_workspace_bytes")
+    return n.value
+
+
+def dlf_ffn_fused_ws(desc, x, w1_packed, b1, w2_packed, b2, residual, y, workspace, workspace_bytes, stream=None):
+    _check(_lib.dlf_ffn_fused_ws(ctypes.byref(desc), _dev(x), _dev(w1_packed), _dev(b1), _dev(w2_packed), _dev(b2),
+                                 _dev(residual), _dev(y), _dev(workspace), int(workspace_bytes), _stream(stream)),
+           "dlf_ffn_fused_ws")
 
 
 def graph_nodes(graph):

@@ -43,9 +43,10 @@ extern "C" dlf_status dlf_ffn_pack(int64_t rows, int64_t k, const uint16_t* w, u
     return ok();
 }
 
-extern "C" dlf_status dlf_ffn_fused(const dlf_ffn_desc* d, const void* x, const void* w1_packed,
-                                    const float* b1, const void* w2_packed, const float* b2,
-                                    const void* residual, void* y, void* stream) {
+namespace {
+
+// the descriptor's checks; fills the sizes and the activation code
+dlf_status check_ffn_desc(const dlf_ffn_desc* d, dlf::FfnArgs* a, int* act) {
     if (!d) return fail(DLF_ERR_INVALID_ARG, "ffn descriptor is NULL");
     if (d->m < 0 || d->d_model < 0 || d->d_ff < 0) return fail(DLF_ERR_INVALID_ARG, "negative dimension");
     if (d->act != DLF_ACT_NONE && d->act != DLF_ACT_RELU && d->act != DLF_ACT_GELU_TANH &&
@@ -61,7 +62,23 @@ extern "C" dlf_status dlf_ffn_fused(const dlf_ffn_desc* d, const void* x, const 
     if (d->d_ff <= 0 || d->d_ff % 256 != 0 || d->d_ff > (int64_t(1) << 24))
         return fail(DLF_ERR_UNSUPPORTED, "d_ff must be a positive multiple of 256 below 2^24");
     if (d->m > (int64_t(1) << 36)) return fail(DLF_ERR_UNSUPPORTED, "too many tokens");
-    if (d->m == 0) return ok();
+    *a = dlf::FfnArgs{};
+    a->M = d->m;
+    a->D = static_cast<int>(d->d_model);
+    a->F = static_cast<int>(d->d_ff);
+    a->parts = 1;
+    *act = d->act == DLF_ACT_RELU ? dlf::kActRelu
+         : d->act == DLF_ACT_GELU_TANH ? dlf::kActGelu
+         : d->act == DLF_ACT_GELU_ERF ? dlf::kActGeluErf : dlf::kActNone;
+    return ok();
+}
+
+// every check of the fused block's arguments, before any HIP call; fills a
+dlf_status check_ffn(const dlf_ffn_desc* d, const void* x, const void* w1_packed, const float* b1,
+                     const void* w2_packed, const float* b2, const void* residual, void* y, dlf::FfnArgs* a,
+                     int* act) {
+    const dlf_status st = check_ffn_desc(d, a, act);
+    if (st != DLF_OK || d->m == 0) return st;
     if (!x || !w1_packed || !w2_packed || !y) return fail(DLF_ERR_INVALID_ARG, "x, weights and y must be non-NULL");
     if (!aligned16(x) || !aligned16(w1_packed) || !aligned16(w2_packed) || !aligned16(y) ||
         (b1 && !aligned16(b1)) || (b2 && !aligned16(b2)) || (residual && !aligned16(residual)))
@@ -72,21 +89,73 @@ extern "C" dlf_status dlf_ffn_fused(const dlf_ffn_desc* d, const void* x, const 
         overlaps(y, act_bytes, w2_packed, w_bytes) || overlaps(y, act_bytes, b1, static_cast<size_t>(d->d_ff) * 4) ||
         overlaps(y, act_bytes, b2, static_cast<size_t>(d->d_model) * 4) || overlaps(y, act_bytes, residual, act_bytes))
         return fail(DLF_ERR_ALIAS, "output overlaps an input");
-    dlf::FfnArgs a{};
-    a.x = static_cast<const uint16_t*>(x);
-    a.w1p = static_cast<const uint16_t*>(w1_packed);
-    a.b1 = b1;
-    a.w2p = static_cast<const uint16_t*>(w2_packed);
-    a.b2 = b2;
-    a.res = static_cast<const uint16_t*>(residual);
-    a.y = static_cast<uint16_t*>(y);
-    a.M = d->m;
-    a.D = static_cast<int>(d->d_model);
-    a.F = static_cast<int>(d->d_ff);
-    const int act = d->act == DLF_ACT_RELU ? dlf::kActRelu
-                  : d->act == DLF_ACT_GELU_TANH ? dlf::kActGelu
-                  : d->act == DLF_ACT_GELU_ERF ? dlf::kActGeluErf : dlf::kActNone;
+    a->x = static_cast<const uint16_t*>(x);
+    a->w1p = static_cast<const uint16_t*>(w1_packed);
+    a->b1 = b1;
+    a->w2p = static_cast<const uint16_t*>(w2_packed);
+    a->b2 = b2;
+    a->res = static_cast<const uint16_t*>(residual);
+    a->y = static_cast<uint16_t*>(y);
+    return ok();
+}
+
+// bytes of the d_ff split's partial sums, 0 where the block does not split
+size_t ffn_ws_bytes(const dlf_ffn_desc* d) {
+    if (dlf::ffn_parts(d->m, static_cast<int>(d->d_model), static_cast<int>(d->d_ff)) != 2) return 0;
+    return static_cast<size_t>(2 * d->m * d->d_model) * 4;
+}
+
+}  // namespace
+
+extern "C" dlf_status dlf_ffn_fused(const dlf_ffn_desc* d, const void* x, const void* w1_packed,
+                                    const float* b1, const void* w2_packed, const float* b2,
+                                    const void* residual, void* y, void* stream) {
+    dlf::FfnArgs a;
+    int act = 0;
+    const dlf_status st = check_ffn(d, x, w1_packed, b1, w2_packed, b2, residual, y, &a, &act);
+    if (st != DLF_OK || d->m == 0) return st;
     const hipError_t e = dlf::launch_ffn(a, act, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DLF_ERR_HIP, "dlf_ffn_fused: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" dlf_status dlf_ffn_workspace_bytes(const dlf_ffn_desc* d, size_t* bytes) {
+    if (!bytes) return fail(DLF_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    dlf::FfnArgs a;
+    int act = 0;
+    const dlf_status st = check_ffn_desc(d, &a, &act);
+    if (st != DLF_OK) return st;
+    *bytes = ffn_ws_bytes(d);
+    return ok();
+}
+
+extern "C" dlf_status dlf_ffn_fused_ws(const dlf_ffn_desc* d, const void* x, const void* w1_packed,
+                                       const float* b1, const void* w2_packed, const float* b2,
+                                       const void* residual, void* y, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+    dlf::FfnArgs a;
+    int act = 0;
+    const dlf_status st = check_ffn(d, x, w1_packed, b1, w2_packed, b2, residual, y, &a, &act);
+    if (st != DLF_OK || d->m == 0) return st;
+    const size_t need = ffn_ws_bytes(d);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DLF_ERR_INVALID_ARG, "workspace of %zu bytes needed (dlf_ffn_workspace_bytes), got %zu",
+                        need, workspace ? workspace_bytes : size_t(0));
+        if (!aligned16(workspace)) return fail(DLF_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        const size_t act_bytes = static_cast<size_t>(d->m * d->d_model) * 2;
+        const size_t w_bytes = static_cast<size_t>(d->d_ff * d->d_model) * 2;
+        if (overlaps(workspace, need, x, act_bytes) || overlaps(workspace, need, y, act_bytes) ||
+            overlaps(workspace, need, residual, act_bytes) || overlaps(workspace, need, w1_packed, w_bytes) ||
+            overlaps(workspace, need, w2_packed, w_bytes) ||
+            overlaps(workspace, need, b1, static_cast<size_t>(d->d_ff) * 4) ||
+            overlaps(workspace, need, b2, static_cast<size_t>(d->d_model) * 4))
+            return fail(DLF_ERR_ALIAS, "workspace overlaps an operand");
+        a.parts = 2;
+        a.ws = static_cast<float*>(workspace);
+    }
+    const hipError_t e = dlf::launch_ffn(a, act, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DLF_ERR_HIP, "dlf_ffn_fused_ws: %s", hipGetErrorString(e));
     return ok();
 }

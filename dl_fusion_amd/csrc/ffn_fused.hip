@@ -43,7 +43,10 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // DB: 32-column output blocks per wave (d_model = 256 DB); FT: 32-token fragments per
 // workgroup.  With FT = 2 the weights are read once per 64 tokens (half the L2 traffic of
 // FT = 1) and the h buffer is single (LDS), which costs a second barrier per chunk.
-template <int ACT, int DB, int FT>
+// SPL = 2: workgroup 2 b + part takes token block b and the chunks of its half of d_ff, and
+// writes its fp32 partial sum of y (no bias, no residual) to p.ws[part]; ffn_reduce_kernel
+// finishes y.  Each workgroup then streams half the weights for its tokens.
+template <int ACT, int DB, int FT, int SPL>
 __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     // weight fragments in flight per wave: the stream is latency-bound, so as many as the
     // registers allow (4 a fragment beside the FT x DB accumulators)
@@ -60,9 +63,11 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     static_assert(QN % kRing == 0, "the ring index repeats from chunk to chunk");
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, tok = lane & 31;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * TOK;
+    const int part = SPL == 2 ? static_cast<int>(blockIdx.x & 1u) : 0;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x / SPL) * TOK;
     const int F = p.F;
     const int nchunks = F / kChunk;
+    const int cbeg = part * nchunks / SPL, cend = (part + 1) * nchunks / SPL;   // this part's chunks
 
     // ---- x rows m0 .. m0+TOK-1 into LDS (zero past M) ----
     for (int i = tid; i < TOK * (D / 8); i += 512) {
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     };
     u32x4_t ring[kRing];
 #pragma unroll
-    for (int q = 0; q < kRing; ++q) ring[q] = *frag(0, q);
+    for (int q = 0; q < kRing; ++q) ring[q] = *frag(cbeg, q);
 
     f32x16_t acc2[DB][FT];
 #pragma unroll
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
             for (int e = 0; e < 16; ++e) acc2[b][f][e] = 0.0f;
     __syncthreads();
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = cbeg; c < cend; ++c) {
         uint8_t* const hbuf = hs[NB == 2 ? (c & 1) : 0];
         // FC1 accumulators: FT token fragments, each split over even and odd k-steps when there
         // is only one, so that two independent chains keep the matrix pipe busy
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
             if constexpr (q + kRing < QN) {
                 ring[q % kRing] = *frag(c, q + kRing);
             } else {
-                if (c + 1 < nchunks) ring[q % kRing] = *frag(c + 1, q + kRing - QN);
+                if (c + 1 < cend) ring[q % kRing] = *frag(c + 1, q + kRing - QN);
             }
             return wv;
         };
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
         });
         if constexpr (NB == 1) {
             // one h buffer: every wave must be done reading the previous chunk's h
-            if (c > 0) {
+            if (c > cbeg) {
                 wait_vm_lgkm<63, 0>();
                 barrier();
             }
@@ -185,6 +190,10 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc2[b][f][4 * g + e];
+                if constexpr (SPL == 2) {
+                    *reinterpret_cast<f32x4_t*>(p.ws + (part * p.M + m) * D + col) = f32x4_t{v[0], v[1], v[2], v[3]};
+                    continue;
+                }
                 if (p.b2) {
                     const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.b2 + col);
 #pragma unroll
@@ -204,44 +213,102 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     }
 }
 
-template <int ACT, int FT>
+// y = bf16(ws[0] + ws[1] + b2 [+ residual]), 8 columns a thread (D is a multiple of 256)
+__global__ __launch_bounds__(256) void ffn_reduce_kernel(const FfnArgs p) {
+    const int64_t groups = p.M * (p.D / 8);
+    const int64_t half = p.M * p.D;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < groups;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t off = 8 * i;
+        const int col = static_cast<int>(off % p.D);
+        float v[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.ws + off + 4 * h);
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p.ws + half + off + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * h + e] = a[e] + b[e];
+        }
+        if (p.b2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.b2 + col + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * h + e] += bv[e];
+            }
+        }
+        if (p.res) {
+            const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(p.res + off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] += __uint_as_float(rv[e] << 16);
+                v[2 * e + 1] += __uint_as_float(rv[e] & 0xFFFF0000u);
+            }
+        }
+        *reinterpret_cast<u32x4_t*>(p.y + off) = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    }
+}
+
+template <int ACT, int FT, int SPL>
 hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
-    const int64_t blocks = (a.M + 32 * FT - 1) / (32 * FT);
+    const int64_t blocks = (a.M + 32 * FT - 1) / (32 * FT) * SPL;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks));
     switch (a.D) {
-        case 256: hipLaunchKernelGGL((ffn_kernel<ACT, 1, FT>), grid, dim3(512), 0, s, a); break;
-        case 512: hipLaunchKernelGGL((ffn_kernel<ACT, 2, FT>), grid, dim3(512), 0, s, a); break;
-        case 768: hipLaunchKernelGGL((ffn_kernel<ACT, 3, FT>), grid, dim3(512), 0, s, a); break;
+        case 256: hipLaunchKernelGGL((ffn_kernel<ACT, 1, FT, SPL>), grid, dim3(512), 0, s, a); break;
+        case 512: hipLaunchKernelGGL((ffn_kernel<ACT, 2, FT, SPL>), grid, dim3(512), 0, s, a); break;
+        case 768: hipLaunchKernelGGL((ffn_kernel<ACT, 3, FT, SPL>), grid, dim3(512), 0, s, a); break;
         case 1024:
             if constexpr (FT == 1) {   // 64 tokens of 1024 columns do not fit LDS beside h
-                hipLaunchKernelGGL((ffn_kernel<ACT, 4, FT>), grid, dim3(512), 0, s, a);
+                hipLaunchKernelGGL((ffn_kernel<ACT, 4, FT, SPL>), grid, dim3(512), 0, s, a);
                 break;
             } else {
                 return hipErrorInvalidValue;
             }
         default: return hipErrorInvalidValue;
     }
+    if constexpr (SPL == 2) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t groups = a.M * (a.D / 8);
+        const int64_t rb = (groups + 255) / 256;
+        hipLaunchKernelGGL(ffn_reduce_kernel, dim3(static_cast<unsigned>(rb < 2048 ? rb : 2048)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 // 64 tokens per workgroup (half the weight traffic) once that still gives a workgroup per CU
 // (256 of them), else 32; d_model 1024 always takes 32.  DLF_FFN_TOK=32|64 forces one (tests).
+// Split over d_ff (parts == 2): 64 tokens and half of d_ff per workgroup.
 template <int ACT>
 hipError_t launch_act(const FfnArgs& a, hipStream_t s) {
+    if (a.parts == 2) return launch_d<ACT, 2, 2>(a, s);
     int tok = a.M >= 64 * 256 && a.D <= 768 ? 64 : 32;
     if (const char* env = std::getenv("DLF_FFN_TOK")) {
         const int t = std::atoi(env);
         if (t == 32 || (t == 64 && a.D <= 768)) tok = t;
     }
-    return tok == 64 ? launch_d<ACT, 2>(a, s) : launch_d<ACT, 1>(a, s);
+    return tok == 64 ? launch_d<ACT, 2, 1>(a, s) : launch_d<ACT, 1, 1>(a, s);
 }
 
 }  // namespace
 
+int ffn_parts(int64_t M, int D, int F) {
+    // built for d_model <= 768 and at least two chunks of d_ff; taken where 64-token blocks
+    // give fewer than 256 workgroups unsplit and at least 256 split (8192 <= M < 16384)
+    const bool can = D <= 768 && F / kChunk >= 2;
+    if (const char* env = std::getenv("DLF_FFN_SPLIT")) {
+        if (std::atoi(env) == 0) return 1;
+        if (std::atoi(env) == 1 && can) return 2;
+    }
+    return can && M >= 64 * 128 && M < 64 * 256 ? 2 : 1;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, int act, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.F <= 0 || a.F % kChunk != 0) return hipErrorInvalidValue;
+    if (a.parts == 2 && (!a.ws || a.D > 768 || a.F / kChunk < 2)) return hipErrorInvalidValue;
     switch (act) {
         case kActNone: return launch_act<kActNone>(a, s);
         case kActRelu: return launch_act<kActRelu>(a, s);

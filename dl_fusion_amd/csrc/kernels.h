@@ -145,7 +145,14 @@ struct FfnArgs {
     uint16_t* y;            // [M][D]
     int64_t M;
     int D, F;               // D in {256, 512, 768, 1024}; F a positive multiple of 256
+    // parts == 2: two workgroups a 64-token block, each over half of d_ff, write fp32 partial
+    // sums of y to ws [2][M][D], which a second kernel adds with b2 and the residual
+    int parts;
+    float* ws;
 };
+// the d_ff parts the fused FFN splits into for these sizes (1 or 2); DLF_FFN_SPLIT=0|1
+// forces one where both are built
+int ffn_parts(int64_t M, int D, int F);
 hipError_t launch_ffn(const FfnArgs& args, int act, hipStream_t stream);
 
 // Elementwise passes of the unfused chain.  dt: 0 fp32, 1 bf16.

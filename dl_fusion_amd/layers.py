@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 from . import (dlf_act_apply, dlf_add, dlf_bn_apply, dlf_bn_scale_shift, dlf_conv_fused, dlf_conv_plain,
-               dlf_ffn_fused, dlf_ffn_pack, ffn_desc,
+               dlf_ffn_fused_ws, dlf_ffn_pack, dlf_ffn_workspace_bytes, ffn_desc,
                dlf_fold_bn, dlf_gemm_fused, dlf_gemm_plain, dlf_quant_apply, dlf_scale_shift_apply,
                conv_desc, gemm_desc)
 
@@ -189,9 +189,10 @@ class Fp8LinearBNReluQuant:
 
 
 class FusedFFN:
-    """Transformer feed-forward block: one dlf_ffn_fused launch (weights packed once at load
-    by dlf_ffn_pack); the unfused form is FC1 (+ b1, act) and FC2 (+ b2, + residual) as two
-    GEMMs with their own register epilogues, the intermediate going through HBM."""
+    """Transformer feed-forward block: dlf_ffn_fused_ws (weights packed once at load by
+    dlf_ffn_pack, and the workspace its d_ff split asks for, allocated at load); the unfused
+    form is FC1 (+ b1, act) and FC2 (+ b2, + residual) as two GEMMs with their own register
+    epilogues, the intermediate going through HBM."""
 
     def __init__(self, inp: dict, device="cuda", with_unfused=True):
         wl = inp["workload"]
@@ -204,6 +205,8 @@ class FusedFFN:
         self.b2 = torch.from_numpy(inp["b2"]).to(device)
         self.res = to_device(inp.get("residual"), "bf16", device)
         self.y = torch.empty((wl.m, wl.d_model), dtype=torch.bfloat16, device=device)
+        self.ws_bytes = dlf_ffn_workspace_bytes(self.desc)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) if self.ws_bytes else None
         self.with_unfused = with_unfused
         if with_unfused:
             self.w1 = to_device(inp["w1"], "bf16", device)
@@ -215,7 +218,8 @@ class FusedFFN:
 
     def forward(self, stream=None, y=None):
         out = self.y if y is None else y
-        dlf_ffn_fused(self.desc, self.x, self.w1p, self.b1, self.w2p, self.b2, self.res, out, stream)
+        dlf_ffn_fused_ws(self.desc, self.x, self.w1p, self.b1, self.w2p, self.b2, self.res, out, self.ws,
+                         self.ws_bytes, stream)
         return out
 
     def forward_unfused(self, stream=None):

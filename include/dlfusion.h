@@ -47,6 +47,7 @@
 #ifndef DLFUSION_H
 #define DLFUSION_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -324,6 +325,29 @@ dlf_status dlf_ffn_pack(int64_t rows, int64_t k, const uint16_t *w, uint16_t *pa
 dlf_status dlf_ffn_fused(const dlf_ffn_desc *d, const void *x, const void *w1_packed,
                          const float *b1, const void *w2_packed, const float *b2,
                          const void *residual, void *y, void *stream);
+
+/* Bytes of device workspace dlf_ffn_fused_ws needs for d (0 where it does
+ * not split), written to *bytes.  The same descriptor checks and statuses as
+ * dlf_ffn_fused; bytes NULL: DLF_ERR_INVALID_ARG.  Host only. */
+dlf_status dlf_ffn_workspace_bytes(const dlf_ffn_desc *d, size_t *bytes);
+
+/* dlf_ffn_fused with a caller-owned workspace, which lets the block split d_ff
+ * where one workgroup per 32 or 64 tokens would stream the weights through
+ * too few CUs (with 8192 <= m < 16384, d_model <= 768 and d_ff >= 512): two
+ * workgroups share a 64-token block, each over half of d_ff, and write fp32
+ * partial sums of act(x W1^T + b1) W2^T to the workspace ([2][m][d_model]); a second
+ * kernel adds them, b2 and the residual and rounds y once (RNE).  The same
+ * result up to the order of the fp32 sums.
+ *   workspace        device, 16-byte aligned, at least dlf_ffn_workspace_bytes(d)
+ *                    bytes (else DLF_ERR_INVALID_ARG), overlapping no operand
+ *                    (DLF_ERR_ALIAS); may be NULL where that size is 0.  Its
+ *                    contents are scratch: calls that share one on overlapping
+ *                    streams race.
+ * Every other argument, check and status as dlf_ffn_fused. */
+dlf_status dlf_ffn_fused_ws(const dlf_ffn_desc *d, const void *x, const void *w1_packed,
+                            const float *b1, const void *w2_packed, const float *b2,
+                            const void *residual, void *y, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Host fusion pass: which chains of a graph become one fused launch        */

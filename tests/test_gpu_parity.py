@@ -1005,3 +1005,40 @@ def test_ffn_without_biases():
     torch.cuda.synchronize()
     err = oracle.rel_error(oracle.widen(host(L.y, "bf16"), "bf16"), ref)
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("split", ["1", "0"])
+def test_ffn_split_over_d_ff(split):
+    """The d_ff split (two workgroups a 64-token block, fp32 partial sums through the
+    workspace, a second kernel adding them with b2 and the residual), forced on and off
+    (DLF_FFN_SPLIT), on ragged token counts, every d_model it is built for and an odd number of
+    chunks (one and two a part); the workspace has a guard band.  Then without biases."""
+    cases = [dict(m=150, d_model=768, d_ff=768, act="gelu_tanh", residual=True),
+             dict(m=65, d_model=256, d_ff=512, act="relu", residual=False),
+             dict(m=300, d_model=512, d_ff=1280, act="gelu_erf", residual=True)]
+    d = dlf()
+    os.environ["DLF_FFN_SPLIT"] = split
+    try:
+        for i, kw in enumerate(cases):
+            wl = workloads.FfnWorkload(f"ffn_split{split}_{i}", seed=80 + i, **kw)
+            inp = workloads.generate(wl)
+            if i == 2:
+                inp["b1"] = np.zeros_like(inp["b1"])
+                inp["b2"] = np.zeros_like(inp["b2"])
+            ref = oracle.ffn(inp)
+            L = layers().make_layer(inp, with_unfused=False)
+            assert (L.ws_bytes == 2 * wl.m * wl.d_model * 4) == (split == "1"), L.ws_bytes
+            wbuf, ws = guarded((max(L.ws_bytes, 16),), torch.uint8)
+            case(f"ffn fused split={split} {wl} workspace={L.ws_bytes}")
+            buf, y = guarded((wl.m, wl.d_model), torch.bfloat16)
+            if i == 2:
+                d.dlf_ffn_fused_ws(L.desc, L.x, L.w1p, None, L.w2p, None, L.res, y, ws, L.ws_bytes)
+            else:
+                d.dlf_ffn_fused_ws(L.desc, L.x, L.w1p, L.b1, L.w2p, L.b2, L.res, y, ws, L.ws_bytes)
+            torch.cuda.synchronize()
+            assert guard_intact(buf, y.numel())
+            assert guard_intact(wbuf, ws.numel()), "write beyond the workspace"
+            err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
+            assert err <= TOL["bf16"], (split, i, err)
+    finally:
+        os.environ.pop("DLF_FFN_SPLIT", None)

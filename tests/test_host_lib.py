@@ -326,3 +326,31 @@ def test_ffn_validation_statuses():
     assert fused(dlf.ffn_desc(64, 768, 3072), r=Y) == dlf.DLF_ERR_ALIAS            # residual == y
     assert fused(dlf.ffn_desc(0, 768, 3072)) == dlf.DLF_OK                         # empty: no launch
     assert lib.dlf_ffn_fused(None, X, W1, None, W2, None, None, Y, 0) == dlf.DLF_ERR_INVALID_ARG
+
+
+@fake_pointers
+def test_ffn_workspace_size_and_checks():
+    """The d_ff split's workspace: 2 m d_model fp32 where the block splits (8192 <= m < 16384,
+    d_model <= 768, d_ff >= 512), else 0; too small, misaligned or overlapping workspaces are
+    refused before any launch."""
+    lib = dlf.raw()
+    ws = dlf.dlf_ffn_workspace_bytes
+    assert ws(dlf.ffn_desc(8192, 768, 3072)) == 2 * 8192 * 768 * 4
+    assert ws(dlf.ffn_desc(16383, 256, 512)) == 2 * 16383 * 256 * 4
+    for m, dm, dff in ((8191, 768, 3072), (16384, 768, 3072), (8192, 1024, 4096), (8192, 768, 256), (0, 768, 3072)):
+        assert ws(dlf.ffn_desc(m, dm, dff)) == 0, (m, dm, dff)
+    n = ctypes.c_size_t(7)
+    assert lib.dlf_ffn_workspace_bytes(ctypes.byref(dlf.ffn_desc(64, 640, 3072)), ctypes.byref(n)) \
+        == dlf.DLF_ERR_UNSUPPORTED and n.value == 0
+    assert lib.dlf_ffn_workspace_bytes(ctypes.byref(dlf.ffn_desc(64, 768, 3072)), None) == dlf.DLF_ERR_INVALID_ARG
+    X, W1, W2, Y, R, WS = 0x1000000, 0x2000000, 0x4000000, 0x6000000, 0x8000000, 0xA000000
+    d = dlf.ffn_desc(8192, 768, 3072)
+    need = ws(d)
+    run = lambda w, nbytes, d=d: lib.dlf_ffn_fused_ws(ctypes.byref(d), X, W1, None, W2, None, R, Y, w, nbytes, 0)
+    assert run(None, 0) == dlf.DLF_ERR_INVALID_ARG               # the split needs its workspace
+    assert run(WS, need - 16) == dlf.DLF_ERR_INVALID_ARG         # too small
+    assert run(WS + 8, need) == dlf.DLF_ERR_INVALID_ARG          # misaligned
+    assert run(Y - 64, need) == dlf.DLF_ERR_ALIAS                # overlaps y
+    assert run(R + 4096, need) == dlf.DLF_ERR_ALIAS              # overlaps the residual
+    small = dlf.ffn_desc(0, 768, 3072)
+    assert run(None, 0, d=small) == dlf.DLF_OK                   # empty: no launch
