@@ -280,11 +280,18 @@ def cpu_baseline(inp, budget_s: float):
         if inp.get("residual") is not None:
             sub["residual"] = inp["residual"][:imgs]
         sub["workload"] = dataclasses.replace(wl, n=imgs)
+        # the whole workload can take well under the budget: then repeat it (at most 20 passes
+        # in all) so that the time is not one short, noisy pass
         t0 = time.perf_counter()
         oracle.conv_bn_act(sub)
-        dt = time.perf_counter() - t0
+        first = time.perf_counter() - t0
+        passes = 1 + int(max(0, min(19, (budget_s - t1 - first) / max(first, 1e-6))))
+        for _ in range(passes - 1):
+            oracle.conv_bn_act(sub)
+        total_s = time.perf_counter() - t0
+        dt = total_s / passes
         frac = imgs / wl.n
-        sample = f"{imgs} of {wl.n} images (full conv+BN+act per image)"
+        sample = f"{imgs} of {wl.n} images (full conv+BN+act per image)" + (f", {passes} passes" if passes > 1 else "")
     else:
         rows = max(1, min(m, 64))
         t0 = time.perf_counter()
@@ -293,10 +300,11 @@ def cpu_baseline(inp, budget_s: float):
         else:
             oracle.fp8_gemm_bn_relu_quant(inp, rows=np.arange(rows))
         dt = time.perf_counter() - t0
+        total_s = dt
         frac = rows / m
         sample = f"{rows} of {m} rows"
     return {"value": fl_total * frac / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+            "kind": "oracle", "sample": sample, "seconds": round(total_s, 3)}
 
 
 def main():
