@@ -19,8 +19,8 @@ widened rows: QKV split store, GELU-erf epilogue, FFN, ResNet stem and stage, wi
 unfused comparisons) and writes the per-kernel averages to kernels__widened_rows.md.
 
 Usage (on a machine with the GPU):
-  python -m dl_fusion_amd.rocprof --workloads 1 2 3 4 --out profiles --scratch gpurun_out/rocprof
-  python -m dl_fusion_amd.rocprof --widened-rows --out profiles --scratch gpurun_out/rocprof
+  python -m dl_fusion_amd.rocprof --workloads 1 2 3 4 --out profiles --scratch /tmp/rocprof
+  python -m dl_fusion_amd.rocprof --widened-rows --out profiles --scratch /tmp/rocprof
 """
 from __future__ import annotations
 
@@ -179,7 +179,7 @@ def main() -> None:
     ap.add_argument("--workloads", type=int, nargs="+", default=[1])
     ap.add_argument("--steps", type=int, default=20, help="timed launches in the trace pass")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
-    ap.add_argument("--scratch", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    ap.add_argument("--scratch", default="/tmp/rocprof")
     ap.add_argument("--passes", nargs="+", default=["trace", "fetch", "write", "mfma"])
     ap.add_argument("--widened-rows", action="store_true", help="trace a whole bench.py run instead")
     args = ap.parse_args()
