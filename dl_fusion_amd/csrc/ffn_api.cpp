@@ -99,10 +99,13 @@ dlf_status check_ffn(const dlf_ffn_desc* d, const void* x, const void* w1_packed
     return ok();
 }
 
-// bytes of the d_ff split's partial sums, 0 where the block does not split
+// parts of the d_ff split, and the bytes of their partial sums (0 where the block does not split)
+int ffn_split(const dlf_ffn_desc* d) {
+    return dlf::ffn_parts(d->m, static_cast<int>(d->d_model), static_cast<int>(d->d_ff));
+}
 size_t ffn_ws_bytes(const dlf_ffn_desc* d) {
-    if (dlf::ffn_parts(d->m, static_cast<int>(d->d_model), static_cast<int>(d->d_ff)) != 2) return 0;
-    return static_cast<size_t>(2 * d->m * d->d_model) * 4;
+    const int parts = ffn_split(d);
+    return parts > 1 ? static_cast<size_t>(parts * d->m * d->d_model) * 4 : 0;
 }
 
 }  // namespace
@@ -152,7 +155,7 @@ extern "C" dlf_status dlf_ffn_fused_ws(const dlf_ffn_desc* d, const void* x, con
             overlaps(workspace, need, b1, static_cast<size_t>(d->d_ff) * 4) ||
             overlaps(workspace, need, b2, static_cast<size_t>(d->d_model) * 4))
             return fail(DLF_ERR_ALIAS, "workspace overlaps an operand");
-        a.parts = 2;
+        a.parts = ffn_split(d);
         a.ws = static_cast<float*>(workspace);
     }
     const hipError_t e = dlf::launch_ffn(a, act, static_cast<hipStream_t>(stream));

@@ -43,10 +43,11 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 // DB: 32-column output blocks per wave (d_model = 256 DB); FT: 32-token fragments per
 // workgroup.  With FT = 2 the weights are read once per 64 tokens (half the L2 traffic of
 // FT = 1) and the h buffer is single (LDS), which costs a second barrier per chunk.
-// SPL = 2: workgroup 2 b + part takes token block b and the chunks of its half of d_ff, and
-// writes its fp32 partial sum of y (no bias, no residual) to p.ws[part]; ffn_reduce_kernel
-// finishes y.  Each workgroup then streams half the weights for its tokens.
-template <int ACT, int DB, int FT, int SPL>
+// SPL: d_ff split into S = p.parts parts: workgroup S b + part takes token block b and the
+// chunks [part nchunks / S, (part + 1) nchunks / S), and writes its fp32 partial sum of y (no
+// bias, no residual) to p.ws[part]; ffn_reduce_kernel finishes y.  Each workgroup then
+// streams 1/S of the weights for its tokens.
+template <int ACT, int DB, int FT, bool SPL>
 __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     // weight fragments in flight per wave: the stream is latency-bound, so as many as the
     // registers allow (4 a fragment beside the FT x DB accumulators)
@@ -63,11 +64,12 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     static_assert(QN % kRing == 0, "the ring index repeats from chunk to chunk");
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, tok = lane & 31;
-    const int part = SPL == 2 ? static_cast<int>(blockIdx.x & 1u) : 0;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x / SPL) * TOK;
+    const int S = SPL ? p.parts : 1;
+    const int part = static_cast<int>(blockIdx.x % static_cast<unsigned>(S));
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x / static_cast<unsigned>(S)) * TOK;
     const int F = p.F;
     const int nchunks = F / kChunk;
-    const int cbeg = part * nchunks / SPL, cend = (part + 1) * nchunks / SPL;   // this part's chunks
+    const int cbeg = part * nchunks / S, cend = (part + 1) * nchunks / S;   // this part's chunks (S <= nchunks)
 
     // ---- x rows m0 .. m0+TOK-1 into LDS (zero past M) ----
     for (int i = tid; i < TOK * (D / 8); i += 512) {
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc2[b][f][4 * g + e];
-                if constexpr (SPL == 2) {
+                if constexpr (SPL) {
                     *reinterpret_cast<f32x4_t*>(p.ws + (part * p.M + m) * D + col) = f32x4_t{v[0], v[1], v[2], v[3]};
                     continue;
                 }
@@ -213,7 +215,8 @@ __global__ __launch_bounds__(512, 1) void ffn_kernel(const FfnArgs p) {
     }
 }
 
-// y = bf16(ws[0] + ws[1] + b2 [+ residual]), 8 columns a thread (D is a multiple of 256)
+// y = bf16(ws[0] + ... + ws[parts-1] + b2 [+ residual]), 8 columns a thread (D is a
+// multiple of 256)
 __global__ __launch_bounds__(256) void ffn_reduce_kernel(const FfnArgs p) {
     const int64_t groups = p.M * (p.D / 8);
     const int64_t half = p.M * p.D;
@@ -225,10 +228,16 @@ __global__ __launch_bounds__(256) void ffn_reduce_kernel(const FfnArgs p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.ws + off + 4 * h);
-            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p.ws + half + off + 4 * h);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * h + e] = a[e] + b[e];
+            for (int e = 0; e < 4; ++e) v[4 * h + e] = a[e];
         }
+        for (int q = 1; q < p.parts; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.ws + q * half + off + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * h + e] += a[e];
+            }
         if (p.b2) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -250,9 +259,9 @@ __global__ __launch_bounds__(256) void ffn_reduce_kernel(const FfnArgs p) {
     }
 }
 
-template <int ACT, int FT, int SPL>
+template <int ACT, int FT, bool SPL>
 hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
-    const int64_t blocks = (a.M + 32 * FT - 1) / (32 * FT) * SPL;
+    const int64_t blocks = (a.M + 32 * FT - 1) / (32 * FT) * (SPL ? a.parts : 1);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks));
     switch (a.D) {
@@ -260,7 +269,7 @@ hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
         case 512: hipLaunchKernelGGL((ffn_kernel<ACT, 2, FT, SPL>), grid, dim3(512), 0, s, a); break;
         case 768: hipLaunchKernelGGL((ffn_kernel<ACT, 3, FT, SPL>), grid, dim3(512), 0, s, a); break;
         case 1024:
-            if constexpr (FT == 1) {   // 64 tokens of 1024 columns do not fit LDS beside h
+            if constexpr (FT == 1 && !SPL) {   // 64 tokens of 1024 columns do not fit LDS beside h; no split
                 hipLaunchKernelGGL((ffn_kernel<ACT, 4, FT, SPL>), grid, dim3(512), 0, s, a);
                 break;
             } else {
@@ -268,7 +277,7 @@ hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
             }
         default: return hipErrorInvalidValue;
     }
-    if constexpr (SPL == 2) {
+    if constexpr (SPL) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t groups = a.M * (a.D / 8);
@@ -278,37 +287,47 @@ hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// 64 tokens per workgroup (half the weight traffic) once that still gives a workgroup per CU
-// (256 of them), else 32; d_model 1024 always takes 32.  DLF_FFN_TOK=32|64 forces one (tests).
-// Split over d_ff (parts == 2): 64 tokens and half of d_ff per workgroup.
+// 64 tokens per workgroup (half the weight traffic) from 8192 tokens (with d_ff split below
+// 16384, unsplit from there), else 32; d_model 1024 always takes 32.  DLF_FFN_TOK=32|64
+// forces one (tests).
 template <int ACT>
 hipError_t launch_act(const FfnArgs& a, hipStream_t s) {
-    if (a.parts == 2) return launch_d<ACT, 2, 2>(a, s);
-    int tok = a.M >= 64 * 256 && a.D <= 768 ? 64 : 32;
+    int tok = a.M >= (a.parts > 1 ? 64 * 128 : 64 * 256) && a.D <= 768 ? 64 : 32;
     if (const char* env = std::getenv("DLF_FFN_TOK")) {
         const int t = std::atoi(env);
         if (t == 32 || (t == 64 && a.D <= 768)) tok = t;
     }
-    return tok == 64 ? launch_d<ACT, 2, 1>(a, s) : launch_d<ACT, 1, 1>(a, s);
+    if (a.parts > 1) return tok == 64 ? launch_d<ACT, 2, true>(a, s) : launch_d<ACT, 1, true>(a, s);
+    return tok == 64 ? launch_d<ACT, 2, false>(a, s) : launch_d<ACT, 1, false>(a, s);
 }
 
 }  // namespace
 
 int ffn_parts(int64_t M, int D, int F) {
-    // built for d_model <= 768 and at least two chunks of d_ff; taken where 64-token blocks
-    // give fewer than 256 workgroups unsplit and at least 256 split (8192 <= M < 16384)
-    const bool can = D <= 768 && F / kChunk >= 2;
+    // built for d_model <= 768 (and S <= the chunks of d_ff).  Every workgroup streams its
+    // part of the weights from L2 at a rate of its own CU until about 160 CUs together reach
+    // the L2's rate (measured: 32 to 188 token blocks unsplit take the same 107-112 us on
+    // BERT-base, 12 chunks; 256 workgroups of 6 chunks 80 us).  So: split only below 160
+    // token blocks, into as many parts as fit one round of 256 workgroups.
+    const int nchunks = F / kChunk;
+    if (D > 768 || nchunks < 2 || M <= 0) return 1;
     if (const char* env = std::getenv("DLF_FFN_SPLIT")) {
-        if (std::atoi(env) == 0) return 1;
-        if (std::atoi(env) == 1 && can) return 2;
+        const int want = std::atoi(env);
+        if (want == 0 || want == 1) return 1;
+        if (want > 1) return want < nchunks ? want : nchunks;
     }
-    return can && M >= 64 * 128 && M < 64 * 256 ? 2 : 1;
+    if (M >= 64 * 256) return 1;
+    const int64_t tok = M >= 64 * 128 ? 64 : 32;
+    const int64_t blocks = (M + tok - 1) / tok;
+    if (blocks >= 160) return 1;
+    const int64_t fit = 256 / blocks;
+    return static_cast<int>(fit < nchunks ? fit : nchunks);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, int act, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     if (a.F <= 0 || a.F % kChunk != 0) return hipErrorInvalidValue;
-    if (a.parts == 2 && (!a.ws || a.D > 768 || a.F / kChunk < 2)) return hipErrorInvalidValue;
+    if (a.parts > 1 && (!a.ws || a.D > 768 || a.parts > a.F / kChunk)) return hipErrorInvalidValue;
     switch (act) {
         case kActNone: return launch_act<kActNone>(a, s);
         case kActRelu: return launch_act<kActRelu>(a, s);

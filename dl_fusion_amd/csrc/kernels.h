@@ -145,13 +145,13 @@ struct FfnArgs {
     uint16_t* y;            // [M][D]
     int64_t M;
     int D, F;               // D in {256, 512, 768, 1024}; F a positive multiple of 256
-    // parts == 2: two workgroups a 64-token block, each over half of d_ff, write fp32 partial
-    // sums of y to ws [2][M][D], which a second kernel adds with b2 and the residual
+    // parts S > 1: S workgroups a token block, each over 1/S of d_ff, write fp32 partial sums
+    // of y to ws [S][M][D], which a second kernel adds with b2 and the residual
     int parts;
     float* ws;
 };
-// the d_ff parts the fused FFN splits into for these sizes (1 or 2); DLF_FFN_SPLIT=0|1
-// forces one where both are built
+// the d_ff parts the fused FFN splits into for these sizes (1 = no split); DLF_FFN_SPLIT=<S>
+// forces S (0 or 1: no split) where a split is built
 int ffn_parts(int64_t M, int D, int F);
 hipError_t launch_ffn(const FfnArgs& args, int act, hipStream_t stream);
 

@@ -333,11 +333,11 @@ dlf_status dlf_ffn_workspace_bytes(const dlf_ffn_desc *d, size_t *bytes);
 
 /* dlf_ffn_fused with a caller-owned workspace, which lets the block split d_ff
  * where one workgroup per 32 or 64 tokens would stream the weights through
- * too few CUs (with 8192 <= m < 16384, d_model <= 768 and d_ff >= 512): two
- * workgroups share a 64-token block, each over half of d_ff, and write fp32
- * partial sums of act(x W1^T + b1) W2^T to the workspace ([2][m][d_model]); a second
- * kernel adds them, b2 and the residual and rounds y once (RNE).  The same
- * result up to the order of the fp32 sums.
+ * too few CUs (fewer than 160 token blocks, d_model <= 768, d_ff >= 512): S
+ * workgroups share a token block, each over 1/S of d_ff, and write fp32
+ * partial sums of act(x W1^T + b1) W2^T to the workspace ([S][m][d_model]); a
+ * second kernel adds them, b2 and the residual and rounds y once (RNE).  The
+ * same result up to the order of the fp32 sums.
  *   workspace        device, 16-byte aligned, at least dlf_ffn_workspace_bytes(d)
  *                    bytes (else DLF_ERR_INVALID_ARG), overlapping no operand
  *                    (DLF_ERR_ALIAS); may be NULL where that size is 0.  Its

@@ -1007,29 +1007,33 @@ def test_ffn_without_biases():
     assert err <= TOL["bf16"], err
 
 
-@pytest.mark.parametrize("split", ["1", "0"])
+@pytest.mark.parametrize("split", ["2", "3", "0", "auto"])
 def test_ffn_split_over_d_ff(split):
-    """The d_ff split (two workgroups a 64-token block, fp32 partial sums through the
-    workspace, a second kernel adding them with b2 and the residual), forced on and off
-    (DLF_FFN_SPLIT), on ragged token counts, every d_model it is built for and an odd number of
-    chunks (one and two a part); the workspace has a guard band.  Then without biases."""
+    """The d_ff split (S workgroups a token block, fp32 partial sums through the workspace, a
+    second kernel adding them with b2 and the residual): forced to 2 and 3 parts, off
+    (DLF_FFN_SPLIT), and the library's own choice (as many parts as fit 256 workgroups, at
+    most one a chunk), on ragged token counts, every d_model it is built for and chunk counts that do
+    not divide evenly; the workspace has a guard band.  The third case has no biases."""
     cases = [dict(m=150, d_model=768, d_ff=768, act="gelu_tanh", residual=True),
              dict(m=65, d_model=256, d_ff=512, act="relu", residual=False),
              dict(m=300, d_model=512, d_ff=1280, act="gelu_erf", residual=True)]
     d = dlf()
-    os.environ["DLF_FFN_SPLIT"] = split
+    if split != "auto":
+        os.environ["DLF_FFN_SPLIT"] = split
     try:
         for i, kw in enumerate(cases):
             wl = workloads.FfnWorkload(f"ffn_split{split}_{i}", seed=80 + i, **kw)
+            nchunks = wl.d_ff // 256
+            parts = {"0": 1, "auto": min(256 // -(-wl.m // 32), nchunks)}.get(split) or min(int(split), nchunks)
             inp = workloads.generate(wl)
             if i == 2:
                 inp["b1"] = np.zeros_like(inp["b1"])
                 inp["b2"] = np.zeros_like(inp["b2"])
             ref = oracle.ffn(inp)
             L = layers().make_layer(inp, with_unfused=False)
-            assert (L.ws_bytes == 2 * wl.m * wl.d_model * 4) == (split == "1"), L.ws_bytes
+            assert L.ws_bytes == (parts * wl.m * wl.d_model * 4 if parts > 1 else 0), (L.ws_bytes, parts)
             wbuf, ws = guarded((max(L.ws_bytes, 16),), torch.uint8)
-            case(f"ffn fused split={split} {wl} workspace={L.ws_bytes}")
+            case(f"ffn fused split={split} parts={parts} {wl}")
             buf, y = guarded((wl.m, wl.d_model), torch.bfloat16)
             if i == 2:
                 d.dlf_ffn_fused_ws(L.desc, L.x, L.w1p, None, L.w2p, None, L.res, y, ws, L.ws_bytes)
