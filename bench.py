@@ -224,7 +224,9 @@ def run_next_rows(torch, steps: int, warmup: int, eager: bool):
     torch.cuda.empty_cache()
     for key, wl in (("f4_ffn_back_to_back", workloads.FFN_BERT_BASE),
                     ("f4_ffn_back_to_back_16k", dataclasses.replace(
-                        workloads.FFN_BERT_BASE, name="ffn_bf16_16384x768x3072_bias_gelu_tanh_residual", m=16384))):
+                        workloads.FFN_BERT_BASE, name="ffn_bf16_16384x768x3072_bias_gelu_tanh_residual", m=16384)),
+                    ("f4_ffn_back_to_back_128", dataclasses.replace(
+                        workloads.FFN_BERT_BASE, name="ffn_bf16_128x768x3072_bias_gelu_tanh_residual", m=128))):
         inp = workloads.generate(wl)
         L = make_layer(inp, with_unfused=True)
         ms = timer(torch, L.forward, steps, warmup)
