@@ -287,12 +287,12 @@ hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// 64 tokens per workgroup (half the weight traffic) from 8192 tokens (with d_ff split below
-// 16384, unsplit from there), else 32; d_model 1024 always takes 32.  DLF_FFN_TOK=32|64
-// forces one (tests).
+// 64 tokens per workgroup (half the weight traffic): split, from 4096 tokens (measured 1.15-
+// 1.2x faster than 32 there, 0.8x at 128-2048); unsplit, from 16384 (where 64-token blocks
+// still fill the CUs).  d_model 1024 always takes 32.  DLF_FFN_TOK=32|64 forces one (tests).
 template <int ACT>
 hipError_t launch_act(const FfnArgs& a, hipStream_t s) {
-    int tok = a.M >= (a.parts > 1 ? 64 * 128 : 64 * 256) && a.D <= 768 ? 64 : 32;
+    int tok = a.M >= (a.parts > 1 ? 4096 : 64 * 256) && a.D <= 768 ? 64 : 32;
     if (const char* env = std::getenv("DLF_FFN_TOK")) {
         const int t = std::atoi(env);
         if (t == 32 || (t == 64 && a.D <= 768)) tok = t;
@@ -317,7 +317,7 @@ int ffn_parts(int64_t M, int D, int F) {
         if (want > 1) return want < nchunks ? want : nchunks;
     }
     if (M >= 64 * 256) return 1;
-    const int64_t tok = M >= 64 * 128 ? 64 : 32;
+    const int64_t tok = M >= 4096 ? 64 : 32;                     // as launch_act takes for a split
     const int64_t blocks = (M + tok - 1) / tok;
     if (blocks >= 160) return 1;
     const int64_t fit = 256 / blocks;

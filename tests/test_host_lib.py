@@ -331,17 +331,20 @@ def test_ffn_validation_statuses():
 @fake_pointers
 def test_ffn_workspace_size_and_checks():
     """The d_ff split's workspace: S m d_model fp32 where the block splits into S parts (below
-    16384 tokens, d_model <= 768, fewer than 160 token blocks of 64 from 8192 tokens, else of
+    16384 tokens, d_model <= 768, fewer than 160 token blocks of 64 from 4096 tokens, else of
     32: as many parts as fit 256 workgroups, at most one a chunk of 256 features), else 0; too
     small, misaligned or overlapping workspaces are refused before any launch."""
     lib = dlf.raw()
     ws = dlf.dlf_ffn_workspace_bytes
     assert ws(dlf.ffn_desc(8192, 768, 3072)) == 2 * 8192 * 768 * 4        # 128 blocks of 64
-    assert ws(dlf.ffn_desc(4096, 768, 3072)) == 2 * 4096 * 768 * 4        # 128 blocks of 32
+    assert ws(dlf.ffn_desc(8191, 768, 3072)) == 2 * 8191 * 768 * 4        # 128 blocks of 64
+    assert ws(dlf.ffn_desc(4096, 768, 3072)) == 4 * 4096 * 768 * 4        # 64 blocks of 64
+    assert ws(dlf.ffn_desc(6000, 768, 3072)) == 2 * 6000 * 768 * 4        # 94 blocks of 64
+    assert ws(dlf.ffn_desc(4095, 768, 3072)) == 2 * 4095 * 768 * 4        # 128 blocks of 32
     assert ws(dlf.ffn_desc(1000, 512, 2048)) == 8 * 1000 * 512 * 4        # 32 blocks: 8 parts
     assert ws(dlf.ffn_desc(128, 768, 3072)) == 12 * 128 * 768 * 4         # 4 blocks: 64, at most 12
     assert ws(dlf.ffn_desc(1, 256, 512)) == 2 * 1 * 256 * 4
-    for m, dm, dff in ((8191, 768, 3072), (6000, 768, 3072), (16383, 256, 512), (16384, 768, 3072), (8192, 1024, 4096),
+    for m, dm, dff in ((10240, 768, 3072), (16383, 256, 512), (16384, 768, 3072), (8192, 1024, 4096),
                        (100, 1024, 4096), (8192, 768, 256), (0, 768, 3072)):
         assert ws(dlf.ffn_desc(m, dm, dff)) == 0, (m, dm, dff)
     n = ctypes.c_size_t(7)
