@@ -26,6 +26,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -40,33 +41,45 @@ int orc_num_threads(void)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Convolution: direct definition.                                           */
-/* [INFR] §3.3 (the per-output convolution loop: accumulate over input        */
-/* channels and kernel taps, skip taps that fall outside the image, i.e. zero */
-/* padding, optional bias added to the accumulator).  Layout here is NHWC for */
-/* x and y and OHWI for the weights; only the indexing differs from the page. */
+/* Convolution: the definition of a zero-padded, strided 2-D convolution,     */
+/* the operator [INFR] §3.3 computes (zero padding, optional bias):           */
+/*   y[b][oh][ow][co] = sum_{r<kh} sum_{s<kw} sum_{ci<cin}                     */
+/*       xpad[b][oh*sh + r][ow*sw + s][ci] * wt[co][r][s][ci]  (+ bias[co])    */
+/* where xpad is x with ph zero rows above and below and pw zero columns on   */
+/* each side.  NHWC x and y, OHWI weights.  xpad is never built: padded_row() */
+/* gives its cin values at one position, the shared zero row outside x.       */
 /* ------------------------------------------------------------------------ */
+static const double *padded_row(const double *x, const double *zeros, int64_t h, int64_t w,
+                                int64_t cin, int64_t ph, int64_t pw, int64_t b, int64_t i, int64_t j)
+{
+    const int64_t xi = i - ph, xj = j - pw;
+    const int inside = xi >= 0 && xi < h && xj >= 0 && xj < w;
+    return inside ? x + ((b * h + xi) * w + xj) * cin : zeros;
+}
+
 static double conv_point(int64_t h, int64_t w, int64_t cin, int64_t kh, int64_t kw,
                          int64_t sh, int64_t sw, int64_t ph, int64_t pw,
-                         const double *x, const double *wt, const double *bias,
+                         const double *x, const double *zeros, const double *wt, const double *bias,
                          int64_t b, int64_t oh, int64_t ow, int64_t co)
 {
-    double acc = bias ? bias[co] : 0.0;
-    for (int64_t r = 0; r < kh; ++r) {
-        const int64_t hi = oh * sh - ph + r;
-        if (hi < 0 || hi >= h)
-            continue;
+    double sum = 0.0;
+    for (int64_t r = 0; r < kh; ++r)
         for (int64_t s = 0; s < kw; ++s) {
-            const int64_t wi = ow * sw - pw + s;
-            if (wi < 0 || wi >= w)
-                continue;
-            const double *xp = x + ((b * h + hi) * w + wi) * cin;
+            const double *xp = padded_row(x, zeros, h, w, cin, ph, pw, b, oh * sh + r, ow * sw + s);
             const double *wp = wt + ((co * kh + r) * kw + s) * cin;
             for (int64_t ci = 0; ci < cin; ++ci)
-                acc += xp[ci] * wp[ci];
+                sum += xp[ci] * wp[ci];
         }
-    }
-    return acc;
+    return bias ? sum + bias[co] : sum;
+}
+
+/* cin zeros: the value of xpad outside x */
+static double *zero_row(int64_t cin)
+{
+    double *z = calloc((size_t)(cin > 0 ? cin : 1), sizeof(double));
+    if (!z)
+        abort();
+    return z;
 }
 
 /* y[n][ho][wo][cout] = conv(x[n][h][w][cin], wt[cout][kh][kw][cin]) (+ bias). */
@@ -76,14 +89,16 @@ void orc_conv2d_nhwc(int64_t n, int64_t h, int64_t w, int64_t cin, int64_t cout,
 {
     const int64_t ho = (h + 2 * ph - kh) / sh + 1;
     const int64_t wo = (w + 2 * pw - kw) / sw + 1;
+    double *zeros = zero_row(cin);
     #pragma omp parallel for schedule(static)
     for (int64_t row = 0; row < n * ho; ++row) {
         const int64_t b = row / ho, oh = row % ho;
         for (int64_t ow = 0; ow < wo; ++ow)
             for (int64_t co = 0; co < cout; ++co)
                 y[((b * ho + oh) * wo + ow) * cout + co] =
-                    conv_point(h, w, cin, kh, kw, sh, sw, ph, pw, x, wt, bias, b, oh, ow, co);
+                    conv_point(h, w, cin, kh, kw, sh, sw, ph, pw, x, zeros, wt, bias, b, oh, ow, co);
     }
+    free(zeros);
 }
 
 /* The same convolution evaluated only at the output pixels pts[i] = (n, ho, wo);
@@ -93,11 +108,13 @@ void orc_conv2d_nhwc_at(int64_t h, int64_t w, int64_t cin, int64_t cout,
                         const double *x, const double *wt, const double *bias,
                         int64_t npts, const int64_t *pts, double *y)
 {
+    double *zeros = zero_row(cin);
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < npts; ++i)
         for (int64_t co = 0; co < cout; ++co)
-            y[i * cout + co] = conv_point(h, w, cin, kh, kw, sh, sw, ph, pw, x, wt, bias,
+            y[i * cout + co] = conv_point(h, w, cin, kh, kw, sh, sw, ph, pw, x, zeros, wt, bias,
                                           pts[3 * i], pts[3 * i + 1], pts[3 * i + 2], co);
+    free(zeros);
 }
 
 /* ------------------------------------------------------------------------ */
