@@ -22,8 +22,25 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 # amplified by the channel's BN scale, so the chain gets twice the fused tolerance.
 TOL_UNFUSED = {"f32": 1e-4, "bf16": 4e-2}
 GUARD = 4096
-CONV_TILES = (0, 1, 2, 3, 4, 5)                  # tile shapes shared by conv and GEMM
-GEMM_TILES = CONV_TILES + tuple(range(6, 16))    # plus the dense-GEMM pipeline variants
+CONV_TILES = (1, 2, 3)                 # the implicit GEMM's tiles: 128x128, 128x64, 64x64
+GEMM_TILES = (0,) + CONV_TILES         # plus the dense GEMM's eight-wave 256x256
+
+
+class _TuningEnv:
+    """The DLF_* tuning switches: the library reads them once when it loads, so every change
+    of the environment here is followed by dlf_tuning_reload()."""
+
+    def __setitem__(self, key, val):
+        os.environ[key] = val
+        dlf().dlf_tuning_reload()
+
+    def pop(self, key, default=None):
+        r = os.environ.pop(key, default)
+        dlf().dlf_tuning_reload()
+        return r
+
+
+ENV = _TuningEnv()
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -33,8 +50,8 @@ def _gpu():
     import dl_fusion_amd  # noqa: F401  (loud failure if the library is missing)
     torch.cuda.set_device(0)
     yield
-    os.environ.pop("DLF_TILE", None)
-    os.environ.pop("DLF_CONV", None)
+    ENV.pop("DLF_TILE", None)
+    ENV.pop("DLF_CONV", None)
 
 
 def dlf():
@@ -86,9 +103,9 @@ def set_route(conv, tile):
     kernel instead of any halo kernel; tile: force an MFMA tile of the implicit GEMM."""
     for key, val in (("DLF_CONV", conv), ("DLF_TILE", None if tile is None else str(tile))):
         if val is None:
-            os.environ.pop(key, None)
+            ENV.pop(key, None)
         else:
-            os.environ[key] = val
+            ENV[key] = val
 
 
 def check_conv(wl, tiles=(), unfused=True):
@@ -185,9 +202,9 @@ def test_bf16_strided_1x1_streaming_route(i):
         for gemm, conv, nb in routes:
             for key, val in (("DLF_GEMM", gemm), ("DLF_CONV", conv), ("DLF_STREAM_NB", nb)):
                 if val is None:
-                    os.environ.pop(key, None)
+                    ENV.pop(key, None)
                 else:
-                    os.environ[key] = val
+                    ENV[key] = val
             case(f"conv_fused {wl} gemm={gemm} conv={conv} block={nb}")
             buf, y = guarded(L.out_shape, torch.bfloat16)
             L.forward(y=y)
@@ -197,7 +214,7 @@ def test_bf16_strided_1x1_streaming_route(i):
             assert err <= TOL["bf16"], (wl, gemm, conv, nb, err)
     finally:
         for key in ("DLF_GEMM", "DLF_CONV", "DLF_STREAM_NB"):
-            os.environ.pop(key, None)
+            ENV.pop(key, None)
 
 # Any number of input channels (Cin % 8 != 0): the implicit GEMM gathers both operands value
 # by value.  The stem geometry (7x7, stride 2, pad 3, three channels), a ragged K of 27, one
@@ -233,7 +250,7 @@ SMALLC_BF16 = [
 @pytest.mark.parametrize("i", range(len(SMALLC_BF16)))
 def test_bf16_conv_small_channel_kernel(i):
     wl = workloads.workload(1, conv_bias=bool(i % 2), **SMALLC_BF16[i])
-    check_conv(wl, tiles=(4,), unfused=(i < 2))
+    check_conv(wl, tiles=(2,), unfused=(i < 2))
 
 
 def test_resnet_stem_full_size_sampled():
@@ -330,12 +347,13 @@ def gemm_reference(inp, rows, residual=None):
 
 
 def sample_rows(m, tile=256, extra=40, seed=0):
+    """Rows 0, 1, m-2, m-1, both rows at every tile edge, and `extra` random rows."""
     rng = np.random.default_rng(seed)
     edges = {0, 1, m - 1, m - 2}
     for t in range(tile, m, tile):
         edges.update({t - 1, t})
-    edges = sorted(r for r in edges if 0 <= r < m)[:24]
-    return np.array(sorted(set(edges) | set(rng.choice(m, min(extra, m), replace=False).tolist())))
+    edges = {r for r in edges if 0 <= r < m}
+    return np.array(sorted(edges | set(rng.choice(m, min(extra, m), replace=False).tolist())))
 
 
 def test_config3_bf16_gemm_bias_gelu_full_size_sampled():
@@ -383,9 +401,9 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
     res_d = layers().to_device(res, "bf16") if res is not None else None
     for tile in (None,) + GEMM_TILES:
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"gemm_fused {wl} tile={tile} residual={res is not None}")
         buf, y = guarded((wl.m, wl.n), torch.bfloat16)
         L.forward(y=y, residual=res_d)
@@ -393,7 +411,7 @@ def test_bf16_gemm_ragged_shapes_every_tile(i):
         assert guard_intact(buf, y.numel())
         err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
         assert err <= TOL["bf16"], (wl, tile, err)
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
     if res is None:
         case(f"gemm_unfused {wl}")
         yu = L.forward_unfused()
@@ -443,9 +461,9 @@ def test_bf16_gemm_streaming_route(i, res):
     try:
         for route in ("stream", "tiled", None):
             if route is None:
-                os.environ.pop("DLF_GEMM", None)
+                ENV.pop("DLF_GEMM", None)
             else:
-                os.environ["DLF_GEMM"] = route
+                ENV["DLF_GEMM"] = route
             case(f"gemm_fused {wl} route={route} residual={res}")
             buf, y = guarded((wl.m, wl.n), torch.bfloat16)
             L.forward(y=y, residual=r_d)
@@ -454,7 +472,7 @@ def test_bf16_gemm_streaming_route(i, res):
             err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
             assert err <= TOL["bf16"], (wl, route, err)
     finally:
-        os.environ.pop("DLF_GEMM", None)
+        ENV.pop("DLF_GEMM", None)
 
 
 
@@ -467,8 +485,8 @@ def test_bf16_gemm_streaming_forced_block_width(nb, n, k):
     ref = gemm_reference(inp, np.arange(wl.m), r)
     L = layers().make_layer(inp, with_unfused=False)
     r_d = layers().to_device(r, "bf16")
-    os.environ["DLF_GEMM"] = "stream"
-    os.environ["DLF_STREAM_NB"] = str(nb)
+    ENV["DLF_GEMM"] = "stream"
+    ENV["DLF_STREAM_NB"] = str(nb)
     try:
         case(f"gemm_fused {wl} route=stream block={nb} residual=True")
         buf, y = guarded((wl.m, wl.n), torch.bfloat16)
@@ -478,8 +496,8 @@ def test_bf16_gemm_streaming_forced_block_width(nb, n, k):
         err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
         assert err <= TOL["bf16"], (wl, nb, err)
     finally:
-        os.environ.pop("DLF_GEMM", None)
-        os.environ.pop("DLF_STREAM_NB", None)
+        ENV.pop("DLF_GEMM", None)
+        ENV.pop("DLF_STREAM_NB", None)
 
 # Rows of 8 MB or more are past the 32-bit offsets of the buffer-resource loads: the library
 # reads them with 64-bit global addresses and the basic tiles (a tuned tile falls back to
@@ -513,11 +531,11 @@ def test_gemm_rows_past_the_buffer_range(i):
     rows = np.arange(wl.m)
     ref = gemm_reference(inp, rows) if idx == 3 else fp8_reference(inp, rows)[0]
     L = layers().make_layer(inp, with_unfused=False)
-    for tile in (None, 12, 1):
+    for tile in (None, 0, 1):
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"wide-row gemm {wl} tile={tile}")
         dt = torch.bfloat16 if idx == 3 else torch.uint8
         buf, y = guarded((wl.m, wl.n), dt)
@@ -529,7 +547,7 @@ def test_gemm_rows_past_the_buffer_range(i):
             assert err <= TOL["bf16"], (tile, err)
         else:
             assert_codes_within_one(host(y, "fp8"), ref)
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
 
 
 # ---------------------------------------------------------------------------
@@ -553,9 +571,9 @@ def test_bf16_gemm_split_store_every_tile(i):
     pc = wl.n // parts
     for tile in (None,) + GEMM_TILES:
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"gemm_fused_split {wl} parts={parts} tile={tile}")
         outs = [guarded((wl.m, pc), torch.bfloat16) for _ in range(parts)]
         dlf().dlf_gemm_fused_split(L.desc, L.x, L.w, None, L.bias, [y for _, y in outs])
@@ -564,7 +582,7 @@ def test_bf16_gemm_split_store_every_tile(i):
             assert guard_intact(buf, y.numel()), p
             err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
             assert err <= TOL["bf16"], (tile, p, err)
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
 
 
 # ---------------------------------------------------------------------------
@@ -589,9 +607,9 @@ def test_bf16_gemm_gated_every_tile(i):
     desc = d.gemm_desc(wl.m, wl.n, wl.k, "bf16", "bf16", "none")
     for tile in (None,) + GEMM_TILES:
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"gemm_fused_gated {gate} {wl} tile={tile}")
         buf, y = guarded((wl.m, wl.n // 2), torch.bfloat16)
         d.dlf_gemm_fused_gated(desc, L.x, L.w, None, L.bias, gate, y)
@@ -599,7 +617,7 @@ def test_bf16_gemm_gated_every_tile(i):
         assert guard_intact(buf, y.numel())
         err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
         assert err <= TOL["bf16"], (tile, err)
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
 
 
 def test_qkv_projection_full_size_sampled():
@@ -624,11 +642,11 @@ def test_fp8_gemm_split_store():
     inp = workloads.generate(wl)
     codes, _ = fp8_reference(inp, np.arange(wl.m))
     L = layers().make_layer(inp, with_unfused=False)
-    for tile in (None, 0, 12, 3):
+    for tile in (None, 0, 3):
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"fp8 split {wl} tile={tile}")
         outs = [guarded((wl.m, 64), torch.uint8) for _ in range(2)]
         dlf().dlf_gemm_fused_split(L.desc, L.x, L.w, L.alpha, L.shift, [y for _, y in outs])
@@ -636,7 +654,7 @@ def test_fp8_gemm_split_store():
         for p, (buf, y) in enumerate(outs):
             assert guard_intact(buf, y.numel()), p
             assert_codes_within_one(host(y, "fp8"), codes[:, 64 * p:64 * (p + 1)])
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
 
 
 # ---------------------------------------------------------------------------
@@ -693,16 +711,16 @@ def test_fp8_gemm_ragged_shapes_every_tile(i):
     L = layers().make_layer(inp)
     for tile in (None,) + GEMM_TILES:
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"fp8_fused {wl} tile={tile}")
         buf, y = guarded((wl.m, wl.n), torch.uint8)
         L.forward(y=y)
         torch.cuda.synchronize()
         assert guard_intact(buf, y.numel())
         assert_codes_within_one(host(y, "fp8"), ref)
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
     case(f"fp8 -> bf16 out {wl}")
     d = dlf()
     yb = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device="cuda")
@@ -735,9 +753,9 @@ def test_fp8_gemm_gelu_every_tile(act):
     desc16 = d.gemm_desc(wl.m, wl.n, wl.k, "fp8", "bf16", act)
     for tile in (None,) + GEMM_TILES:
         if tile is None:
-            os.environ.pop("DLF_TILE", None)
+            ENV.pop("DLF_TILE", None)
         else:
-            os.environ["DLF_TILE"] = str(tile)
+            ENV["DLF_TILE"] = str(tile)
         case(f"fp8 {act} {wl} tile={tile}")
         buf, y = guarded((wl.m, wl.n), torch.uint8)
         d.dlf_gemm_fused(desc8, L.x, L.w, L.alpha, L.shift, None, y)
@@ -745,7 +763,7 @@ def test_fp8_gemm_gelu_every_tile(act):
         assert guard_intact(buf, y.numel())
         diff = np.abs(signed_code_order(host(y, "fp8")) - signed_code_order(codes))
         assert diff.max() <= 1, (tile, diff.max())
-    os.environ.pop("DLF_TILE", None)
+    ENV.pop("DLF_TILE", None)
     case(f"fp8 {act} -> bf16 {wl}")
     yb = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device="cuda")
     d.dlf_gemm_fused(desc16, L.x, L.w, L.alpha, L.shift, None, yb)
@@ -860,16 +878,14 @@ NETWORKS = [
 @pytest.mark.parametrize("fuse", [True, False])
 @pytest.mark.parametrize("i", range(len(NETWORKS)))
 def test_network_under_the_fusion_plan(i, fuse):
-    """The library's plan (identical to the oracle's) executed through the C ABI: every
-    tensor the plan keeps in memory against the oracle network evaluated with the same
-    storage roundings (fused chains: folded bf16 weights, one rounding; other ops: a
-    rounding each).
-
-    A stored tensor that d roundings separate from the inputs (a fused chain counts once,
-    every unfused op once) is held to 1e-2 * max(2, d): each layer adds at most about two
-    bf16 units of the last place of its own (summation order, fp32 vs binary64), and a
-    difference in its input passes through a BN-normalised layer without growing, so the
-    differences add along the longest path.  d <= 2 is the single-layer bf16 bar."""
+    """The library's plan (identical to the oracle's) executed through the C ABI, checked layer
+    by layer: every tensor the plan keeps in memory against the oracle's plain definition of the
+    step that writes it (a fused chain: conv with the master weights -> BN -> [+ residual] ->
+    activation, unfolded; any other op on its own), evaluated in binary64 on the GPU's own stored
+    input tensors.  Each step is one fused launch or one unfused op, so each is held to the
+    single-layer bf16 bar.  The end-to-end difference to the oracle network (every step on the
+    oracle's own stored tensors) is printed as a report: it adds the steps' differences along
+    the path and is no parity bar."""
     from oracle import fusion as ofusion, network as onet
     from workloads import graphs
     from dl_fusion_amd.network import Network
@@ -884,24 +900,18 @@ def test_network_under_the_fusion_plan(i, fuse):
     dev = {j: layers().to_device(b, "bf16") for j, b in bits.items()}
     net.forward(dev)
     torch.cuda.synchronize()
-    ref = onet.forward(g, params, bits, plan)
-    assert sorted(net.bufs) == sorted(k for k in ref if g[k]["op"] != "input")
-    # roundings between the inputs and each stored tensor, along the longest path
-    chain_of = {j: p["nodes"] for p in plan for j in p["nodes"]}
-    depth = {}
-    for j, nd in enumerate(g):
-        if nd["op"] == "input":
-            depth[j] = 0
-        elif j in chain_of:
-            nodes = chain_of[j]
-            if nodes[-1] == j:
-                srcs = {s for k in nodes for s in g[k]["inputs"] if s not in nodes}
-                depth[j] = 1 + max(depth[s] for s in srcs)
-        else:
-            depth[j] = 1 + max(depth[s] for s in nd["inputs"])
-    for j, t in net.bufs.items():
-        err = oracle.rel_error(oracle.widen(host(t, "bf16"), "bf16"), ref[j])
-        assert err <= 1e-2 * max(2, depth[j]), (j, g[j]["op"], depth[j], err)
+    steps = onet.steps(g, plan)
+    assert sorted(net.bufs) == sorted(steps)
+    stored = {j: oracle.widen(b, "bf16") for j, b in bits.items()}
+    stored.update({j: oracle.widen(host(t, "bf16"), "bf16") for j, t in net.bufs.items()})
+    for j, nodes in steps.items():
+        ref = onet.step(g, params, stored, nodes)
+        err = oracle.rel_error(stored[j], ref)
+        assert err <= TOL["bf16"], (j, [g[k]["op"] for k in nodes], err)
+    ref_net = onet.forward(g, params, bits, plan)
+    end = max(oracle.rel_error(stored[j], ref_net[j]) for j in net.outputs)
+    print(f"[report] network {kind} fuse={fuse}: end-to-end rel error {end:.3e} over "
+          f"{len(steps)} stored tensors", flush=True)
     if fuse:
         assert net.launches == len(plan) + sum(
             1 for j, nd in enumerate(g) if nd["op"] != "input" and all(j not in p["nodes"] for p in plan))
@@ -965,13 +975,13 @@ def test_ffn_token_blocks(tok):
         ref = oracle.ffn(inp)
         L = layers().make_layer(inp, with_unfused=False)
         case(f"ffn fused tok={tok} {wl}")
-        os.environ["DLF_FFN_TOK"] = tok
+        ENV["DLF_FFN_TOK"] = tok
         try:
             buf, y = guarded((wl.m, wl.d_model), torch.bfloat16)
             L.forward(y=y)
             torch.cuda.synchronize()
         finally:
-            os.environ.pop("DLF_FFN_TOK", None)
+            ENV.pop("DLF_FFN_TOK", None)
         assert guard_intact(buf, y.numel())
         err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
         assert err <= TOL["bf16"], (tok, i, err)
@@ -1019,7 +1029,7 @@ def test_ffn_split_over_d_ff(split):
              dict(m=300, d_model=512, d_ff=1280, act="gelu_erf", residual=True)]
     d = dlf()
     if split != "auto":
-        os.environ["DLF_FFN_SPLIT"] = split
+        ENV["DLF_FFN_SPLIT"] = split
     try:
         for i, kw in enumerate(cases):
             wl = workloads.FfnWorkload(f"ffn_split{split}_{i}", seed=80 + i, **kw)
@@ -1045,4 +1055,4 @@ def test_ffn_split_over_d_ff(split):
             err = oracle.rel_error(oracle.widen(host(y, "bf16"), "bf16"), ref)
             assert err <= TOL["bf16"], (split, i, err)
     finally:
-        os.environ.pop("DLF_FFN_SPLIT", None)
+        ENV.pop("DLF_FFN_SPLIT", None)
