@@ -129,6 +129,8 @@ _lib.dlf_status_string.restype = ctypes.c_char_p
 _lib.dlf_status_string.argtypes = [ctypes.c_int]
 _lib.dlf_last_error.restype = ctypes.c_char_p
 _lib.dlf_last_error.argtypes = []
+_lib.dlf_tuning_reload.restype = None
+_lib.dlf_tuning_reload.argtypes = []
 
 
 class DlfError(RuntimeError):
@@ -144,6 +146,12 @@ def dlf_status_string(status: int) -> str:
 
 def dlf_last_error() -> str:
     return _lib.dlf_last_error().decode()
+
+
+def dlf_tuning_reload():
+    """Re-read the DLF_* tuning switches from the environment (the library reads them once,
+    when it is loaded)."""
+    _lib.dlf_tuning_reload()
 
 
 def _check(status: int, func: str):

@@ -33,6 +33,39 @@ dlf_status ok() {
     return DLF_OK;
 }
 
+namespace {
+
+Options read_options() {
+    Options o{-1, 0, 0, 0, 0, 0};
+    if (const char* e = std::getenv("DLF_TILE")) {
+        const int t = std::atoi(e);
+        if (t >= 0 && t < kTileCount) o.tile = t;
+    }
+    if (const char* e = std::getenv("DLF_GEMM")) o.gemm = std::strcmp(e, "tiled") == 0 ? 1 : std::strcmp(e, "stream") == 0 ? 2 : 0;
+    if (const char* e = std::getenv("DLF_CONV")) o.conv = std::strcmp(e, "generic") == 0 ? 1 : std::strcmp(e, "stream") == 0 ? 2 : 0;
+    if (const char* e = std::getenv("DLF_STREAM_NB")) {
+        const int nb = std::atoi(e);
+        if (nb == 128 || nb == 256 || nb == 384) o.stream_nb = nb;
+    }
+    if (const char* e = std::getenv("DLF_FFN_TOK")) {
+        const int t = std::atoi(e);
+        if (t == 32 || t == 64) o.ffn_tok = t;
+    }
+    if (const char* e = std::getenv("DLF_FFN_SPLIT")) {
+        const int v = std::atoi(e);
+        o.ffn_split = v <= 1 ? 1 : v;
+    }
+    return o;
+}
+
+// read once at library load (static initialisation), replaced only by dlf_tuning_reload
+Options g_options = read_options();
+
+}  // namespace
+
+const Options& options() { return g_options; }
+void reload_options() { g_options = read_options(); }
+
 }  // namespace dlf
 
 namespace {
@@ -68,32 +101,27 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Tile of the MFMA kernel for an M x N output.  DLF_TILE=<n> forces one (tuning
-// only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x (tile area /
-// relative MFMA efficiency of the tile shape).  Where that picks 256 x 256 for a
-// dense GEMM, the eight-wave 256 x 256 variant with one barrier per two K slices
-// runs instead: measured 7-10% faster on the 4096 x 11008 x 4096 bf16 and
-// 8192 x 4096 x 4096 fp8 GEMMs.
+// Tile of the MFMA kernel for an M x N output.  A tile forced by DLF_TILE wins where the route
+// has it (tuning only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x (tile
+// area / relative MFMA efficiency of the tile shape).  The 256 x 256 tile is the eight-wave
+// pipeline with one barrier per two K slices (dense GEMMs only): measured 7-10% faster than
+// four waves of 128 x 128 on the 4096 x 11008 x 4096 bf16 and 8192 x 4096 x 4096 fp8 GEMMs.
 // Memory-bound GEMMs (many rows, short K, narrow N) take the streaming kernel unless a tile
-// is forced (DLF_TILE) or DLF_GEMM=tiled asks for the tiled kernel; DLF_GEMM=stream takes it
-// wherever it applies (tests of both routes).
+// is forced or DLF_GEMM=tiled asks for the tiled kernel; DLF_GEMM=stream takes it wherever it
+// applies (tests of both routes).
 bool stream_gemm(const dlf::MmaArgs& a) {
-    if (std::getenv("DLF_TILE")) return false;
-    const char* g = std::getenv("DLF_GEMM");
-    if (g && std::strcmp(g, "tiled") == 0) return false;
-    if (g && std::strcmp(g, "stream") == 0) return dlf::gemm_stream_ok(a);
+    const dlf::Options& o = dlf::options();
+    if (o.tile >= 0 || o.gemm == 1) return false;
+    if (o.gemm == 2) return dlf::gemm_stream_ok(a);
     return dlf::gemm_stream_pays(a);
 }
 
 int pick_tile(int64_t M, int64_t N, bool dense) {
-    if (const char* env = std::getenv("DLF_TILE")) {
-        const int t = std::atoi(env);
-        if (t >= 0 && t < dlf::kTileCount) return t;
-    }
-    // Measured on MI355X: the four-wave 256x128 and 256x64 tiles lost to 128x128 / 128x64 on
-    // every shape swept (memory-bound 1x1 layers, FFN projections, square GEMMs), and the
-    // four-wave 256x256 tile of the implicit GEMM to 128x128; the dense 256x256 tile is the
-    // eight-wave pipeline.
+    const int forced = dlf::options().tile;
+    if (forced >= 0 && (dense || forced != dlf::kTile256x256)) return forced;
+    // Measured on MI355X: four-wave 256x128 and 256x64 tiles lost to 128x128 / 128x64 on
+    // every shape swept (memory-bound 1x1 layers, FFN projections, square GEMMs), and a
+    // four-wave 256x256 tile of the implicit GEMM to 128x128.
     const int cands[] = {dlf::kTile256x256, dlf::kTile128x128, dlf::kTile128x64, dlf::kTile64x64};
     const double eff[] = {1.0, 0.8, 0.65, 0.5};
     int best = dlf::kTile64x64;
@@ -110,7 +138,6 @@ int pick_tile(int64_t M, int64_t N, bool dense) {
             best_cost = cost;
         }
     }
-    if (dense && best == dlf::kTile256x256) best = dlf::kTile256x256w8ab2;
     return best;
 }
 
@@ -209,9 +236,8 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     // kernel.  DLF_CONV=generic forces the implicit GEMM, DLF_CONV=stream the halo kernel
     // that streams weights (tests of every route).
     dlf::HaloPlan plan{};
-    const char* force = std::getenv("DLF_CONV");
-    const bool generic = force && std::strcmp(force, "generic") == 0;
-    const bool stream_only = force && std::strcmp(force, "stream") == 0;
+    const bool generic = dlf::options().conv == 1;
+    const bool stream_only = dlf::options().conv == 2;
     dlf::SmallCArgs sc{};
     if (!generic && g.K > 0 &&
         dlf::conv_smallc_plan(static_cast<int>(d->n), static_cast<int>(d->h), static_cast<int>(d->w),
@@ -267,8 +293,8 @@ dlf_status launch_conv(const dlf_conv_desc* d, const ConvGeom& g, const void* x,
     if (!generic && d->kh == 1 && d->kw == 1 && d->pad_h == 0 && d->pad_w == 0 && stream_gemm(a))
         return hip_status(dlf::launch_gemm_stream(a, act_code(d->act), s), what);
     // the value-by-value gather (c_in % 8 != 0) is latency-bound: smaller tiles, more of them
-    const int tile = d->c_in % 8 != 0 && !std::getenv("DLF_TILE") ? static_cast<int>(dlf::kTile128x64)
-                                                                  : pick_tile(g.M, d->c_out, false);
+    const int tile = d->c_in % 8 != 0 && dlf::options().tile < 0 ? static_cast<int>(dlf::kTile128x64)
+                                                                 : pick_tile(g.M, d->c_out, false);
     return hip_status(dlf::launch_mma_bf16(a, true, act_code(d->act), tile, s), what);
 }
 
@@ -307,6 +333,8 @@ const char* dlf_status_string(dlf_status s) {
 }
 
 const char* dlf_last_error(void) { return g_last_error; }
+
+void dlf_tuning_reload(void) { dlf::reload_options(); }
 
 dlf_status dlf_fold_bn(int64_t cout, int64_t k, const float* w, const float* conv_bias, const float* gamma,
                        const float* beta, const float* mean, const float* var, double eps,

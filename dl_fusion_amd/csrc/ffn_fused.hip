@@ -293,10 +293,8 @@ hipError_t launch_d(const FfnArgs& a, hipStream_t s) {
 template <int ACT>
 hipError_t launch_act(const FfnArgs& a, hipStream_t s) {
     int tok = a.M >= (a.parts > 1 ? 4096 : 64 * 256) && a.D <= 768 ? 64 : 32;
-    if (const char* env = std::getenv("DLF_FFN_TOK")) {
-        const int t = std::atoi(env);
-        if (t == 32 || (t == 64 && a.D <= 768)) tok = t;
-    }
+    const int t = options().ffn_tok;
+    if (t == 32 || (t == 64 && a.D <= 768)) tok = t;
     if (a.parts > 1) return tok == 64 ? launch_d<ACT, 2, true>(a, s) : launch_d<ACT, 1, true>(a, s);
     return tok == 64 ? launch_d<ACT, 2, false>(a, s) : launch_d<ACT, 1, false>(a, s);
 }
@@ -311,11 +309,9 @@ int ffn_parts(int64_t M, int D, int F) {
     // token blocks, into as many parts as fit one round of 256 workgroups.
     const int nchunks = F / kChunk;
     if (D > 768 || nchunks < 2 || M <= 0) return 1;
-    if (const char* env = std::getenv("DLF_FFN_SPLIT")) {
-        const int want = std::atoi(env);
-        if (want == 0 || want == 1) return 1;
-        if (want > 1) return want < nchunks ? want : nchunks;
-    }
+    const int want = options().ffn_split;
+    if (want == 1) return 1;
+    if (want > 1) return want < nchunks ? want : nchunks;
     if (M >= 64 * 256) return 1;
     const int64_t tok = M >= 4096 ? 64 : 32;                     // as launch_act takes for a split
     const int64_t blocks = (M + tok - 1) / tok;

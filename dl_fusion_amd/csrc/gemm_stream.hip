@@ -293,10 +293,8 @@ bool built(int64_t nb, int64_t k) { return (k == 128 && nb <= 384) || (k == 256 
 // a workgroup cost more than the fourfold reads of A), or what DLF_STREAM_NB asks for where
 // that is built and divides N (tuning only); 0 if none
 int64_t block_cols(int64_t n, int64_t k, bool gather) {
-    if (const char* env = std::getenv("DLF_STREAM_NB")) {
-        const int64_t nb = std::atoll(env);
-        if ((nb == 128 || nb == 256 || nb == 384) && n % nb == 0 && built(nb, k)) return nb;
-    }
+    const int64_t nb = options().stream_nb;
+    if (nb != 0 && n % nb == 0 && built(nb, k)) return nb;
     if (gather) return n % 128 == 0 ? 128 : 0;
     for (const int64_t nb : {384, 256, 128})
         if (n % nb == 0 && built(nb, k)) return nb;

@@ -7,6 +7,26 @@
 
 namespace dlf {
 
+// Route and tile switches (tuning and tests).  They are read from the environment once, when
+// the library is loaded, and again by dlf_tuning_reload():
+//   DLF_TILE=<n>            force MFMA tile n (a kTile* value the route has)
+//   DLF_GEMM=tiled|stream   the tiled MFMA kernel, or the streaming kernel wherever it applies
+//   DLF_CONV=generic|stream the implicit GEMM for every conv, or the weight-streaming halo kernel
+//                           for every 3x3 stride-1 conv
+//   DLF_STREAM_NB=128|256|384  the streaming kernel's column block, where built and dividing N
+//   DLF_FFN_TOK=32|64       the fused FFN's token block
+//   DLF_FFN_SPLIT=<s>       the fused FFN's d_ff parts (0 or 1: no split)
+struct Options {
+    int tile;        // forced tile, or -1
+    int gemm;        // 0 the library's choice, 1 tiled only, 2 streaming where it applies
+    int conv;        // 0 the library's choice, 1 implicit GEMM, 2 weight-streaming halo kernel
+    int stream_nb;   // 0, or the forced column block
+    int ffn_tok;     // 0, or the forced token block
+    int ffn_split;   // 0 the library's choice, 1 no split, >= 2 that many parts
+};
+const Options& options();
+void reload_options();
+
 // Arguments of the MFMA GEMM / implicit-GEMM kernel.  C[m][n] = sum_k A[m][k] B[n][k]
 // followed by the register epilogue.  For a convolution, A is gathered on the fly
 // from the NHWC input (row m = (img, ho, wo), k = (r*KW + s)*Cin + ci).
@@ -29,28 +49,14 @@ struct MmaArgs {
     int H, W, Cin, Ho, Wo, KW, SH, SW, PH, PW;
 };
 
-// Output tile shapes of the MFMA kernel (rows x columns of C per workgroup).
+// Output tile shapes of the MFMA kernel (rows x columns of C per workgroup).  The 256 x 256
+// tile serves the dense GEMM only; the implicit-GEMM convolution takes the other three.
 enum MmaTile : int {
-    kTile256x256 = 0,   // 2x2 waves of 128x128
+    kTile256x256 = 0,   // 2x4 waves of 128x64, one barrier per two K slices
     kTile128x128 = 1,   // 2x2 waves of 64x64
-    kTile256x64 = 2,    // 4x1 waves of 64x64
+    kTile128x64 = 2,    // 2x2 waves of 64x32
     kTile64x64 = 3,     // 2x2 waves of 32x32
-    kTile128x64 = 4,    // 2x2 waves of 64x32
-    kTile256x128 = 5,   // 2x2 waves of 128x64
-    // dense-GEMM pipeline variants (DLF_TILE selects one): eight waves (two per SIMD), three
-    // or five stages, one barrier per two K slices, register staging.  kTile256x256w8ab2 is
-    // the default wherever the cost model picks 256 x 256 for a dense GEMM.
-    kTile256x256w8 = 6,   // 2x4 waves of 128x64
-    kTile256x256w8t = 7,  // 4x2 waves of 64x128
-    kTile256x256s3 = 8,   // 2x2 waves of 128x128, three stages
-    kTile256x128s3 = 9,   // 2x2 waves of 128x64, three stages
-    kTile256x128w8 = 10,  // 4x2 waves of 64x64
-    kTile256x256w8b2 = 11,   // 4x2 waves of 64x128, one barrier per two K slices
-    kTile256x256w8ab2 = 12,  // 2x4 waves of 128x64, one barrier per two K slices
-    kTile256x256w8s5 = 13,   // 4x2 waves of 64x128, five stages
-    kTile256x256w8r = 14,    // 4x2 waves of 64x128, operands staged through registers
-    kTile256x256w8ar = 15,   // 2x4 waves of 128x64, operands staged through registers
-    kTileCount = 16
+    kTileCount = 4
 };
 int mma_tile_rows(int tile);
 int mma_tile_cols(int tile);

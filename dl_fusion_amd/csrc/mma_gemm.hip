@@ -7,9 +7,7 @@ namespace dlf {
 
 int mma_tile_rows(int tile) {
     switch (tile) {
-        case kTile256x256: case kTile256x128: case kTile256x64: case kTile256x256w8: case kTile256x256w8t:
-        case kTile256x256s3: case kTile256x128s3: case kTile256x128w8: case kTile256x256w8b2:
-        case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r: case kTile256x256w8ar: return 256;
+        case kTile256x256: return 256;
         case kTile128x128: case kTile128x64: return 128;
         case kTile64x64: return 64;
         default: return 0;
@@ -18,10 +16,8 @@ int mma_tile_rows(int tile) {
 
 int mma_tile_cols(int tile) {
     switch (tile) {
-        case kTile256x256: case kTile256x256w8: case kTile256x256w8t: case kTile256x256s3:
-        case kTile256x256w8b2: case kTile256x256w8ab2: case kTile256x256w8s5: case kTile256x256w8r:
-        case kTile256x256w8ar: return 256;
-        case kTile256x128: case kTile128x128: case kTile256x128s3: case kTile256x128w8: return 128;
+        case kTile256x256: return 256;
+        case kTile128x128: return 128;
         default: return 64;
     }
 }
@@ -29,25 +25,22 @@ int mma_tile_cols(int tile) {
 namespace {
 
 // The buffer form holds while a 256-row panel spans less than 2 GB (rows under 8 MB); longer
-// rows take the global-address form, which has the six basic tiles only.
+// rows take the global-address form.
 bool dense_buffer_ok(const MmaArgs& a, int elem) { return static_cast<int64_t>(a.K) * elem < (int64_t(1) << 23); }
-int wide_tile(int tile) { return tile <= kTile256x128 ? tile : static_cast<int>(kTile256x256); }
 
 }  // namespace
 
 hipError_t launch_mma_bf16(const MmaArgs& a, bool conv, int act, int tile, hipStream_t s) {
     if (conv) return launch_mma_bf16_conv(a, act, tile, s);
     const bool wide = !dense_buffer_ok(a, 2);
-    const int t = wide ? wide_tile(tile) : tile;
-    if (act >= kActSiluMul) return launch_mma_bf16_gated(a, wide, act, t, s);
-    return launch_mma_bf16_dense(a, wide, act, t, s);
+    if (act >= kActSiluMul) return launch_mma_bf16_gated(a, wide, act, tile, s);
+    return launch_mma_bf16_dense(a, wide, act, tile, s);
 }
 
 hipError_t launch_mma_fp8(const MmaArgs& a, int act, int out, int tile, hipStream_t s) {
     const bool wide = !dense_buffer_ok(a, 1);
-    const int t = wide ? wide_tile(tile) : tile;
-    if (out == kOutFp8) return launch_mma_fp8_q(a, wide, act, t, s);
-    return launch_mma_fp8_b(a, wide, act, out, t, s);
+    if (out == kOutFp8) return launch_mma_fp8_q(a, wide, act, tile, s);
+    return launch_mma_fp8_b(a, wide, act, out, tile, s);
 }
 
 }  // namespace dlf

@@ -55,13 +55,10 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64];
 // 16-byte chunk inside one tap (Cin % 8 == 0), or value by value (any Cin).
 enum : int { kDense = 0, kConvAligned = 1, kConvGeneric = 2, kDenseWide = 3, kConvAnyC = 4 };
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1, bool REG_ = false>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int SPB_ = 1>
 struct TileShape {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int SPB = SPB_;                       // K slices consumed per barrier
-    // REG: operand slices travel global -> registers -> LDS (global_load_dwordx4 +
-    // ds_write_b128) instead of the LDS-DMA path; the LDS image is identical
-    static constexpr bool REG = REG_;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 fragments per wave
     static constexpr int NW = WAVES_M * WAVES_N;           // waves per workgroup
@@ -73,7 +70,6 @@ struct TileShape {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "whole 32x32 fragments");
     static_assert(LA >= 1 && LB >= 1, "each wave loads at least one kilobyte per operand");
     static_assert(STAGES >= 2 * SPB, "the ring holds the slices being read and the ones landing");
-    static_assert(!REG || (STAGES == 3 && SPB == 1), "register path: three LDS stages, one slice per barrier");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r.  Rows are 64 bytes (four
@@ -147,15 +143,14 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     constexpr bool DENSE = AMODE == kDense || AMODE == kDenseWide;
     // dense operands as buffers: the LDS-DMA loads are then not FLAT instructions, which
     // keeps the compiler's count of outstanding LDS reads exact while they are in flight, and
-    // the offsets are 32-bit (the register path keeps its global loads)
-    constexpr bool BUF = AMODE == kDense && !TS::REG;
+    // the offsets are 32-bit
+    constexpr bool BUF = AMODE == kDense;
     constexpr int CE = 16 / ELEM;                 // elements per 16-byte chunk
     constexpr int KE = kRowBytes / ELEM;          // K elements per slice
     constexpr int S = TS::STAGES;
     // vmcnt units per slice per lane.  The value-by-value gather completes inside the slice's
     // issue (its values pass through registers into LDS), so it leaves none outstanding.
     constexpr int LOADS = AMODE == kConvAnyC ? 0 : TS::LA + TS::LB;
-    static_assert(AMODE != kConvAnyC || !TS::REG, "the gather writes LDS itself");
     using F = Frag<ELEM>;
     // the LDS holds the operand ring during the K loop and the rounded output tile after it
     constexpr int STAGED = OUT == kOutF32 ? 0 : TS::BM * TS::BN * (OUT == kOutFp8 ? 1 : 2);
@@ -230,8 +225,6 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         for (int j = 0; j < TS::LB; ++j)
             b_off[j] = static_cast<uint32_t>(((wave * TS::LB + j) * kRowsPerLoad + prow) * row_bytes + b_lchunk[j] * 16);
     }
-    // register staging for the REG path: two sets of this lane's 16-byte pieces of a slice
-    u32x4_t rv[TS::REG ? 2 : 1][TS::LA + TS::LB];
     // Issues this lane's loads of slice kt (kt may exceed the last slice: then all zero
     // page).  sink(j, src, lds_dst) receives load slot j (A slots first, then B).
     auto gen_slice = [&](int kt, auto sink) {
@@ -348,26 +341,6 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     auto issue_slice = [&](int kt) {
         gen_slice(kt, [&](int, const void* src, uint8_t* dst) { load_lds16(src, dst); });
     };
-    // register path: loads into register set `set`; the later LDS write puts lane i's piece
-    // at dst + 16 i, the position the LDS-DMA path would have used
-    auto load_slice = [&](auto set_c, int kt) {
-        constexpr int set = decltype(set_c)::value;
-        gen_slice(kt, [&](int j, const void* src, uint8_t*) {
-            rv[set][j] = *static_cast<const u32x4_t*>(src);
-        });
-    };
-    auto write_slice = [&](auto set_c, int kt) {
-        constexpr int set = decltype(set_c)::value;
-        uint8_t* sA = smem + (kt % S) * TS::STAGE;
-        uint8_t* sB = sA + TS::BM * kRowBytes;
-#pragma unroll
-        for (int j = 0; j < TS::LA; ++j)
-            *reinterpret_cast<u32x4_t*>(sA + (wave * TS::LA + j) * 1024 + lane * 16) = rv[set][j];
-#pragma unroll
-        for (int j = 0; j < TS::LB; ++j)
-            *reinterpret_cast<u32x4_t*>(sB + (wave * TS::LB + j) * 1024 + lane * 16) = rv[set][TS::LA + j];
-    };
-
     f32x16_t acc[TS::FN][TS::FM];     // D = W . X^T: acc[j][i] covers columns of fragment j, rows of i
 #pragma unroll
     for (int j = 0; j < TS::FN; ++j)
@@ -391,9 +364,8 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     const int x_row = wm * TS::WTM + (lane & 31);   // activation fragment rows in the tile
     const int w_row = wn * TS::WTN + (lane & 31);   // weight fragment rows in the tile
     constexpr int P = SPB * F::kSteps;               // steps between transitions
-    // steps per loop iteration: even (static fragment buffers); the register path also needs
-    // two slices per iteration (static register sets)
-    constexpr int U = TS::REG ? 2 * F::kSteps : (P >= 2 ? P : 2);
+    // steps per loop iteration: even (static fragment buffers)
+    constexpr int U = P >= 2 ? P : 2;
     constexpr int SLICES_PER_ITER = U / F::kSteps;
     const int KTP = (KT + SLICES_PER_ITER - 1) / SLICES_PER_ITER * SLICES_PER_ITER;
     const int steps = KTP * F::kSteps;
@@ -420,22 +392,9 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if constexpr (TS::REG) {
-        // slices 0 and 1 go to LDS; slices 2 and 3 stay in flight in the register sets
-        load_slice(I0{}, 0);
-        load_slice(I1{}, 1);
-        wait_vmcnt<LOADS>();
-        write_slice(I0{}, 0);
-        load_slice(I0{}, 2);
-        wait_vmcnt<LOADS>();
-        write_slice(I1{}, 1);
-        load_slice(I1{}, 3);
-        wait_vmcnt<2 * LOADS>();
-    } else {
 #pragma unroll
-        for (int s2 = 0; s2 < S; ++s2) issue_slice(s2);
-        wait_vmcnt<(S - SPB) * LOADS>();
-    }
+    for (int s2 = 0; s2 < S; ++s2) issue_slice(s2);
+    wait_vmcnt<(S - SPB) * LOADS>();
     barrier();
     read_frags(I0{}, 0, 0);
 
@@ -458,19 +417,6 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
             read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
             mma_all(std::integral_constant<int, c>{});
             schedule(std::integral_constant<int, R>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-        } else if constexpr (TS::REG) {
-            // slice kt+2 has reached its registers (kt+3 may be in flight) and this wave's
-            // LDS writes of slice kt+1 are done; after the barrier slice kt+1 is visible to
-            // all and stage (kt+2)%3 (slice kt-1) is free
-            wait_vmcnt<LOADS>();
-            barrier();
-            constexpr int set = slice_in_iter & 1;          // register set of slice kt+2 (and kt+4)
-            write_slice(std::integral_constant<int, set>{}, kt + 2);
-            load_slice(std::integral_constant<int, set>{}, kt + 4);
-            read_frags(std::integral_constant<int, n>{}, kt + 1, 0);
-            mma_all(std::integral_constant<int, c>{});
-            schedule(std::integral_constant<int, R>{}, std::integral_constant<int, LOADS>{},
-                     std::integral_constant<int, LOADS>{});
         } else {
             wait_vmcnt<(S - 2 * SPB) * LOADS>();
             barrier();
@@ -647,23 +593,13 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
     }
 }
 
-using T256x256 = TileShape<256, 256, 2, 2, 4>;
-using T256x128 = TileShape<256, 128, 2, 2, 4>;
+// The tiles the library chooses from (api.cpp, pick_tile): the eight-wave 256 x 256 tile with
+// one barrier per two K slices for large dense GEMMs (two waves per SIMD, each 128 x 64), and
+// four-wave tiles for everything smaller and for the implicit-GEMM convolution.
+using T256x256 = TileShape<256, 256, 2, 4, 4, 2>;
 using T128x128 = TileShape<128, 128, 2, 2, 4>;
-using T256x64 = TileShape<256, 64, 4, 1, 4>;
 using T128x64 = TileShape<128, 64, 2, 2, 4>;
 using T64x64 = TileShape<64, 64, 2, 2, 4>;
-// tuning variants (dense GEMM only): two waves per SIMD, or fewer stages
-using T256x256w8 = TileShape<256, 256, 2, 4, 4>;    // 8 waves of 128x64
-using T256x256w8t = TileShape<256, 256, 4, 2, 4>;   // 8 waves of 64x128
-using T256x256s3 = TileShape<256, 256, 2, 2, 3>;
-using T256x128s3 = TileShape<256, 128, 2, 2, 3>;
-using T256x128w8 = TileShape<256, 128, 4, 2, 4>;    // 8 waves of 64x64
-using T256x256w8b2 = TileShape<256, 256, 4, 2, 4, 2>;  // 8 waves of 64x128, barrier every 2 slices
-using T256x256w8ab2 = TileShape<256, 256, 2, 4, 4, 2>; // 8 waves of 128x64, barrier every 2 slices
-using T256x256w8s5 = TileShape<256, 256, 4, 2, 5>;     // 8 waves of 64x128, five stages
-using T256x256w8r = TileShape<256, 256, 4, 2, 3, 1, true>;   // 8 waves of 64x128, register path
-using T256x256w8ar = TileShape<256, 256, 2, 4, 3, 1, true>;  // 8 waves of 128x64, register path
 
 template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 hipError_t launch_one(const MmaArgs& a, hipStream_t stream) {
@@ -680,28 +616,13 @@ hipError_t launch_one(const MmaArgs& a, hipStream_t stream) {
 template <int ELEM, int AMODE, int ACT, int OUT>
 hipError_t launch_tile(const MmaArgs& a, int tile, hipStream_t s) {
     switch (tile) {
-        case kTile256x256: return launch_one<ELEM, T256x256, AMODE, ACT, OUT>(a, s);
-        case kTile256x128: return launch_one<ELEM, T256x128, AMODE, ACT, OUT>(a, s);
         case kTile128x128: return launch_one<ELEM, T128x128, AMODE, ACT, OUT>(a, s);
-        case kTile256x64: return launch_one<ELEM, T256x64, AMODE, ACT, OUT>(a, s);
         case kTile128x64: return launch_one<ELEM, T128x64, AMODE, ACT, OUT>(a, s);
         case kTile64x64: return launch_one<ELEM, T64x64, AMODE, ACT, OUT>(a, s);
         default: break;
     }
-    if constexpr (AMODE == kDense) {
-        switch (tile) {
-            case kTile256x256w8r: return launch_one<ELEM, T256x256w8r, AMODE, ACT, OUT>(a, s);
-            case kTile256x256w8ar: return launch_one<ELEM, T256x256w8ar, AMODE, ACT, OUT>(a, s);
-            case kTile256x256w8: return launch_one<ELEM, T256x256w8, AMODE, ACT, OUT>(a, s);
-            case kTile256x256w8t: return launch_one<ELEM, T256x256w8t, AMODE, ACT, OUT>(a, s);
-            case kTile256x256s3: return launch_one<ELEM, T256x256s3, AMODE, ACT, OUT>(a, s);
-            case kTile256x128s3: return launch_one<ELEM, T256x128s3, AMODE, ACT, OUT>(a, s);
-            case kTile256x128w8: return launch_one<ELEM, T256x128w8, AMODE, ACT, OUT>(a, s);
-            case kTile256x256w8b2: return launch_one<ELEM, T256x256w8b2, AMODE, ACT, OUT>(a, s);
-            case kTile256x256w8ab2: return launch_one<ELEM, T256x256w8ab2, AMODE, ACT, OUT>(a, s);
-            case kTile256x256w8s5: return launch_one<ELEM, T256x256w8s5, AMODE, ACT, OUT>(a, s);
-            default: break;
-        }
+    if constexpr (AMODE == kDense || AMODE == kDenseWide) {
+        if (tile == kTile256x256) return launch_one<ELEM, T256x256, AMODE, ACT, OUT>(a, s);
     }
     return hipErrorInvalidValue;
 }

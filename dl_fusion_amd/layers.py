@@ -9,6 +9,12 @@ to the GPU once, and ``forward()`` enqueues the single fused kernel.
 add, activation and quantisation kernels, each through device memory, for the
 HBM-traffic and timing comparison.
 
+Where the library has no fused kernel for a layer it says so with
+DLF_ERR_UNSUPPORTED, before launching anything; ``forward()`` then runs the
+unfused chain in its place, for that call and every later one ("OpenPPL算子融合
+深度解析" §4.2 keeps the separate ops where a fusion does not apply; the MindIE-SD
+RFC §3.7 falls back to the original graph).  Every other error is raised.
+
 Inputs arrive as host numpy arrays in their storage format (float32 values,
 bf16 bit patterns as uint16, or e4m3 codes as uint8).
 """
@@ -17,8 +23,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (dlf_act_apply, dlf_add, dlf_bn_apply, dlf_bn_scale_shift, dlf_conv_fused, dlf_conv_plain,
-               dlf_ffn_fused_ws, dlf_ffn_pack, dlf_ffn_workspace_bytes, ffn_desc,
+from . import (DLF_ERR_UNSUPPORTED, DlfError, dlf_act_apply, dlf_add, dlf_bn_apply, dlf_bn_scale_shift,
+               dlf_conv_fused, dlf_conv_plain, dlf_ffn_fused_ws, dlf_ffn_pack, dlf_ffn_workspace_bytes, ffn_desc,
                dlf_fold_bn, dlf_gemm_fused, dlf_gemm_plain, dlf_quant_apply, dlf_scale_shift_apply,
                conv_desc, gemm_desc)
 
@@ -50,6 +56,26 @@ def _torch_dtype(dtype: str):
     return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
 
 
+class _FallbackLayer:
+    """forward() = the fused call, or the unfused chain once the library has answered
+    DLF_ERR_UNSUPPORTED for this layer."""
+
+    fused_ok = True
+
+    def forward(self, stream=None, y=None, **kw):
+        out = self.y if y is None else y
+        if self.fused_ok:
+            try:
+                self._fused(out, stream, **kw)
+                return out
+            except DlfError as e:
+                if e.status != DLF_ERR_UNSUPPORTED:
+                    raise
+                self.fused_ok = False
+                self.unsupported = e.detail
+        return self.forward_unfused(stream, y=out, **kw)
+
+
 def _master_cast(w: np.ndarray, dtype: str) -> np.ndarray:
     """Unfolded fp32 master weights in the layer's storage type (unfused chain only)."""
     if dtype == "f32":
@@ -58,7 +84,7 @@ def _master_cast(w: np.ndarray, dtype: str) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-class FusedConvBNAct:
+class FusedConvBNAct(_FallbackLayer):
     """Conv2d (NHWC / OHWI) -> BatchNorm -> [+ residual] -> activation."""
 
     def __init__(self, inp: dict, device="cuda", with_unfused=True):
@@ -78,40 +104,47 @@ class FusedConvBNAct:
         self.res = to_device(inp.get("residual"), wl.dtype, device)
         self.out_shape = (wl.n, wl.ho, wl.wo, wl.cout)
         self.y = torch.empty(self.out_shape, dtype=_torch_dtype(wl.dtype), device=device)
+        self._inp, self._device = inp, device
         self.with_unfused = with_unfused
         if with_unfused:
-            self.w_raw = to_device(_master_cast(inp["w"], wl.dtype), wl.dtype, device)
-            cb = inp["conv_bias"]
-            self.conv_bias = torch.from_numpy(np.asarray(cb, np.float32)).to(device) if cb is not None else None
-            self.bn = [torch.from_numpy(np.asarray(inp[k], np.float32)).to(device)
-                       for k in ("gamma", "beta", "mean", "var")]
-            self.eps = inp["eps"]
-            self.t1 = torch.empty_like(self.y)
-            self.t2 = torch.empty_like(self.y)
-            self.y_unfused = torch.empty_like(self.y)
+            self._unfused_buffers()
+
+    def _unfused_buffers(self):
+        if getattr(self, "t1", None) is not None:
+            return
+        inp, wl, device = self._inp, self.wl, self._device
+        self.w_raw = to_device(_master_cast(inp["w"], wl.dtype), wl.dtype, device)
+        cb = inp["conv_bias"]
+        self.conv_bias = torch.from_numpy(np.asarray(cb, np.float32)).to(device) if cb is not None else None
+        self.bn = [torch.from_numpy(np.asarray(inp[k], np.float32)).to(device)
+                   for k in ("gamma", "beta", "mean", "var")]
+        self.eps = inp["eps"]
+        self.t1 = torch.empty_like(self.y)
+        self.t2 = torch.empty_like(self.y)
+        self.y_unfused = torch.empty_like(self.y)
 
     @property
     def rows(self):
         return self.wl.n * self.wl.ho * self.wl.wo
 
-    def forward(self, stream=None, x=None, y=None):
-        out = self.y if y is None else y
+    def _fused(self, out, stream, x=None):
         dlf_conv_fused(self.desc, self.x if x is None else x, self.w, self.b, self.res, out, stream)
-        return out
 
-    def forward_unfused(self, stream=None):
+    def forward_unfused(self, stream=None, y=None, x=None):
         wl = self.wl
-        dlf_conv_plain(self.desc_plain, self.x, self.w_raw, self.conv_bias, self.t1, stream)
+        self._unfused_buffers()
+        out = self.y_unfused if y is None else y
+        dlf_conv_plain(self.desc_plain, self.x if x is None else x, self.w_raw, self.conv_bias, self.t1, stream)
         dlf_bn_apply(self.rows, wl.cout, wl.dtype, self.t1, *self.bn, self.eps, self.t2, stream)
         cur = self.t2
         if self.res is not None:
             dlf_add(self.t2.numel(), wl.dtype, self.t2, self.res, self.t1, stream)
             cur = self.t1
-        dlf_act_apply(cur.numel(), wl.dtype, wl.act, cur, self.y_unfused, stream)
-        return self.y_unfused
+        dlf_act_apply(cur.numel(), wl.dtype, wl.act, cur, out, stream)
+        return out
 
 
-class FusedLinearAct:
+class FusedLinearAct(_FallbackLayer):
     """MatMul (x W^T, W in [out][in]) -> + bias -> activation, bf16 in/out."""
 
     def __init__(self, inp: dict, device="cuda", with_unfused=True):
@@ -125,27 +158,34 @@ class FusedLinearAct:
         self.y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=device)
         self.with_unfused = with_unfused
         if with_unfused:
+            self._unfused_buffers()
+
+    def _unfused_buffers(self):
+        if getattr(self, "t1", None) is None:
             self.t1 = torch.empty_like(self.y)
             self.t2 = torch.empty_like(self.y)
             self.y_unfused = torch.empty_like(self.y)
 
-    def forward(self, stream=None, y=None, residual=None):
-        out = self.y if y is None else y
+    def _fused(self, out, stream, residual=None):
         dlf_gemm_fused(self.desc, self.x, self.w, None, self.bias, residual, out, stream)
+
+    def forward_unfused(self, stream=None, y=None, residual=None):
+        wl = self.wl
+        self._unfused_buffers()
+        out = self.y_unfused if y is None else y
+        dlf_gemm_plain(self.desc_plain, self.x, self.w, 1.0, self.t1, stream)
+        cur, free = self.t1, self.t2
+        if self.bias is not None:
+            dlf_scale_shift_apply(wl.m, wl.n, "bf16", cur, None, self.bias, free, stream)
+            cur, free = free, cur
+        if residual is not None:
+            dlf_add(cur.numel(), "bf16", cur, residual, free, stream)
+            cur, free = free, cur
+        dlf_act_apply(cur.numel(), "bf16", wl.act, cur, out, stream)
         return out
 
-    def forward_unfused(self, stream=None):
-        wl = self.wl
-        dlf_gemm_plain(self.desc_plain, self.x, self.w, 1.0, self.t1, stream)
-        cur = self.t1
-        if self.bias is not None:
-            dlf_scale_shift_apply(wl.m, wl.n, "bf16", self.t1, None, self.bias, self.t2, stream)
-            cur = self.t2
-        dlf_act_apply(cur.numel(), "bf16", wl.act, cur, self.y_unfused, stream)
-        return self.y_unfused
 
-
-class Fp8LinearBNReluQuant:
+class Fp8LinearBNReluQuant(_FallbackLayer):
     """fp8 e4m3 MatMul with static scales -> folded BN scale/shift -> ReLU -> static e4m3 output."""
 
     def __init__(self, inp: dict, device="cuda", with_unfused=True):
@@ -164,68 +204,89 @@ class Fp8LinearBNReluQuant:
         self.alpha = torch.from_numpy(alpha).to(device)
         self.shift = torch.from_numpy(shift).to(device)
         self.y = torch.empty((wl.m, wl.n), dtype=torch.uint8, device=device)
+        self._inp, self._device = inp, device
         self.with_unfused = with_unfused
         if with_unfused:
-            self.bn = [torch.from_numpy(np.asarray(inp[k], np.float32)).to(device)
-                       for k in ("gamma", "beta", "mean", "var")]
-            self.eps = inp["eps"]
-            self.dequant = float(np.float32(float(self.s_x) * float(self.s_w)))
-            self.t1 = torch.empty((wl.m, wl.n), dtype=torch.float32, device=device)
-            self.t2 = torch.empty_like(self.t1)
-            self.y_unfused = torch.empty_like(self.y)
+            self._unfused_buffers()
 
-    def forward(self, stream=None, y=None):
-        out = self.y if y is None else y
+    def _unfused_buffers(self):
+        if getattr(self, "t1", None) is not None:
+            return
+        inp, wl, device = self._inp, self.wl, self._device
+        self.bn = [torch.from_numpy(np.asarray(inp[k], np.float32)).to(device)
+                   for k in ("gamma", "beta", "mean", "var")]
+        self.eps = inp["eps"]
+        self.dequant = float(np.float32(float(self.s_x) * float(self.s_w)))
+        self.t1 = torch.empty((wl.m, wl.n), dtype=torch.float32, device=device)
+        self.t2 = torch.empty_like(self.t1)
+        self.y_unfused = torch.empty_like(self.y)
+
+    def _fused(self, out, stream):
         dlf_gemm_fused(self.desc, self.x, self.w, self.alpha, self.shift, None, out, stream)
-        return out
 
-    def forward_unfused(self, stream=None):
+    def forward_unfused(self, stream=None, y=None):
         wl = self.wl
+        self._unfused_buffers()
+        out = self.y_unfused if y is None else y
         dlf_gemm_plain(self.desc_plain, self.x, self.w, self.dequant, self.t1, stream)
         dlf_bn_apply(wl.m, wl.n, "f32", self.t1, *self.bn, self.eps, self.t2, stream)
         dlf_act_apply(self.t2.numel(), "f32", "relu", self.t2, self.t2, stream)
-        dlf_quant_apply(self.t2.numel(), self.t2, self.inv_s_y, self.y_unfused, stream)
-        return self.y_unfused
+        dlf_quant_apply(self.t2.numel(), self.t2, self.inv_s_y, out, stream)
+        return out
 
 
-class FusedFFN:
+class FusedFFN(_FallbackLayer):
     """Transformer feed-forward block: dlf_ffn_fused_ws (weights packed once at load by
     dlf_ffn_pack, and the workspace its d_ff split asks for, allocated at load); the unfused
     form is FC1 (+ b1, act) and FC2 (+ b2, + residual) as two GEMMs with their own register
-    epilogues, the intermediate going through HBM."""
+    epilogues, the intermediate going through HBM.  A block the fused kernel is not built for
+    (d_model outside 256/512/768/1024, d_ff not a multiple of 256) runs the two GEMMs."""
 
     def __init__(self, inp: dict, device="cuda", with_unfused=True):
         wl = inp["workload"]
         self.wl = wl
         self.desc = ffn_desc(wl.m, wl.d_model, wl.d_ff, wl.act)
         self.x = to_device(inp["x"], "bf16", device)
-        self.w1p = to_device(dlf_ffn_pack(inp["w1"]), "bf16", device)
-        self.w2p = to_device(dlf_ffn_pack(inp["w2"]), "bf16", device)
         self.b1 = torch.from_numpy(inp["b1"]).to(device)
         self.b2 = torch.from_numpy(inp["b2"]).to(device)
         self.res = to_device(inp.get("residual"), "bf16", device)
         self.y = torch.empty((wl.m, wl.d_model), dtype=torch.bfloat16, device=device)
-        self.ws_bytes = dlf_ffn_workspace_bytes(self.desc)
+        self._inp, self._device = inp, device
+        try:
+            self.ws_bytes = dlf_ffn_workspace_bytes(self.desc)
+        except DlfError as e:
+            if e.status != DLF_ERR_UNSUPPORTED:
+                raise
+            self.fused_ok, self.unsupported, self.ws_bytes = False, e.detail, 0
+        if self.fused_ok:
+            self.w1p = to_device(dlf_ffn_pack(inp["w1"]), "bf16", device)
+            self.w2p = to_device(dlf_ffn_pack(inp["w2"]), "bf16", device)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) if self.ws_bytes else None
         self.with_unfused = with_unfused
-        if with_unfused:
-            self.w1 = to_device(inp["w1"], "bf16", device)
-            self.w2 = to_device(inp["w2"], "bf16", device)
-            self.desc1 = gemm_desc(wl.m, wl.d_ff, wl.d_model, "bf16", "bf16", wl.act)
-            self.desc2 = gemm_desc(wl.m, wl.d_model, wl.d_ff, "bf16", "bf16", "none")
-            self.h = torch.empty((wl.m, wl.d_ff), dtype=torch.bfloat16, device=device)
-            self.y_unfused = torch.empty_like(self.y)
+        if with_unfused or not self.fused_ok:
+            self._unfused_buffers()
 
-    def forward(self, stream=None, y=None):
-        out = self.y if y is None else y
+    def _unfused_buffers(self):
+        if getattr(self, "h", None) is not None:
+            return
+        inp, wl, device = self._inp, self.wl, self._device
+        self.w1 = to_device(inp["w1"], "bf16", device)
+        self.w2 = to_device(inp["w2"], "bf16", device)
+        self.desc1 = gemm_desc(wl.m, wl.d_ff, wl.d_model, "bf16", "bf16", wl.act)
+        self.desc2 = gemm_desc(wl.m, wl.d_model, wl.d_ff, "bf16", "bf16", "none")
+        self.h = torch.empty((wl.m, wl.d_ff), dtype=torch.bfloat16, device=device)
+        self.y_unfused = torch.empty_like(self.y)
+
+    def _fused(self, out, stream):
         dlf_ffn_fused_ws(self.desc, self.x, self.w1p, self.b1, self.w2p, self.b2, self.res, out, self.ws,
                          self.ws_bytes, stream)
-        return out
 
-    def forward_unfused(self, stream=None):
+    def forward_unfused(self, stream=None, y=None):
+        self._unfused_buffers()
+        out = self.y_unfused if y is None else y
         dlf_gemm_fused(self.desc1, self.x, self.w1, None, self.b1, None, self.h, stream)
-        dlf_gemm_fused(self.desc2, self.h, self.w2, None, self.b2, self.res, self.y_unfused, stream)
-        return self.y_unfused
+        dlf_gemm_fused(self.desc2, self.h, self.w2, None, self.b2, self.res, out, stream)
+        return out
 
 
 def make_layer(inp: dict, device="cuda", with_unfused=True):

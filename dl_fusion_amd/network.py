@@ -5,7 +5,10 @@ chosen chain's BatchNorm is folded into its conv (dlf_fold_bn, binary64, one rou
 bf16) and every tensor the plan keeps in memory gets its buffer.  forward() then only
 enqueues kernels: one dlf_conv_fused per chosen chain, and the separate conv / BN / Add /
 activation kernels for every op outside a chain.  With fuse=False every op runs on its own,
-which is the unfused network the fused one is measured against.
+which is the unfused network the fused one is measured against.  A chain the library answers
+with DLF_ERR_UNSUPPORTED (it launches nothing then) runs as its separate ops instead, through
+buffers of its own for the chain's inner tensors, from that call on ("OpenPPL算子融合深度解析"
+§4.2; the MindIE-SD RFC §3.7 falls back to the original graph).
 
 The graph format is the pass's (a list of node dicts in topological order: op, inputs,
 shape, dtype, flops, output, training, plus "attrs" with conv geometry and BN epsilon);
@@ -17,8 +20,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (conv_desc, dlf_act_apply, dlf_add, dlf_bn_apply, dlf_conv_fused, dlf_conv_plain,
-               dlf_fold_bn, dlf_fusion_plan)
+from . import (DLF_ERR_UNSUPPORTED, DlfError, conv_desc, dlf_act_apply, dlf_add, dlf_bn_apply, dlf_conv_fused,
+               dlf_conv_plain, dlf_fold_bn, dlf_fusion_plan)
 
 # MI355X: dense bf16 peak over HBM bandwidth (flops per byte), and the autofusion article's
 # fraction of a group's arithmetic charged as the cost of the bigger kernel
@@ -107,10 +110,25 @@ class Network:
             prev = nodes[nodes.index(add) - 1]
             res_src = [j for j in self.graph[add]["inputs"] if j != prev][0]
         out = nodes[-1]
+        fallback = []            # the chain's separate ops and its inner buffers, once needed
 
         def run(env, stream):
-            res = env[res_src] if res_src is not None else None
-            dlf_conv_fused(desc, env[x_src], w_d, bias_d, res, env[out], stream)
+            if not fallback:
+                res = env[res_src] if res_src is not None else None
+                try:
+                    dlf_conv_fused(desc, env[x_src], w_d, bias_d, res, env[out], stream)
+                    return
+                except DlfError as e:
+                    if e.status != DLF_ERR_UNSUPPORTED:
+                        raise
+                    inner = {i: torch.empty(self.graph[i]["shape"], dtype=torch.bfloat16, device=device)
+                             for i in nodes[:-1]}
+                    fallback.append(([self._single_step(i, params, device) for i in nodes], inner))
+            steps, inner = fallback[0]
+            local = dict(env)
+            local.update(inner)
+            for st in steps:
+                st(local, stream)
         return run
 
     def _single_step(self, i, params, device):

@@ -42,7 +42,9 @@
  *    outputs are valid and launch nothing.
  *  - The output must not overlap any input (DLF_ERR_ALIAS): every input
  *    element is read by many output tiles.
- *  - Thread safety: no global mutable state besides the thread-local error.
+ *  - Thread safety: no global mutable state besides the thread-local error and
+ *    the tuning switches, which are read once when the library loads (see
+ *    dlf_tuning_reload).
  */
 #ifndef DLFUSION_H
 #define DLFUSION_H
@@ -442,6 +444,19 @@ const char *dlf_status_string(dlf_status s);
 /* Detail of the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next library call on this thread. */
 const char *dlf_last_error(void);
+
+/* ---------------------------------------------------------------------- */
+/* Tuning switches                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Kernel routes and tiles can be forced for tuning and tests through the
+ * environment: DLF_TILE (an MFMA tile index), DLF_GEMM (tiled | stream),
+ * DLF_CONV (generic | stream), DLF_STREAM_NB (128 | 256 | 384), DLF_FFN_TOK
+ * (32 | 64) and DLF_FFN_SPLIT (d_ff parts; 0 or 1: none).  Forcing a route
+ * never changes a result beyond the order of fp32 sums.  The library reads
+ * them once when it is loaded; dlf_tuning_reload() reads them again.  Host
+ * only; it must not run concurrently with another library call. */
+void dlf_tuning_reload(void);
 
 #ifdef __cplusplus
 }
