@@ -118,6 +118,7 @@ _SIGS = {
     "dlf_ffn_workspace_bytes": [ctypes.POINTER(dlf_ffn_desc), ctypes.POINTER(ctypes.c_size_t)],
     "dlf_ffn_fused_ws": [ctypes.POINTER(dlf_ffn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                          _vp],
+    "dlf_clock_probe": [ctypes.c_int32, ctypes.c_int32, _vp, _vp],
     "dlf_fusion_plan": [ctypes.POINTER(dlf_graph_node), ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                         ctypes.POINTER(dlf_fusion_group), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
@@ -304,6 +305,11 @@ def dlf_ffn_fused_ws(desc, x, w1_packed, b1, w2_packed, b2, residual, y, workspa
     _check(_lib.dlf_ffn_fused_ws(ctypes.byref(desc), _dev(x), _dev(w1_packed), _dev(b1), _dev(w2_packed), _dev(b2),
                                  _dev(residual), _dev(y), _dev(workspace), int(workspace_bytes), _stream(stream)),
            "dlf_ffn_fused_ws")
+
+
+def dlf_clock_probe(workgroups, iters, stamps, stream=None):
+    """Enqueue the shader-clock probe; stamps: a device int64 tensor of 4 * workgroups values."""
+    _check(_lib.dlf_clock_probe(int(workgroups), int(iters), _dev(stamps), _stream(stream)), "dlf_clock_probe")
 
 
 def graph_nodes(graph):

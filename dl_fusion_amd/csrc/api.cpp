@@ -336,6 +336,14 @@ const char* dlf_last_error(void) { return g_last_error; }
 
 void dlf_tuning_reload(void) { dlf::reload_options(); }
 
+dlf_status dlf_clock_probe(int32_t workgroups, int32_t iters, uint64_t* stamps, void* stream) {
+    if (workgroups < 1 || workgroups > 65536 || iters < 1)
+        return fail(DLF_ERR_INVALID_ARG, "workgroups must be in [1, 65536] and iters >= 1");
+    if (!stamps || !aligned16(stamps)) return fail(DLF_ERR_INVALID_ARG, "stamps must be a 16-byte aligned device pointer");
+    return hip_status(dlf::launch_clock_probe(workgroups, iters, stamps, static_cast<hipStream_t>(stream)),
+                      "dlf_clock_probe");
+}
+
 dlf_status dlf_fold_bn(int64_t cout, int64_t k, const float* w, const float* conv_bias, const float* gamma,
                        const float* beta, const float* mean, const float* var, double eps,
                        dlf_dtype w_out_dtype, void* w_out, float* bias_out) {

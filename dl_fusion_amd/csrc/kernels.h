@@ -161,6 +161,10 @@ struct FfnArgs {
 int ffn_parts(int64_t M, int D, int F);
 hipError_t launch_ffn(const FfnArgs& args, int act, hipStream_t stream);
 
+// Shader-clock probe: workgroups x 4 waves of back-to-back bf16 MFMAs; stamps[4 b + 0..3] =
+// s_memtime before / after, s_memrealtime before / after, for workgroup b.
+hipError_t launch_clock_probe(int workgroups, int iters, uint64_t* stamps, hipStream_t stream);
+
 // Elementwise passes of the unfused chain.  dt: 0 fp32, 1 bf16.
 hipError_t launch_bn_apply(int64_t rows, int64_t c, int dt, const void* y, const float* gamma,
                            const float* beta, const float* mean, const float* var, float eps,

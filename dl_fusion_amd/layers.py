@@ -127,18 +127,20 @@ class FusedConvBNAct(_FallbackLayer):
     def rows(self):
         return self.wl.n * self.wl.ho * self.wl.wo
 
-    def _fused(self, out, stream, x=None):
-        dlf_conv_fused(self.desc, self.x if x is None else x, self.w, self.b, self.res, out, stream)
+    def _fused(self, out, stream, x=None, residual=None):
+        dlf_conv_fused(self.desc, self.x if x is None else x, self.w, self.b,
+                       self.res if residual is None else residual, out, stream)
 
-    def forward_unfused(self, stream=None, y=None, x=None):
+    def forward_unfused(self, stream=None, y=None, x=None, residual=None):
         wl = self.wl
         self._unfused_buffers()
         out = self.y_unfused if y is None else y
+        res = self.res if residual is None else residual
         dlf_conv_plain(self.desc_plain, self.x if x is None else x, self.w_raw, self.conv_bias, self.t1, stream)
         dlf_bn_apply(self.rows, wl.cout, wl.dtype, self.t1, *self.bn, self.eps, self.t2, stream)
         cur = self.t2
-        if self.res is not None:
-            dlf_add(self.t2.numel(), wl.dtype, self.t2, self.res, self.t1, stream)
+        if res is not None:
+            dlf_add(self.t2.numel(), wl.dtype, self.t2, res, self.t1, stream)
             cur = self.t1
         dlf_act_apply(cur.numel(), wl.dtype, wl.act, cur, out, stream)
         return out

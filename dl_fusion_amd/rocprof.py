@@ -79,9 +79,18 @@ def shown(cmd: list[str]) -> str:
     return "cd /tmp && " + " ".join(out)
 
 
-def bench_cmd(idx: int, steps: int, extra: list[str]) -> list[str]:
+def timing_mode(wl) -> str:
+    """The timing bench.py takes the workload's roofline from: the rotating-copy (cold) graph for
+    an HBM-bound conv workload, the graph over resident inputs otherwise."""
+    import bench  # noqa: E402
+    fused, _ = bench.bytes_model(wl)
+    hbm = fused / (bench.PEAK_HBM_GBS * 1e9) > bench.flops(wl) / (bench.PEAK_TFLOPS[wl.dtype] * 1e12)
+    return "cold" if hbm and wl.kind == "conv" and wl.dtype == "bf16" else "graph"
+
+
+def bench_cmd(idx: int, steps: int, extra: list[str], timing: str = "graph") -> list[str]:
     return [PYTHON, os.path.join(ROOT, "bench.py"), "--only", "--workload", str(idx),
-            "--steps", str(steps), "--warmup", "2", "--no-cpu", "--no-unfused"] + extra
+            "--steps", str(steps), "--warmup", "2", "--no-cpu", "--no-unfused", "--timing", timing] + extra
 
 
 def run(cmd: list[str], log: str, timeout: int) -> None:
@@ -157,7 +166,8 @@ def kernel_hash() -> str:
 def widened_rows_trace(rocprof: str, out: str, scratch: str, steps: int) -> None:
     d = os.path.join(scratch, "widened_trace")
     shutil.rmtree(d, ignore_errors=True)
-    prog = [PYTHON, os.path.join(ROOT, "bench.py"), "--steps", str(steps), "--warmup", "2", "--no-cpu"]
+    prog = [PYTHON, os.path.join(ROOT, "bench.py"), "--steps", str(steps), "--warmup", "2", "--no-cpu",
+            "--timing", "graph"]
     cmd = [rocprof, "--kernel-trace", "--stats", "-d", d, "-o", "t", "--"] + prog
     run(cmd, d + ".log", 600)
     rows = top_kernels(db_path(d))
@@ -208,7 +218,7 @@ def main() -> None:
             d = os.path.join(args.scratch, f"w{idx}_{ps}")
             shutil.rmtree(d, ignore_errors=True)
             if ps == "trace":
-                prog = bench_cmd(idx, args.steps, [])
+                prog = bench_cmd(idx, args.steps, [], timing_mode(wl))
                 cmd = [rocprof, "--kernel-trace", "--stats", "-d", d, "-o", "t", "--"] + prog
                 t0 = time.time()
                 run(cmd, d + ".log", 300)

@@ -458,6 +458,25 @@ const char *dlf_last_error(void);
  * only; it must not run concurrently with another library call. */
 void dlf_tuning_reload(void);
 
+/* ---------------------------------------------------------------------- */
+/* Measurement aid                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Shader-clock probe for a clock-derived matrix-core peak (the pages ask for
+ * each fused kernel's throughput against the hardware's limits: [OPPL] §5.2
+ * measures per-kernel DRAM throughput, [INFR] §1.2 places a fused op on the
+ * roofline).  Launches `workgroups` workgroups of four waves; each runs
+ * `iters` steps of four independent bf16 32x32x16 MFMAs and writes, for
+ * workgroup b,
+ *     stamps[4b + 0], stamps[4b + 1]  shader-clock counter before, after
+ *     stamps[4b + 2], stamps[4b + 3]  100 MHz constant counter before, after
+ * so that (s1 - s0) / (r1 - r0) * 100 MHz is the shader clock the chip held
+ * while its matrix pipes were busy.
+ *   workgroups  1 .. 65536; iters >= 1 (else DLF_ERR_INVALID_ARG)
+ *   stamps      device, 16-byte aligned, 4 * workgroups uint64 values
+ *   stream      hipStream_t or NULL; asynchronous like every launch */
+dlf_status dlf_clock_probe(int32_t workgroups, int32_t iters, uint64_t *stamps, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

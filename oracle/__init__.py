@@ -383,9 +383,11 @@ def fp8_gemm_bn_relu_quant(inp: dict, rows=None):
 # ---------------------------------------------------------------------------
 # Comparison metric shared by the parity tests
 # ---------------------------------------------------------------------------
-def rel_error(got, ref) -> float:
-    """max_i |g_i - o_i| / max(|o_i|, rms_c(o)): the relative error, floored at the rms of
-    the element's output channel c (the last axis; a 1-D array is one channel).
+def rel_error(got, ref, floor_of=None) -> float:
+    """max_i |g_i - o_i| / max(|o_i|, rms_c(f)): the relative error, floored at the rms of
+    the element's output channel c (the last axis; a 1-D array is one channel) of f = ref, or
+    of f = floor_of (same shape) where given: the value before the activation, for a step whose
+    activation follows every rounding of the method.
 
     A plain element-wise relative error is ill-posed where ReLU/GELU outputs are ~0, so
     it is floored.  The floor is per channel because the BN fold multiplies each output
@@ -400,7 +402,8 @@ def rel_error(got, ref) -> float:
     c = o.shape[-1] if o.ndim > 1 else 1
     g2 = g.reshape(-1, c)
     o2 = o.reshape(-1, c)
-    rms = np.sqrt(np.mean(o2 * o2, axis=0))
+    f2 = o2 if floor_of is None else np.asarray(floor_of, dtype=np.float64).reshape(-1, c)
+    rms = np.sqrt(np.mean(f2 * f2, axis=0))
     rms = np.where(rms > 0, rms, 1.0)
     den = np.maximum(np.abs(o2), rms[None, :])
     return float(np.max(np.abs(g2 - o2) / den))

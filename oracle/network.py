@@ -22,10 +22,11 @@ from . import activation, add, batchnorm, conv2d, round_bf16, widen
 _ACTS = {"relu": "relu", "gelu": "gelu_tanh", "gelu_erf": "gelu_erf"}
 
 
-def step(graph, params, vals, nodes):
+def step(graph, params, vals, nodes, with_pre=False):
     """The stored tensor that the step `nodes` (a fused chain in chain order, or [i] for an op
     on its own) produces, in binary64 and unrounded, from the stored tensors in `vals`
-    ({node: binary64 array})."""
+    ({node: binary64 array}).  with_pre: returns (pre, out), pre being the value the step's
+    activation is applied to (out itself for a step that ends in no activation)."""
     head = nodes[0]
     nd = graph[head]
     op = nd["op"]
@@ -39,9 +40,12 @@ def step(graph, params, vals, nodes):
     elif op == "add":
         y = add(src[0], src[1])
     elif op in _ACTS:
+        pre = src[0]
         y = activation(src[0], _ACTS[op])
     else:
         raise NotImplementedError(op)
+    if op not in _ACTS:
+        pre = y
     prev = head
     for i in nodes[1:]:
         op = graph[i]["op"]
@@ -52,11 +56,14 @@ def step(graph, params, vals, nodes):
             other = [j for j in graph[i]["inputs"] if j != prev][0]
             y = add(y, vals[other])
         elif op in _ACTS:
+            pre = y
             y = activation(y, _ACTS[op])
         else:
             raise NotImplementedError(op)
+        if op not in _ACTS:
+            pre = y
         prev = i
-    return y
+    return (pre, y) if with_pre else y
 
 
 def steps(graph, plan):

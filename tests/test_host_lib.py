@@ -362,3 +362,24 @@ def test_ffn_workspace_size_and_checks():
     assert run(R + 4096, need) == dlf.DLF_ERR_ALIAS              # overlaps the residual
     small = dlf.ffn_desc(0, 768, 3072)
     assert run(None, 0, d=small) == dlf.DLF_OK                   # empty: no launch
+
+
+@fake_pointers
+def test_clock_probe_validation_statuses():
+    raw = dlf.raw()
+    fake = ctypes.c_void_p(0x100000)
+    assert raw.dlf_clock_probe(0, 10, fake, None) == dlf.DLF_ERR_INVALID_ARG
+    assert raw.dlf_clock_probe(65537, 10, fake, None) == dlf.DLF_ERR_INVALID_ARG
+    assert raw.dlf_clock_probe(8, 0, fake, None) == dlf.DLF_ERR_INVALID_ARG
+    assert raw.dlf_clock_probe(8, 10, None, None) == dlf.DLF_ERR_INVALID_ARG
+    assert raw.dlf_clock_probe(8, 10, ctypes.c_void_p(0x100008), None) == dlf.DLF_ERR_INVALID_ARG
+
+
+def test_tuning_reload_reads_the_environment():
+    # a reload with and without a switch set is harmless on the host (no launch happens)
+    os.environ["DLF_TILE"] = "2"
+    try:
+        dlf.dlf_tuning_reload()
+    finally:
+        os.environ.pop("DLF_TILE", None)
+        dlf.dlf_tuning_reload()

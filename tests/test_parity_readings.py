@@ -15,6 +15,12 @@ meet while the alternative reading cannot:
   residual sum as bf16 tensors, which the fused kernel keeps in fp32 registers ("OpenPPL算子融合
   深度解析" §2.1: every elementwise op writes its tensor back).  Exact arithmetic with only those
   storage roundings already exceeds 2e-2 on the residual workload, and stays inside 4e-2.
+- R17, the pre-activation floor of a network step.  In a network whose BN statistics do not
+  centre each channel's conv output (random running statistics over post-ReLU inputs), ReLU
+  leaves some channels nearly empty: their rms after the activation is far below the size of
+  the values the method rounded.  The exact method misses 2e-2 there under the per-channel
+  floor of the output, and meets it with room under the per-channel floor of the value before
+  the activation, on every fused step of a ResNet stage.
 - R15, the row floor for fewer than 8 tokens.  With one or two tokens a column's rms is the
   element itself, so an output whose FC2 sum nearly cancels is judged on its own rounding:
   the exact FFN arithmetic (bf16 intermediate, bf16 output) fails the per-column floor there
@@ -120,3 +126,38 @@ def test_r15_column_floor_holds_from_a_few_dozen_tokens():
         wl = workloads.FfnWorkload(f"ffn_r15b_{i}", seed=54 + i, **kw)
         inp = workloads.generate(wl)
         assert oracle.rel_error(method_ffn_exact(inp), oracle.ffn(inp)) < 0.75 * BF16_TOL, i
+
+
+def test_r17_network_steps_need_the_pre_activation_floor():
+    from oracle import fusion as ofusion, network as onet
+    from workloads import graphs
+    g = graphs.resnet_stage_graph(n=1, h=56, w=56, cin=256, cmid=128, cout=512, stride=2, blocks=2)
+    params = graphs.draw_params(g, seed=7)
+    plan = ofusion.plan(g, 2516.6e12 / 8.0e12, 0.05)
+    bits = {j: workloads.bf16_bits(params[j]["x"]) for j, nd in enumerate(g) if nd["op"] == "input"}
+    vals = onet.forward(g, params, bits, plan)
+    worst_out, worst_pre = 0.0, 0.0
+    for j, nodes in onet.steps(g, plan).items():
+        c = nodes[0]
+        if g[c]["op"] != "conv":
+            continue
+        pre, ref = onet.step(g, params, vals, nodes, with_pre=True)
+        # the method's arithmetic for this step: fold, W' rounded once to bf16, exact sums
+        bn, a = nodes[1], g[c]["attrs"]
+        p = params[bn]
+        w_f, b_f = oracle.fold_bn(params[c]["w"], None, p["gamma"], p["beta"], p["mean"], p["var"],
+                                  g[bn]["attrs"]["eps"])
+        y = oracle.conv2d(vals[g[c]["inputs"][0]], oracle.round_bf16(w_f), b_f.astype(np.float32), a["stride"],
+                          a["pad"])
+        prev = bn
+        for i in nodes[2:]:
+            if g[i]["op"] == "add":
+                y = oracle.add(y, vals[[q for q in g[i]["inputs"] if q != prev][0]])
+            else:
+                y = oracle.activation(y, {"relu": "relu", "gelu": "gelu_tanh"}[g[i]["op"]])
+            prev = i
+        got = oracle.round_bf16(y)
+        worst_out = max(worst_out, oracle.rel_error(got, ref))
+        worst_pre = max(worst_pre, oracle.rel_error(got, ref, floor_of=pre))
+    assert worst_out > BF16_TOL, worst_out
+    assert worst_pre < 0.75 * BF16_TOL, worst_pre
