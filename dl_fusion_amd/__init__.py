@@ -118,6 +118,7 @@ _SIGS = {
     "dlf_ffn_workspace_bytes": [ctypes.POINTER(dlf_ffn_desc), ctypes.POINTER(ctypes.c_size_t)],
     "dlf_ffn_fused_ws": [ctypes.POINTER(dlf_ffn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                          _vp],
+    "dlf_ffn_fused_noalloc": [ctypes.POINTER(dlf_ffn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "dlf_clock_probe": [ctypes.c_int32, ctypes.c_int32, _vp, _vp],
     "dlf_fusion_plan": [ctypes.POINTER(dlf_graph_node), ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                         ctypes.POINTER(dlf_fusion_group), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
@@ -305,6 +306,16 @@ def dlf_ffn_fused_ws(desc, x, w1_packed, b1, w2_packed, b2, residual, y, workspa
     _check(_lib.dlf_ffn_fused_ws(ctypes.byref(desc), _dev(x), _dev(w1_packed), _dev(b1), _dev(w2_packed), _dev(b2),
                                  _dev(residual), _dev(y), _dev(workspace), int(workspace_bytes), _stream(stream)),
            "dlf_ffn_fused_ws")
+
+
+DLF_FFN_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def dlf_ffn_fused_noalloc(desc, x, w1_packed, b1, w2_packed, b2, residual, y, stream=None):
+    """dlf_ffn_fused_ws without a workspace: the split's partial sums use the library's static
+    device scratch (see include/dlfusion.h)."""
+    _check(_lib.dlf_ffn_fused_noalloc(ctypes.byref(desc), _dev(x), _dev(w1_packed), _dev(b1), _dev(w2_packed),
+                                      _dev(b2), _dev(residual), _dev(y), _stream(stream)), "dlf_ffn_fused_noalloc")
 
 
 def dlf_clock_probe(workgroups, iters, stamps, stream=None):

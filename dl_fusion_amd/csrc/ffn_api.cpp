@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dlfusion.h"
 #include "device_common.h"
@@ -160,5 +161,67 @@ extern "C" dlf_status dlf_ffn_fused_ws(const dlf_ffn_desc* d, const void* x, con
     }
     const hipError_t e = dlf::launch_ffn(a, act, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DLF_ERR_HIP, "dlf_ffn_fused_ws: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------------------------
+// No-allocation form: the d_ff split's fp32 partial sums go to a static device array instead of
+// a caller's workspace.  Each device the library runs on holds its own copy of the array until
+// the process ends; its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[DLF_FFN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of scratch on each device, once looked up
+
+dlf_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DLF_ERR_HIP, "dlf_ffn_fused_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DLF_ERR_UNSUPPORTED, "dlf_ffn_fused_noalloc: device %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(DLF_ERR_HIP, "dlf_ffn_fused_noalloc: hipGetSymbolAddress(scratch): %s",
+                        e != hipSuccess ? hipGetErrorString(e) : "null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+
+}  // namespace
+
+extern "C" dlf_status dlf_ffn_fused_noalloc(const dlf_ffn_desc* d, const void* x, const void* w1_packed,
+                                            const float* b1, const void* w2_packed, const float* b2,
+                                            const void* residual, void* y, void* stream) {
+    dlf::FfnArgs a;
+    int act = 0;
+    const dlf_status st = check_ffn(d, x, w1_packed, b1, w2_packed, b2, residual, y, &a, &act);
+    if (st != DLF_OK || d->m == 0) return st;
+    const size_t need = ffn_ws_bytes(d);
+    if (need > DLF_FFN_NOALLOC_SCRATCH_BYTES)
+        return fail(DLF_ERR_INVALID_ARG,
+                    "dlf_ffn_fused_noalloc: the d_ff split needs %zu bytes of scratch, the static scratch holds %zu "
+                    "(dlf_ffn_fused_ws takes a workspace of any size)",
+                    need, static_cast<size_t>(DLF_FFN_NOALLOC_SCRATCH_BYTES));
+    if (need > 0) {
+        void* ptr = nullptr;
+        const dlf_status sst = scratch_on_current_device(&ptr);
+        if (sst != DLF_OK) return sst;
+        // every partial sum is written before it is read: nothing needs clearing between calls
+        a.parts = ffn_split(d);
+        a.ws = static_cast<float*>(ptr);
+    }
+    const hipError_t e = dlf::launch_ffn(a, act, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DLF_ERR_HIP, "dlf_ffn_fused_noalloc: %s", hipGetErrorString(e));
     return ok();
 }

@@ -351,6 +351,28 @@ dlf_status dlf_ffn_fused_ws(const dlf_ffn_desc *d, const void *x, const void *w1
                             const void *residual, void *y, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* Bytes of the static device scratch behind dlf_ffn_fused_noalloc (32 MiB). */
+#define DLF_FFN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* dlf_ffn_fused_ws for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The d_ff split's partial sums go to a static device array of
+ * DLF_FFN_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends; the call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ *   - A block whose split needs more than DLF_FFN_NOALLOC_SCRATCH_BYTES
+ *     (dlf_ffn_workspace_bytes(d) tells) is rejected with
+ *     DLF_ERR_INVALID_ARG before anything is launched; use dlf_ffn_fused_ws.
+ *   - Every call on one device shares that device's array: calls that may
+ *     overlap on one device (concurrent streams, several host threads) race.
+ *     Its contents persist between calls; none is read before it is written.
+ *   - The first call on a device looks the array's address up (a HIP runtime
+ *     query, not an allocation); later calls reuse it.
+ * Every other argument, check, status and the result as dlf_ffn_fused_ws. */
+dlf_status dlf_ffn_fused_noalloc(const dlf_ffn_desc *d, const void *x, const void *w1_packed,
+                                 const float *b1, const void *w2_packed, const float *b2,
+                                 const void *residual, void *y, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Host fusion pass: which chains of a graph become one fused launch        */
 /* ---------------------------------------------------------------------- */
