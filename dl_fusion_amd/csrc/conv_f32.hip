@@ -1,14 +1,21 @@
 // fp32 direct convolution with the register epilogue (bias -> residual -> act).
 //
-// Used for fp32 layers (small, latency-bound shapes).  Each lane computes one
-// output element (pixel m, channel co); a workgroup covers 256/TC pixels x TC
-// channels, so even a 32x32x32 layer spreads over 128 workgroups.  The
-// workgroup's weights are staged in LDS transposed to [k][channel] in slices of
-// 4096 values (consecutive lanes read consecutive channels), together with the
-// im2col rows of its pixels (zero outside the image), each gathered by
-// independent loads so that a slice costs one memory round trip.  fp32
-// accumulation, then the epilogue of "OpenPPL算子融合深度解析" §4.3 before the
-// single store.
+// Used for fp32 layers (small, latency-bound shapes: a 1x32x32 16->32 3x3 layer is 9.4 MFLOP,
+// a few hundred cycles of FMA work spread over the chip, so its time is launch, one memory
+// round trip and the store).  Each lane computes one output element (pixel m, channel co);
+// a workgroup covers 256/TC pixels x TC channels.
+//
+// conv_f32_regw_kernel (K <= 256, Cin a multiple of 4): one pass.  Each lane loads its
+// channel's K weights straight into registers with 16-byte loads while the workgroup gathers
+// the receptive fields of its pixels into LDS (one 16-byte load per tap and 4 channels, zero
+// outside the image); after one barrier a lane reads 4 input values per LDS read (the lanes of
+// a pixel read the same address) for 4 FMAs against its registers.
+//
+// conv_f32_kernel (any other shape): weights staged in LDS transposed to [k][channel] in
+// slices of 4096 values, together with the im2col rows of its pixels, each gathered by
+// independent loads so that a slice costs one memory round trip.
+//
+// fp32 accumulation, then the epilogue of "OpenPPL算子融合深度解析" §4.3 before the single store.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -69,6 +76,80 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
     p.y[idx] = activate<ACT>(v);
 }
 
+// K <= KMAX (a multiple of 4), Cin % 4 == 0.  256 lanes: 8 pixels x 32 channels.
+template <int KMAX, int ACT>
+__global__ __launch_bounds__(256) void conv_f32_regw_kernel(const ConvF32Args p) {
+    constexpr int TC = 32, PPB = 8, K4 = KMAX / 4;
+    __shared__ f32x4_t xs[PPB][K4];
+    const int tid = static_cast<int>(threadIdx.x);
+    const int co_l = tid % TC, pl = tid / TC;
+    const int m0 = static_cast<int>(blockIdx.x) * PPB;
+    const int co = static_cast<int>(blockIdx.y) * TC + co_l;
+    const int k4n = p.K >> 2;
+    // this lane's weights (a row of K values, 16-byte aligned: K % 4 == 0); rows past Cout
+    // read row 0 and their results are never stored
+    const f32x4_t* wrow = reinterpret_cast<const f32x4_t*>(p.w + static_cast<int64_t>(co < p.Cout ? co : 0) * p.K);
+    f32x4_t wr[K4];
+#pragma unroll
+    for (int q = 0; q < K4; ++q) wr[q] = q < k4n ? wrow[q] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // receptive fields of the workgroup's pixels: item e = (pixel, 4 consecutive k), one tap each
+    const int hw = p.Ho * p.Wo;
+    const int c4 = p.Cin >> 2;
+    for (int e = tid; e < PPB * k4n; e += 256) {
+        const int q = e / k4n, kk4 = e - q * k4n;
+        const int m = m0 + q;
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (m < p.M) {
+            const int img = m / hw, rem = m - img * hw;
+            const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
+            const int tap = kk4 / c4, ci = (kk4 - tap * c4) * 4;
+            const int r = tap / p.KW, sx = tap - r * p.KW;
+            const int hi = ho * p.SH - p.PH + r, wi = wo * p.SW - p.PW + sx;
+            if (static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                static_cast<unsigned>(wi) < static_cast<unsigned>(p.W))
+                v = *reinterpret_cast<const f32x4_t*>(p.x + ((static_cast<int64_t>(img) * p.H + hi) * p.W + wi) * p.Cin + ci);
+        }
+        xs[q][kk4] = v;
+    }
+    __syncthreads();
+    float acc0 = 0.0f, acc1 = 0.0f;    // two chains: even and odd k
+#pragma unroll
+    for (int q = 0; q < K4; ++q) {
+        if (q < k4n) {
+            const f32x4_t xv = xs[pl][q];
+            acc0 = fmaf(xv[0], wr[q][0], acc0);
+            acc1 = fmaf(xv[1], wr[q][1], acc1);
+            acc0 = fmaf(xv[2], wr[q][2], acc0);
+            acc1 = fmaf(xv[3], wr[q][3], acc1);
+        }
+    }
+    const int m = m0 + pl;
+    if (m >= p.M || co >= p.Cout) return;
+    const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
+    float v = (acc0 + acc1) + (p.bias ? p.bias[co] : 0.0f);
+    if (p.res) v += p.res[idx];
+    p.y[idx] = activate<ACT>(v);
+}
+
+template <int KMAX>
+hipError_t launch_regw(const ConvF32Args& a, int act, hipStream_t s) {
+    const int64_t gx = (a.M + 7) / 8;
+    const int gy = (a.Cout + 31) / 32;
+    if (gx == 0 || gy == 0) return hipSuccess;
+    if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+    switch (act) {
+        case kActNone: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActNone>), grid, dim3(256), 0, s, a); break;
+        case kActRelu: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActRelu>), grid, dim3(256), 0, s, a); break;
+        case kActGelu: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActGelu>), grid, dim3(256), 0, s, a); break;
+        case kActGeluErf:
+            hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActGeluErf>), grid, dim3(256), 0, s, a);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int TC>
 hipError_t launch_tc(const ConvF32Args& a, int act, hipStream_t s) {
     constexpr int PPB = 256 / TC;
@@ -90,6 +171,13 @@ hipError_t launch_tc(const ConvF32Args& a, int act, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_conv_f32(const ConvF32Args& a, int act, hipStream_t s) {
+    // the register path wants 16-byte rows of x and w (Cin % 4 == 0) and K <= 256; x, w, y are
+    // 16-byte aligned (checked on the host)
+    if (a.Cin % 4 == 0 && a.K > 0 && a.K <= 256) {
+        if (a.K <= 64) return launch_regw<64>(a, act, s);
+        if (a.K <= 160) return launch_regw<160>(a, act, s);
+        return launch_regw<256>(a, act, s);
+    }
     return a.Cout <= 32 ? launch_tc<32>(a, act, s) : launch_tc<64>(a, act, s);
 }
 

@@ -314,6 +314,11 @@ RAGGED_F32 = [
     dict(n=1, h=5, w=5, cin=16, cout=70, kh=1, kw=1, stride=1, pad=0, act="gelu_tanh", residual=True),
     dict(n=3, h=11, w=6, cin=7, cout=33, kh=5, kw=3, stride=1, pad=2, act="none", residual=False),
     dict(n=2, h=6, w=9, cin=12, cout=40, kh=3, kw=3, stride=1, pad=1, act="gelu_erf", residual=True),
+    # the register-weight path at its largest K (252) with stride 2, and a 1x1 with K = 4
+    dict(n=3, h=13, w=10, cin=28, cout=96, kh=3, kw=3, stride=2, pad=1, act="gelu_tanh", residual=False),
+    dict(n=2, h=7, w=5, cin=4, cout=31, kh=1, kw=1, stride=1, pad=0, act="relu", residual=True),
+    # K = 260 just past it (the sliced kernel)
+    dict(n=1, h=6, w=6, cin=52, cout=20, kh=1, kw=5, stride=1, pad=2, act="relu", residual=False),
 ]
 
 
