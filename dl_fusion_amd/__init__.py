@@ -18,7 +18,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdlfusion.so")
+# DLF_LIBRARY names another build of the same library (the sanitizer build of the host code the
+# CPU test-suite runs under); by default the in-tree build
+LIB_PATH = os.environ.get("DLF_LIBRARY") or os.path.join(_HERE, "libdlfusion.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -137,6 +137,172 @@ struct Frag<1> {   // fp8 e4m3: 64 K per MFMA; a lane supplies 32 values (two ch
     }
 };
 
+// The register epilogue and the store of one output tile: acc[j][i] of wave (wm, wn) holds
+// rows m0 + wm*WTM + 32 i + (lane & 31) and, in register group g = e/4, columns
+// n0 + wn*WTN + 32 j + 8 g + 4 (lane/32) + e%4.  Every wave of the workgroup calls it after its
+// last LDS read of operands: the LDS (smem) is then reused to stage the rounded tile.
+template <class TS, int AMODE, int ACT, int OUT>
+__device__ __forceinline__ void mma_epilogue(const MmaArgs& p, f32x16_t (&acc)[TS::FN][TS::FM], uint8_t* smem,
+                                             const int wm, const int wn, const int lane, const int tid,
+                                             const int64_t m0, const int n0) {
+    const int64_t M = p.M;
+    const int N = p.N;
+    // ---- epilogue.  Lane holds output row  m = m0 + wm*WTM + 32 i + (lane & 31)  and, in
+    //      register group g = e/4, columns  n = n0 + wn*WTN + 32 j + 8 g + 4 (lane/32) + e%4 ----
+    const int lrow = lane & 31, half = lane >> 5;
+    if constexpr (OUT == kOutF32) {
+        // fp32 result of the plain fp8 GEMM: acc * dequant, stored directly (16 B per lane-group)
+#pragma unroll
+        for (int j = 0; j < TS::FN; ++j)
+#pragma unroll
+            for (int i = 0; i < TS::FM; ++i) {
+                const int64_t m = m0 + wm * TS::WTM + 32 * i + lrow;
+                if (m >= M) continue;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * TS::WTN + 32 * j + 8 * g + 4 * half;
+                    float* dst = static_cast<float*>(p.c) + m * N + n;
+                    if (n + 3 < N && (N & 3) == 0) {
+                        f32x4_t v;
+                        for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e] * p.dequant;
+                        *reinterpret_cast<f32x4_t*>(dst) = v;
+                    } else {
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) dst[e] = acc[j][i][4 * g + e] * p.dequant;
+                    }
+                }
+            }
+        return;
+    } else {
+        constexpr int OB = OUT == kOutFp8 ? 1 : 2;            // output bytes per element
+        // gated: columns (2j, 2j+1) are (gate j, up j) and give output column j
+        constexpr bool GATED = ACT >= kActSiluMul;
+        static_assert(!GATED || (OUT == kOutBf16 && AMODE != kConvAligned && AMODE != kConvGeneric &&
+                                 AMODE != kConvAnyC),
+                      "gated epilogue: dense bf16 output");
+        constexpr int SROW = (GATED ? TS::BN / 2 : TS::BN) * OB;   // staging row bytes
+        constexpr int CPR = SROW / 16;                        // 16-byte chunks per staged row
+        // staged chunk cc of row r lives at chunk cc ^ (r & XM): the 16 rows written by one
+        // store instruction land in distinct bank groups instead of one
+        constexpr int XM = (CPR < 16 ? CPR : 16) - 1;
+        __syncthreads();   // all waves are done reading operand slices: the LDS is reused for staging
+        const float* const scale = p.scale;
+        const float* const shift = p.shift;
+        const int64_t m_last = M - 1;
+        const int n_last4 = N >= 4 ? N - 4 : 0;
+#pragma unroll
+        for (int j = 0; j < TS::FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * TS::WTN + 32 * j + 8 * g + 4 * half;   // first of 4 columns
+                const int n = n0 + nl;
+                // per-column parameters; columns past N read a clamped (valid) address and
+                // their results are never written out
+                float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if ((N & 3) == 0) {   // n % 4 == 0: the run of four is entirely in or past N
+                    const int nc = min(n, n_last4);
+                    if (scale) {
+                        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(scale + nc);
+                        sc[0] = t[0]; sc[1] = t[1]; sc[2] = t[2]; sc[3] = t[3];
+                    }
+                    if (shift) {
+                        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(shift + nc);
+                        sh[0] = t[0]; sh[1] = t[1]; sh[2] = t[2]; sh[3] = t[3];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int nc = min(n + e, N - 1);
+                        if (scale) sc[e] = scale[nc];
+                        if (shift) sh[e] = shift[nc];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < TS::FM; ++i) {
+                    const int ml = wm * TS::WTM + 32 * i + lrow;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = acc[j][i][4 * g + e];
+                        v[e] = scale ? fmaf(t, sc[e], sh[e]) : t + sh[e];
+                    }
+                    if (!GATED && p.res != nullptr) {
+                        const int64_t mc = min(m0 + ml, m_last);
+                        if ((N & 3) == 0) {   // 8-byte aligned run of four
+                            const uint2 t = *reinterpret_cast<const uint2*>(p.res + mc * N + min(n, n_last4));
+                            v[0] += __uint_as_float(t.x << 16);
+                            v[1] += __uint_as_float(t.x & 0xFFFF0000u);
+                            v[2] += __uint_as_float(t.y << 16);
+                            v[3] += __uint_as_float(t.y & 0xFFFF0000u);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.res[mc * N + min(n + e, N - 1)]);
+                        }
+                    }
+                    if constexpr (GATED) {
+                        // output columns nl/2 and nl/2 + 1 (nl % 4 == 0): one 4-byte staging write
+                        const int cb = (nl >> 1) * OB;
+                        uint8_t* dst = smem + ml * SROW + ((((cb >> 4) ^ (ml & XM))) << 4) + (cb & 15);
+                        *reinterpret_cast<uint32_t*>(dst) =
+                            pack_bf16x2(gate_act<ACT>(v[0]) * v[1], gate_act<ACT>(v[2]) * v[3]);
+                        continue;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                    const int cb = nl * OB;                               // byte column in the row
+                    uint8_t* dst = smem + ml * SROW + ((((cb >> 4) ^ (ml & XM))) << 4) + (cb & 15);
+                    if constexpr (OUT == kOutFp8) {
+                        *reinterpret_cast<uint32_t*>(dst) = quant_e4m3_x4(v[0], v[1], v[2], v[3], p.out_inv_scale);
+                    } else {
+                        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                                            (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+                                            (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // coalesced write-out: 16-byte chunks of the staged tile, row-major
+        if (!GATED && p.parts > 1) {
+            // split store: a chunk lies in one part (the part width is a whole number of chunks)
+            const int pc = p.part_cols;
+            for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
+                const int ml = q / CPR, cc = q - ml * CPR;
+                const int64_t m = m0 + ml;
+                const int n = n0 + cc * (16 / OB);
+                if (m >= M || n >= N) continue;
+                const int part = (n >= pc) + (n >= 2 * pc) + (n >= 3 * pc);
+                uint8_t* const base = static_cast<uint8_t*>(part == 0 ? p.outs[0] : part == 1 ? p.outs[1]
+                                                            : part == 2 ? p.outs[2] : p.outs[3]);
+                *reinterpret_cast<u32x4_t*>(base + (m * pc + (n - part * pc)) * OB) =
+                    *reinterpret_cast<const u32x4_t*>(smem + ml * SROW + ((cc ^ (ml & XM)) << 4));
+            }
+            return;
+        }
+        const int NO = GATED ? N / 2 : N;                     // output columns
+        const int no0 = GATED ? n0 / 2 : n0;                  // first output column of the tile
+        const bool vec_ok = ((static_cast<int64_t>(NO) * OB) & 15) == 0;
+        uint8_t* const cbytes = static_cast<uint8_t*>(p.c);
+        for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
+            const int ml = q / CPR, cc = q - ml * CPR;
+            const int64_t m = m0 + ml;
+            const int nl = cc * (16 / OB);
+            const int n = no0 + nl;
+            if (m >= M || n >= NO) continue;
+            const uint8_t* src = smem + ml * SROW + ((cc ^ (ml & XM)) << 4);
+            uint8_t* dst = cbytes + (m * NO + n) * OB;
+            if (vec_ok && n + 16 / OB <= NO) {
+                *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+            } else {
+                const int cnt = min(16 / OB, NO - n) * OB;
+                for (int b = 0; b < cnt; ++b) dst[b] = src[b];
+            }
+        }
+    }
+}
+
 template <int ELEM, class TS, int AMODE, int ACT, int OUT>
 __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const int tiles_m,
                                                           const int tiles_n) {
@@ -437,160 +603,7 @@ __global__ __launch_bounds__(TS::NT, 1) void mma_kernel(const MmaArgs p, const i
         }
     }
 
-    // ---- epilogue.  Lane holds output row  m = m0 + wm*WTM + 32 i + (lane & 31)  and, in
-    //      register group g = e/4, columns  n = n0 + wn*WTN + 32 j + 8 g + 4 (lane/32) + e%4 ----
-    const int lrow = lane & 31, half = lane >> 5;
-    if constexpr (OUT == kOutF32) {
-        // fp32 result of the plain fp8 GEMM: acc * dequant, stored directly (16 B per lane-group)
-#pragma unroll
-        for (int j = 0; j < TS::FN; ++j)
-#pragma unroll
-            for (int i = 0; i < TS::FM; ++i) {
-                const int64_t m = m0 + wm * TS::WTM + 32 * i + lrow;
-                if (m >= M) continue;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * TS::WTN + 32 * j + 8 * g + 4 * half;
-                    float* dst = static_cast<float*>(p.c) + m * N + n;
-                    if (n + 3 < N && (N & 3) == 0) {
-                        f32x4_t v;
-                        for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e] * p.dequant;
-                        *reinterpret_cast<f32x4_t*>(dst) = v;
-                    } else {
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) dst[e] = acc[j][i][4 * g + e] * p.dequant;
-                    }
-                }
-            }
-        return;
-    } else {
-        constexpr int OB = OUT == kOutFp8 ? 1 : 2;            // output bytes per element
-        // gated: columns (2j, 2j+1) are (gate j, up j) and give output column j
-        constexpr bool GATED = ACT >= kActSiluMul;
-        static_assert(!GATED || (OUT == kOutBf16 && AMODE != kConvAligned && AMODE != kConvGeneric &&
-                                 AMODE != kConvAnyC),
-                      "gated epilogue: dense bf16 output");
-        constexpr int SROW = (GATED ? TS::BN / 2 : TS::BN) * OB;   // staging row bytes
-        constexpr int CPR = SROW / 16;                        // 16-byte chunks per staged row
-        // staged chunk cc of row r lives at chunk cc ^ (r & XM): the 16 rows written by one
-        // store instruction land in distinct bank groups instead of one
-        constexpr int XM = (CPR < 16 ? CPR : 16) - 1;
-        __syncthreads();   // all waves are done reading operand slices: the LDS is reused for staging
-        const float* const scale = p.scale;
-        const float* const shift = p.shift;
-        const int64_t m_last = M - 1;
-        const int n_last4 = N >= 4 ? N - 4 : 0;
-#pragma unroll
-        for (int j = 0; j < TS::FN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * TS::WTN + 32 * j + 8 * g + 4 * half;   // first of 4 columns
-                const int n = n0 + nl;
-                // per-column parameters; columns past N read a clamped (valid) address and
-                // their results are never written out
-                float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if ((N & 3) == 0) {   // n % 4 == 0: the run of four is entirely in or past N
-                    const int nc = min(n, n_last4);
-                    if (scale) {
-                        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(scale + nc);
-                        sc[0] = t[0]; sc[1] = t[1]; sc[2] = t[2]; sc[3] = t[3];
-                    }
-                    if (shift) {
-                        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(shift + nc);
-                        sh[0] = t[0]; sh[1] = t[1]; sh[2] = t[2]; sh[3] = t[3];
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int nc = min(n + e, N - 1);
-                        if (scale) sc[e] = scale[nc];
-                        if (shift) sh[e] = shift[nc];
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < TS::FM; ++i) {
-                    const int ml = wm * TS::WTM + 32 * i + lrow;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float t = acc[j][i][4 * g + e];
-                        v[e] = scale ? fmaf(t, sc[e], sh[e]) : t + sh[e];
-                    }
-                    if (!GATED && p.res != nullptr) {
-                        const int64_t mc = min(m0 + ml, m_last);
-                        if ((N & 3) == 0) {   // 8-byte aligned run of four
-                            const uint2 t = *reinterpret_cast<const uint2*>(p.res + mc * N + min(n, n_last4));
-                            v[0] += __uint_as_float(t.x << 16);
-                            v[1] += __uint_as_float(t.x & 0xFFFF0000u);
-                            v[2] += __uint_as_float(t.y << 16);
-                            v[3] += __uint_as_float(t.y & 0xFFFF0000u);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.res[mc * N + min(n + e, N - 1)]);
-                        }
-                    }
-                    if constexpr (GATED) {
-                        // output columns nl/2 and nl/2 + 1 (nl % 4 == 0): one 4-byte staging write
-                        const int cb = (nl >> 1) * OB;
-                        uint8_t* dst = smem + ml * SROW + ((((cb >> 4) ^ (ml & XM))) << 4) + (cb & 15);
-                        *reinterpret_cast<uint32_t*>(dst) =
-                            pack_bf16x2(gate_act<ACT>(v[0]) * v[1], gate_act<ACT>(v[2]) * v[3]);
-                        continue;
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
-                    const int cb = nl * OB;                               // byte column in the row
-                    uint8_t* dst = smem + ml * SROW + ((((cb >> 4) ^ (ml & XM))) << 4) + (cb & 15);
-                    if constexpr (OUT == kOutFp8) {
-                        *reinterpret_cast<uint32_t*>(dst) = quant_e4m3_x4(v[0], v[1], v[2], v[3], p.out_inv_scale);
-                    } else {
-                        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[0])) |
-                                            (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-                        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[2])) |
-                                            (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-                        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        // coalesced write-out: 16-byte chunks of the staged tile, row-major
-        if (!GATED && p.parts > 1) {
-            // split store: a chunk lies in one part (the part width is a whole number of chunks)
-            const int pc = p.part_cols;
-            for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
-                const int ml = q / CPR, cc = q - ml * CPR;
-                const int64_t m = m0 + ml;
-                const int n = n0 + cc * (16 / OB);
-                if (m >= M || n >= N) continue;
-                const int part = (n >= pc) + (n >= 2 * pc) + (n >= 3 * pc);
-                uint8_t* const base = static_cast<uint8_t*>(part == 0 ? p.outs[0] : part == 1 ? p.outs[1]
-                                                            : part == 2 ? p.outs[2] : p.outs[3]);
-                *reinterpret_cast<u32x4_t*>(base + (m * pc + (n - part * pc)) * OB) =
-                    *reinterpret_cast<const u32x4_t*>(smem + ml * SROW + ((cc ^ (ml & XM)) << 4));
-            }
-            return;
-        }
-        const int NO = GATED ? N / 2 : N;                     // output columns
-        const int no0 = GATED ? n0 / 2 : n0;                  // first output column of the tile
-        const bool vec_ok = ((static_cast<int64_t>(NO) * OB) & 15) == 0;
-        uint8_t* const cbytes = static_cast<uint8_t*>(p.c);
-        for (int q = tid; q < TS::BM * CPR; q += TS::NT) {
-            const int ml = q / CPR, cc = q - ml * CPR;
-            const int64_t m = m0 + ml;
-            const int nl = cc * (16 / OB);
-            const int n = no0 + nl;
-            if (m >= M || n >= NO) continue;
-            const uint8_t* src = smem + ml * SROW + ((cc ^ (ml & XM)) << 4);
-            uint8_t* dst = cbytes + (m * NO + n) * OB;
-            if (vec_ok && n + 16 / OB <= NO) {
-                *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
-            } else {
-                const int cnt = min(16 / OB, NO - n) * OB;
-                for (int b = 0; b < cnt; ++b) dst[b] = src[b];
-            }
-        }
-    }
+    mma_epilogue<TS, AMODE, ACT, OUT>(p, acc, smem, wm, wn, lane, tid, m0, n0);
 }
 
 // The tiles the library chooses from (api.cpp, pick_tile): the eight-wave 256 x 256 tile with

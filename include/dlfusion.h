@@ -56,7 +56,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are int-sized.  A C++ translation unit gives them int as their fixed
+ * underlying type, so that every int a C caller passes is a value of the type (an unknown code
+ * is then a checked error, never undefined behaviour). */
+#ifdef __cplusplus
+#define DLF_ENUM enum : int
+#else
+#define DLF_ENUM enum
+#endif
+
+typedef DLF_ENUM {
     DLF_OK = 0,
     DLF_ERR_INVALID_ARG = -1,   /* null / negative / non-finite / misaligned argument */
     DLF_ERR_UNSUPPORTED = -2,   /* no fused kernel for this combination: run the unfused chain */
@@ -64,7 +73,7 @@ typedef enum {
     DLF_ERR_ALIAS = -4          /* the output overlaps an input */
 } dlf_status;
 
-typedef enum {
+typedef DLF_ENUM {
     DLF_F32 = 0,                /* IEEE binary32 */
     DLF_BF16 = 1,               /* bfloat16, stored as uint16 bit patterns */
     DLF_FP8_E4M3 = 2            /* OCP e4m3fn codes (uint8): max 448, no inf, S.1111.111 = NaN */
@@ -76,7 +85,7 @@ typedef enum {
  * v Phi(v) = 0.5 v (1 + erf(v / sqrt(2))), the erf type beside tanh in [RFC]
  * §2.1 and §2.4.  Every activation is available to every fused path; on the fp8
  * GEMM the GELU forms give the quantised MatMul + GELU of [RFC] §2.1. */
-typedef enum {
+typedef DLF_ENUM {
     DLF_ACT_NONE = 0,
     DLF_ACT_RELU = 1,
     DLF_ACT_GELU_TANH = 2,
@@ -87,7 +96,7 @@ typedef enum {
  * SILU gives SwiGLU (silu(g) = g / (1 + e^-g); [RFC] §2.2 GMM + SwiGLU, §2.3
  * the gated Linear form); the GELU forms give GELU x Mul ([RFC] §2.4,
  * gelu(x) * y). */
-typedef enum {
+typedef DLF_ENUM {
     DLF_GATE_SILU = 0,
     DLF_GATE_GELU_TANH = 1,
     DLF_GATE_GELU_ERF = 2
@@ -379,7 +388,7 @@ dlf_status dlf_ffn_fused_noalloc(const dlf_ffn_desc *d, const void *x, const voi
 
 /* Operation of a graph node.  The pass fuses a contraction (CONV, MATMUL,
  * MATMUL_FP8) with the epilogue ops that follow it; every other op is kept. */
-typedef enum {
+typedef DLF_ENUM {
     DLF_OP_INPUT = 0,           /* a tensor that no node computes */
     DLF_OP_CONV = 1,
     DLF_OP_MATMUL = 2,

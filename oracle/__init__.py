@@ -29,7 +29,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c (the sanitizer build); by default the in-tree one
+_LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(HERE, "liboracle.so")
 _lib = None
 
 _i64 = ctypes.c_int64

@@ -1031,11 +1031,16 @@ def test_ffn_split_over_d_ff(split):
     second kernel adding them with b2 and the residual): forced to 2 and 3 parts, off
     (DLF_FFN_SPLIT), and the library's own choice (as many parts as fit 256 workgroups, at
     most one a chunk), on ragged token counts, every d_model it is built for and chunk counts that do
-    not divide evenly; the workspace has a guard band.  The third case has no biases."""
+    not divide evenly; the workspace has a guard band.  The third case has no biases.  Unsplit,
+    the 64-token workgroup is forced (DLF_FFN_TOK), so its walk over several d_ff chunks (the
+    single h buffer behind a second barrier) runs on ragged token tails at d_model 256, 512 and
+    768."""
     cases = [dict(m=150, d_model=768, d_ff=768, act="gelu_tanh", residual=True),
-             dict(m=65, d_model=256, d_ff=512, act="relu", residual=False),
+             dict(m=200, d_model=256, d_ff=1024, act="relu", residual=False),
              dict(m=300, d_model=512, d_ff=1280, act="gelu_erf", residual=True)]
     d = dlf()
+    if split == "0":
+        ENV["DLF_FFN_TOK"] = "64"
     if split != "auto":
         ENV["DLF_FFN_SPLIT"] = split
     try:
@@ -1064,3 +1069,4 @@ def test_ffn_split_over_d_ff(split):
             assert err <= TOL["bf16"], (split, i, err)
     finally:
         ENV.pop("DLF_FFN_SPLIT", None)
+        ENV.pop("DLF_FFN_TOK", None)
