@@ -5,7 +5,7 @@
 // round trip and the store).  Each lane computes one output element (pixel m, channel co);
 // a workgroup covers 256/TC pixels x TC channels.
 //
-// conv_f32_regw_kernel (K <= 256, Cin a multiple of 4): one pass.  Each lane loads its
+// conv_f32_regw_kernel (K <= 256, Cin a multiple of 4): one pass, 32 x PPB lanes.  Each lane loads its
 // channel's K weights straight into registers with 16-byte loads while the workgroup gathers
 // the receptive fields of its pixels into LDS (one 16-byte load per tap and 4 channels, zero
 // outside the image); after one barrier a lane reads 4 input values per LDS read (the lanes of
@@ -76,10 +76,10 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
     p.y[idx] = activate<ACT>(v);
 }
 
-// K <= KMAX (a multiple of 4), Cin % 4 == 0.  256 lanes: 8 pixels x 32 channels.
-template <int KMAX, int ACT>
-__global__ __launch_bounds__(256) void conv_f32_regw_kernel(const ConvF32Args p) {
-    constexpr int TC = 32, PPB = 8, K4 = KMAX / 4;
+// K <= KMAX (a multiple of 4), Cin % 4 == 0.  32 PPB lanes: PPB pixels x 32 channels.
+template <int KMAX, int PPB, int ACT>
+__global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Args p) {
+    constexpr int TC = 32, K4 = KMAX / 4, NT = 32 * PPB;
     __shared__ f32x4_t xs[PPB][K4];
     const int tid = static_cast<int>(threadIdx.x);
     const int co_l = tid % TC, pl = tid / TC;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void conv_f32_regw_kernel(const ConvF32Args p)
     // receptive fields of the workgroup's pixels: item e = (pixel, 4 consecutive k), one tap each
     const int hw = p.Ho * p.Wo;
     const int c4 = p.Cin >> 2;
-    for (int e = tid; e < PPB * k4n; e += 256) {
+    for (int e = tid; e < PPB * k4n; e += NT) {
         const int q = e / k4n, kk4 = e - q * k4n;
         const int m = m0 + q;
         f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -131,23 +131,34 @@ __global__ __launch_bounds__(256) void conv_f32_regw_kernel(const ConvF32Args p)
     p.y[idx] = activate<ACT>(v);
 }
 
-template <int KMAX>
-hipError_t launch_regw(const ConvF32Args& a, int act, hipStream_t s) {
-    const int64_t gx = (a.M + 7) / 8;
+template <int KMAX, int PPB>
+hipError_t launch_regw_ppb(const ConvF32Args& a, int act, hipStream_t s) {
+    const int64_t gx = (a.M + PPB - 1) / PPB;
     const int gy = (a.Cout + 31) / 32;
     if (gx == 0 || gy == 0) return hipSuccess;
     if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), block(32 * PPB);
     switch (act) {
-        case kActNone: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActNone>), grid, dim3(256), 0, s, a); break;
-        case kActRelu: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActRelu>), grid, dim3(256), 0, s, a); break;
-        case kActGelu: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActGelu>), grid, dim3(256), 0, s, a); break;
+        case kActNone: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, PPB, kActNone>), grid, block, 0, s, a); break;
+        case kActRelu: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, PPB, kActRelu>), grid, block, 0, s, a); break;
+        case kActGelu: hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, PPB, kActGelu>), grid, block, 0, s, a); break;
         case kActGeluErf:
-            hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, kActGeluErf>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((conv_f32_regw_kernel<KMAX, PPB, kActGeluErf>), grid, block, 0, s, a);
             break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Fewer pixels a workgroup while that still leaves workgroups for every CU: the weight loads
+// into registers (a 16-byte load per lane for each 4 of K) are the same per lane, so more,
+// smaller workgroups spread them over more CUs.
+template <int KMAX>
+hipError_t launch_regw(const ConvF32Args& a, int act, hipStream_t s) {
+    const int64_t wg8 = (static_cast<int64_t>(a.M) + 7) / 8 * ((a.Cout + 31) / 32);
+    if (wg8 >= 512) return launch_regw_ppb<KMAX, 8>(a, act, s);
+    if (wg8 >= 128) return launch_regw_ppb<KMAX, 4>(a, act, s);
+    return launch_regw_ppb<KMAX, 2>(a, act, s);
 }
 
 template <int TC>
