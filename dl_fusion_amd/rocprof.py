@@ -52,7 +52,8 @@ def fused_kernel(wl) -> str:
     """Name fragment of the kernel the library runs for workload wl's fused layer."""
     if wl.kind == "conv":
         if wl.dtype == "f32":
-            return "conv_f32_kernel"
+            k = wl.kh * wl.kw * wl.cin
+            return "conv_f32_regw_kernel" if wl.cin % 4 == 0 and 0 < k <= 256 else "conv_f32_kernel"
         # the routes of the library's halo plan, in its order
         if (wl.kh, wl.kw, wl.stride, wl.pad) != (3, 3, 1, 1) or wl.cout % 32 != 0:
             return "mma_kernel"
