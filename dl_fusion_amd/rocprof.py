@@ -116,6 +116,17 @@ def run(cmd: list[str], log: str, timeout: int) -> None:
         print(f"  (rocprofv3 exited {rc} after the program finished; results kept)", flush=True)
 
 
+def bench_figure(log: str):
+    """The roofline time (ms per launch, and how it was timed) that bench.py printed in its JSON
+    line during a profiled run, or None if the log holds no such line."""
+    with open(log) as f:
+        for line in reversed(f.read().splitlines()):
+            if line.startswith("{") and '"metric"' in line:
+                r = json.loads(line).get("roofline") or {}
+                return {"ms": r["ms"], "timing": r.get("timing", "")} if "ms" in r else None
+    return None
+
+
 def db_path(d: str) -> str:
     found = sorted(glob.glob(os.path.join(d, "**", "*results.db"), recursive=True))
     if not found:
@@ -236,6 +247,12 @@ def main() -> None:
                 if fused:
                     res["avg_us"] = fused[0][2]
                     res["kernel_name"] = fused[0][0]
+                own = bench_figure(d + ".log")
+                if own is not None and fused:
+                    lines += ["", f"- bench.py's own figure in this run ({own['timing']}, HIP events on the "
+                              f"launching stream): {own['ms'] * 1e3:.3f} us per launch; trace average / bench "
+                              f"figure = {fused[0][2] / (own['ms'] * 1e3):.3f}"]
+                    res["bench_us"] = own["ms"] * 1e3
                 lines.append("")
                 print(f"  trace done in {time.time() - t0:.0f} s", flush=True)
             else:
@@ -287,6 +304,8 @@ def main() -> None:
                 traffic[wl.name]["mfma_busy"] = util
         if "avg_us" in res and wl.name in traffic:
             traffic[wl.name]["trace_avg_us"] = res["avg_us"]
+            if "bench_us" in res:
+                traffic[wl.name]["bench_us_same_run"] = res["bench_us"]
         name = f"{frag}__{wl.name}.md"
         with open(os.path.join(args.out, name), "w") as f:
             f.write("\n".join(lines) + "\n")

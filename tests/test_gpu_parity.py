@@ -300,6 +300,14 @@ HALO_BF16 = [
     # forced routes, the streaming halo kernel and the implicit GEMM)
     dict(n=32, h=10, w=20, cin=64, cout=64, act="gelu_erf", residual=True),
     dict(n=64, h=7, w=7, cin=128, cout=64, act="gelu_erf", residual=False),
+    # small images with 64 to 320 input channels, one to five 64-channel groups, ragged row
+    # tiles, three output-channel tiles, a one-row image 128 wide, and 121-pixel images
+    dict(n=3, h=9, w=13, cin=192, cout=128, act="relu", residual=True),
+    dict(n=2, h=16, w=16, cin=128, cout=64, act="none", residual=False),
+    dict(n=2, h=12, w=11, cin=320, cout=192, act="gelu_tanh", residual=True),
+    dict(n=5, h=8, w=9, cin=64, cout=128, act="relu", residual=False),
+    dict(n=2, h=1, w=128, cin=64, cout=64, act="relu", residual=True),
+    dict(n=64, h=11, w=11, cin=128, cout=128, act="gelu_erf", residual=False),
 ]
 
 
