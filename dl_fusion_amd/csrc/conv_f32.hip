@@ -5,11 +5,12 @@
 // round trip and the store).  Each lane computes one output element (pixel m, channel co);
 // a workgroup covers 256/TC pixels x TC channels.
 //
-// conv_f32_regw_kernel (K <= 256, Cin a multiple of 4): one pass, 32 x PPB lanes.  Each lane loads its
-// channel's K weights straight into registers with 16-byte loads while the workgroup gathers
-// the receptive fields of its pixels into LDS (one 16-byte load per tap and 4 channels, zero
-// outside the image); after one barrier a lane reads 4 input values per LDS read (the lanes of
-// a pixel read the same address) for 4 FMAs against its registers.
+// conv_f32_regw_kernel (K <= 256, Cin a multiple of 4): one pass, 32 x PPB lanes.  The workgroup
+// copies its 32 channels' K weights into LDS once (16-byte loads of one contiguous block) while
+// it gathers the receptive fields of its pixels (one 16-byte load per tap and 4 channels, zero
+// outside the image); after one barrier a lane reads 4 weights of its channel and 4 input values
+// of its pixel per pair of LDS reads (the lanes of a pixel read the same input address) for 4
+// FMAs.
 //
 // conv_f32_kernel (any other shape): weights staged in LDS transposed to [k][channel] in
 // slices of 4096 values, together with the im2col rows of its pixels, each gathered by
@@ -80,18 +81,26 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
 template <int KMAX, int PPB, int ACT>
 __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Args p) {
     constexpr int TC = 32, K4 = KMAX / 4, NT = 32 * PPB;
+    // weight rows padded by 16 bytes: the 16 channels one 16-byte LDS read serves per cycle then
+    // start in 16 distinct 4-bank groups (row stride KMAX + 4 words, a multiple of 4 that is not
+    // a multiple of 64 for KMAX = 64, 160, 256)
+    constexpr int WS = KMAX + 4;
+    __shared__ f32x4_t ws[TC * WS / 4];
     __shared__ f32x4_t xs[PPB][K4];
     const int tid = static_cast<int>(threadIdx.x);
     const int co_l = tid % TC, pl = tid / TC;
     const int m0 = static_cast<int>(blockIdx.x) * PPB;
-    const int co = static_cast<int>(blockIdx.y) * TC + co_l;
+    const int c0 = static_cast<int>(blockIdx.y) * TC;
+    const int co = c0 + co_l;
     const int k4n = p.K >> 2;
-    // this lane's weights (a row of K values, 16-byte aligned: K % 4 == 0); rows past Cout
-    // read row 0 and their results are never stored
-    const f32x4_t* wrow = reinterpret_cast<const f32x4_t*>(p.w + static_cast<int64_t>(co < p.Cout ? co : 0) * p.K);
-    f32x4_t wr[K4];
-#pragma unroll
-    for (int q = 0; q < K4; ++q) wr[q] = q < k4n ? wrow[q] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // the workgroup's weight rows c0 .. c0 + 31 are one block of 32 K values (K % 4 == 0, w 16-byte
+    // aligned); rows past Cout are left unread and their results never stored
+    const int rows = min(TC, p.Cout - c0);
+    const f32x4_t* const wblk = reinterpret_cast<const f32x4_t*>(p.w + static_cast<int64_t>(c0) * p.K);
+    for (int e = tid; e < rows * k4n; e += NT) {
+        const int r = e / k4n, q = e - r * k4n;
+        ws[r * (WS / 4) + q] = wblk[e];
+    }
     // receptive fields of the workgroup's pixels: item e = (pixel, 4 consecutive k), one tap each
     const int hw = p.Ho * p.Wo;
     const int c4 = p.Cin >> 2;
@@ -112,19 +121,21 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
         xs[q][kk4] = v;
     }
     __syncthreads();
+    const int m = m0 + pl;
+    if (m >= p.M || co >= p.Cout) return;
+    const f32x4_t* const wrow = ws + co_l * (WS / 4);
     float acc0 = 0.0f, acc1 = 0.0f;    // two chains: even and odd k
 #pragma unroll
     for (int q = 0; q < K4; ++q) {
         if (q < k4n) {
             const f32x4_t xv = xs[pl][q];
-            acc0 = fmaf(xv[0], wr[q][0], acc0);
-            acc1 = fmaf(xv[1], wr[q][1], acc1);
-            acc0 = fmaf(xv[2], wr[q][2], acc0);
-            acc1 = fmaf(xv[3], wr[q][3], acc1);
+            const f32x4_t wv = wrow[q];
+            acc0 = fmaf(xv[0], wv[0], acc0);
+            acc1 = fmaf(xv[1], wv[1], acc1);
+            acc0 = fmaf(xv[2], wv[2], acc0);
+            acc1 = fmaf(xv[3], wv[3], acc1);
         }
     }
-    const int m = m0 + pl;
-    if (m >= p.M || co >= p.Cout) return;
     const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
     float v = (acc0 + acc1) + (p.bias ? p.bias[co] : 0.0f);
     if (p.res) v += p.res[idx];
@@ -150,14 +161,17 @@ hipError_t launch_regw_ppb(const ConvF32Args& a, int act, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Fewer pixels a workgroup while that still leaves workgroups for every CU: the weight loads
-// into registers (a 16-byte load per lane for each 4 of K) are the same per lane, so more,
-// smaller workgroups spread them over more CUs.
+// The weights are staged once per workgroup, so larger pixel blocks cut the weight traffic: 16
+// pixels a workgroup measured best on a 1x32x32 16->32 layer (64 workgroups, 4.45 us a launch in
+// a graph, against 4.7 us with 8, 5.1 us with 4 and 5.4 us with 32).  Smaller blocks only where
+// 16 would leave fewer than 64 workgroups.
 template <int KMAX>
 hipError_t launch_regw(const ConvF32Args& a, int act, hipStream_t s) {
-    const int64_t wg8 = (static_cast<int64_t>(a.M) + 7) / 8 * ((a.Cout + 31) / 32);
-    if (wg8 >= 512) return launch_regw_ppb<KMAX, 8>(a, act, s);
-    if (wg8 >= 128) return launch_regw_ppb<KMAX, 4>(a, act, s);
+    const int64_t cb = (a.Cout + 31) / 32;
+    auto wgs = [&](int ppb) { return (static_cast<int64_t>(a.M) + ppb - 1) / ppb * cb; };
+    if (wgs(16) >= 64) return launch_regw_ppb<KMAX, 16>(a, act, s);
+    if (wgs(8) >= 64) return launch_regw_ppb<KMAX, 8>(a, act, s);
+    if (wgs(4) >= 64) return launch_regw_ppb<KMAX, 4>(a, act, s);
     return launch_regw_ppb<KMAX, 2>(a, act, s);
 }
 

@@ -327,6 +327,9 @@ RAGGED_F32 = [
     dict(n=2, h=7, w=5, cin=4, cout=31, kh=1, kw=1, stride=1, pad=0, act="relu", residual=True),
     # K = 260 just past it (the sliced kernel)
     dict(n=1, h=6, w=6, cin=52, cout=20, kh=1, kw=5, stride=1, pad=2, act="relu", residual=False),
+    # the register-weight path's 8- and 16-pixel workgroups, the second with a one-pixel tail
+    dict(n=2, h=16, w=16, cin=8, cout=24, kh=3, kw=3, stride=1, pad=1, act="relu", residual=True),
+    dict(n=1, h=33, w=33, cin=4, cout=16, kh=3, kw=3, stride=1, pad=1, act="gelu_tanh", residual=False),
 ]
 
 
