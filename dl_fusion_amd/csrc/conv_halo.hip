@@ -283,7 +283,7 @@ constexpr int kRWeights = 9 * kWStage;   // 72 KB
 constexpr int kRHalo = 44 * 1024;        // one halo buffer: (th + 2) (W + 2) pixels x 128 B
 constexpr int kRLoads = kRHalo / 4096;   // halo loads per producer wave (1 KB each)
 constexpr int kRBlocks = 256;            // 32 per XCD
-constexpr int kRDist = 2;                // fragment prefetch distance (k-steps)
+constexpr int kRDist = 3;                // fragment prefetch distance (k-steps)
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0) only
 
