@@ -251,7 +251,8 @@ def main() -> None:
                 if own is not None and fused:
                     lines += ["", f"- bench.py's own figure in this run ({own['timing']}, HIP events on the "
                               f"launching stream): {own['ms'] * 1e3:.3f} us per launch; trace average / bench "
-                              f"figure = {fused[0][2] / (own['ms'] * 1e3):.3f}"]
+                              f"figure = {fused[0][2] / (own['ms'] * 1e3):.3f} (under the tracer a graph launch "
+                              f"also pays the trace's own per-dispatch cost, which dominates a kernel of a few us)"]
                     res["bench_us"] = own["ms"] * 1e3
                 lines.append("")
                 print(f"  trace done in {time.time() - t0:.0f} s", flush=True)
