@@ -38,8 +38,6 @@ constexpr int kS = 4;                      // weight ring stages
 constexpr int kWStage = kCo * 128;         // one weight slice: 64 rows x 128 bytes
 constexpr int kWLoads = kWStage / 1024 / 4;   // 1 KB weight loads per wave per slice (2)
 
-__device__ __attribute__((aligned(64))) uint8_t g_halo_zero[64];
-
 __device__ __forceinline__ int wchunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Chunk swizzle of halo pixel (hr, wc) of an image of width W, keyed on its unpadded index
@@ -81,9 +79,15 @@ __global__ __launch_bounds__(256, 1) void conv_halo_kernel(const HaloArgs p, con
     const int KT = 9 * Q;                                   // K slices
     const int ps = Cin * 2;                                 // halo bytes per pixel
     const int sh = Cin >= 128 ? 0 : 1, xm = Cin >= 128 ? 15 : 7;   // halo swizzle
-    const void* const zp = g_halo_zero;
-    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
-    const uint8_t* const wb = reinterpret_cast<const uint8_t*>(p.w);
+    // this image and this tile's 64 weight rows as buffers (the host keeps an image below 2 GB):
+    // the loads are then not FLAT instructions, so the compiler counts outstanding LDS reads
+    // exactly instead of waiting for every one (and every load in flight) before each MFMA;
+    // positions outside the image and slices past the last read zeros
+    const __amdgpu_buffer_rsrc_t xr =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(p.x) + static_cast<int64_t>(img) * p.H * W * ps,
+                    static_cast<uint32_t>(p.H * W * ps));
+    const __amdgpu_buffer_rsrc_t wr_ =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(p.w) + static_cast<int64_t>(c0) * K * 2, static_cast<uint32_t>(kCo * K * 2));
 
     // ---- halo: (th+2) x (W+2) pixels, one 1 KB load instruction per 1024/ps pixels ----
     {
@@ -97,12 +101,12 @@ __global__ __launch_bounds__(256, 1) void conv_halo_kernel(const HaloArgs p, con
             const int hi = h0 - 1 + hr, wi = wc - 1;
             const bool ok = q < nhp && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
                             static_cast<unsigned>(wi) < static_cast<unsigned>(W);
-            const int64_t off = ((static_cast<int64_t>(img) * p.H + hi) * W + wi) * ps + lc * 16;
-            load_lds16(ok ? static_cast<const void*>(xb + off) : zp, halo + li * 1024);
+            const uint32_t off = static_cast<uint32_t>((hi * W + wi) * ps + lc * 16);
+            load_lds16_buf(xr, ok ? off : kOutOfRange, halo + li * 1024);
         }
     }
 
-    // ---- weight slices: slice kt = (tap kt / Q, channel group kt % Q); past KT: zero page ----
+    // ---- weight slices: slice kt = (tap kt / Q, channel group kt % Q); past KT: zeros ----
     auto issue_w = [&](int kt) {
         uint8_t* st = ring + (kt % kS) * kWStage;
         const bool kin = kt < KT;
@@ -112,8 +116,8 @@ __global__ __launch_bounds__(256, 1) void conv_halo_kernel(const HaloArgs p, con
             const int blk = wave * kWLoads + j;                 // 8 rows per 1 KB
             const int r = blk * 8 + (lane >> 3), pc = lane & 7;
             const int lc = wchunk(r, pc);
-            const int64_t off = (static_cast<int64_t>(c0 + r) * K + t * Cin + q * 64 + lc * 8) * 2;
-            load_lds16(kin ? static_cast<const void*>(wb + off) : zp, st + blk * 1024);
+            const uint32_t off = static_cast<uint32_t>((r * K + t * Cin + q * 64 + lc * 8) * 2);
+            load_lds16_buf(wr_, kin ? off : kOutOfRange, st + blk * 1024);
         }
     };
 
@@ -889,6 +893,7 @@ bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, Ha
     }
     if (Cin != 64 && (Cin <= 0 || Cin % 128 != 0)) return false;   // the halo swizzle stays inside a pixel
     if (Cin > 1024 || W > 256) return false;
+    if (static_cast<int64_t>(H) * W * Cin * 2 >= (int64_t(1) << 31)) return false;   // 32-bit buffer offsets
     const int ps = Cin * 2;
     int th = 256 / W;                      // at most 8 fragments of 32 pixels
     if (th > H) th = H;
