@@ -307,6 +307,11 @@ int ffn_parts(int64_t M, int D, int F) {
     // the L2's rate (measured: 32 to 188 token blocks unsplit take the same 107-112 us on
     // BERT-base, 12 chunks; 256 workgroups of 6 chunks 80 us).  So: split only below 160
     // token blocks, into as many parts as fit one round of 256 workgroups.
+    // The split's fp32 partial sums make a round trip through memory, 8 S M D bytes, which can
+    // exceed the 4 M F bytes of h that the fusion keeps on chip (BERT-base: 9.4 MB against
+    // 1.6 MB at 128 tokens and 12 parts, 100.7 MB against 100.7 MB at 8192 tokens and 2).  The
+    // choice is made on time, which includes that traffic: 19.6 us against 112 us unsplit at
+    // 128 tokens, 116 us against 126-153 us at 8192; from 16384 tokens the walk is unsplit.
     const int nchunks = F / kChunk;
     if (D > 768 || nchunks < 2 || M <= 0) return 1;
     const int want = options().ffn_split;
