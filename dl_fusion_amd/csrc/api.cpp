@@ -103,9 +103,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 // Tile of the MFMA kernel for an M x N output.  A tile forced by DLF_TILE wins where the route
 // has it (tuning only).  Otherwise the estimate is (rounds of 256 concurrent tiles) x (tile
-// area / relative MFMA efficiency of the tile shape).  The 256 x 256 tile is the eight-wave
-// pipeline with one barrier per two K slices (dense GEMMs only): measured 7-10% faster than
-// four waves of 128 x 128 on the 4096 x 11008 x 4096 bf16 and 8192 x 4096 x 4096 fp8 GEMMs.
+// area / relative MFMA efficiency of the tile shape).  The 256 x 256 tile is the sixteen-wave
+// pipeline with one barrier per two K slices (dense GEMMs only): its eight-wave predecessor
+// was measured 7-10% faster than four waves of 128 x 128 on the 4096 x 11008 x 4096 bf16 and
+// 8192 x 4096 x 4096 fp8 GEMMs, and sixteen waves another 3.5-4.5%.
 // Memory-bound GEMMs (many rows, short K, narrow N) take the streaming kernel unless a tile
 // is forced or DLF_GEMM=tiled asks for the tiled kernel; DLF_GEMM=stream takes it wherever it
 // applies (tests of both routes).

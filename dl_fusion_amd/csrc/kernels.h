@@ -52,7 +52,7 @@ struct MmaArgs {
 // Output tile shapes of the MFMA kernel (rows x columns of C per workgroup).  The 256 x 256
 // tile serves the dense GEMM only; the implicit-GEMM convolution takes the other three.
 enum MmaTile : int {
-    kTile256x256 = 0,   // 2x4 waves of 128x64, one barrier per two K slices
+    kTile256x256 = 0,   // 4x4 waves of 64x64, one barrier per two K slices
     kTile128x128 = 1,   // 2x2 waves of 64x64
     kTile128x64 = 2,    // 2x2 waves of 64x32
     kTile64x64 = 3,     // 2x2 waves of 32x32
