@@ -368,16 +368,22 @@ __global__ __launch_bounds__(512, 1) void conv_halo_res_kernel(const HaloArgs p,
             }
         };
         // staged output of spatial tile st (in buf) -> y; lane handles chunk ptid % 8 of rows
-        // ptid / 8 + 32 i, so both addresses advance by constants (the swizzle repeats every 16 rows)
+        // ptid / 8 + 32 i, so both addresses advance by constants (the swizzle repeats every 16
+        // rows).  Eight lanes write a whole 128-byte line, so the stores write through to device
+        // scope.
         auto store_tile = [&](int st, const uint8_t* buf) {
             const int img = st / row_tiles, h0 = (st - img * row_tiles) * th;
             const int npix = min(th, H - h0) * W;
             const int ml0 = ptid >> 3, cc = ptid & 7;
             const uint8_t* src = buf + ml0 * SROW + ((cc ^ stg_swz(ml0)) << 4);
-            uint8_t* dst = yb + (((static_cast<int64_t>(img) * H + h0) * W + ml0) * p.Cout + c0) * 2 + cc * 16;
-            const int64_t dstep = static_cast<int64_t>(32) * p.Cout * 2;
-            for (int ml = ml0; ml < npix; ml += 32, src += 32 * SROW, dst += dstep)
-                *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+            const __amdgpu_buffer_rsrc_t yr =
+                buffer_rsrc(yb + ((static_cast<int64_t>(img) * H + h0) * W * p.Cout + c0) * 2,
+                            static_cast<uint32_t>(npix * p.Cout * 2));
+            uint32_t voff = static_cast<uint32_t>(ml0 * p.Cout * 2 + cc * 16);
+            const uint32_t dstep = static_cast<uint32_t>(32 * p.Cout * 2);
+            for (int ml = ml0; ml < npix; ml += 32, src += 32 * SROW, voff += dstep)
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(src), yr, voff, 0,
+                                                       kStoreDevice);
         };
         load_halo(s_first, smem + kRWeights);
         load_weights(std::integral_constant<int, 6>{}, std::integral_constant<int, 18>{});

@@ -4,24 +4,41 @@
 // conv epilogue of "OpenPPL算子融合深度解析" §4.3 with the folded BN of §3.1).
 //
 // A 16-byte-chunk implicit GEMM wastes most of its loads here: a chunk of 8 k-values spans
-// several taps and is not aligned.  Instead each workgroup keeps in LDS
-//   - its 64 output channels' weights, re-laid as [co][r][s (KW rounded up to 4)][4 channels],
-//   - the input patch under `th` output rows, as [row][column][4 channels] (8 bytes a pixel,
-//     zero outside the image and in the fourth channel),
-// so that one lane's 8 k-values of a 32x32x16 MFMA (two neighbouring taps s, s+1 of one
-// kernel row, four channels each) are 16 contiguous bytes for both operands.  Both are
-// filled with 16-byte global loads of whole input rows and of the weight block (the host
-// checks that rows and the block are multiples of 16 bytes) and scattered value by value
-// into the padded layouts.  The K loop then runs KH x ceil(KW/4) MFMA steps per 32-pixel
-// fragment and channel fragment, out of LDS only.
+// several taps and is not aligned.  Instead one workgroup per CU keeps in LDS
+//   - its 64 output channels' weights as [co][r][t][4 channels], t = s + toff the kernel
+//     column shifted so that the image's column 0 falls on an even patch column (toff is 1
+//     for an odd left padding), zero outside the kernel and in channels past c_in,
+//   - the input patch under its output rows as [row][column][4 channels] (8 bytes a pixel),
+//     the image's column 0 at the even column pwl, zero outside the image,
+// so that one lane's 8 k-values of a 32x32x16 MFMA (two neighbouring taps t, t+1 of one
+// kernel row, four channels each) are 16 contiguous bytes in both, 16-byte aligned in the
+// patch when the column stride is even.  Both are built in one pass without a separate
+// zero fill: a thread loads whole input pixel pairs (c_in dwords, dword-aligned because
+// pairs start at even image columns) and writes them out widened to four channels, and
+// positions outside the image or the kernel come from loads past the buffer, which read 0.
+//
+// What bounds this layer is its output: 64 output channels from 3 input channels make
+// 51 MB written against 10 MB read for a batch of 32 224x224 images.  The workgroup
+// therefore splits its 16 waves by role.  Eight compute waves (two per SIMD) run the K
+// loop for two 32-pixel fragments each per round and leave the finished fragments in LDS;
+// eight store waves copy a round's fragments out to memory while the compute waves run the
+// next round.  When every wave stores its own fragments, all of them stall on the full
+// store queue after each fragment, and the stores come in bursts separated by stretches of
+// K loop with no store in flight.
 #include "device_common.h"
 #include "kernels.h"
+#include "mma_common.h"
 
 namespace dlf {
 namespace {
 
-constexpr int kSmallLds = 65536;   // bytes: weights first, then the patch
-constexpr int kSmallStage = 4096;  // bytes a wave: one finished 32-pixel fragment
+constexpr int kScLds = 160 * 1024;                  // the CU's whole LDS: one workgroup per CU
+constexpr int kScThreads = 1024;                    // 16 waves
+constexpr int kScCompute = 8;                       // compute waves, two per SIMD; the rest store
+constexpr int kScRound = 2 * kScCompute;            // 32-pixel fragments a round
+constexpr int kScFrag = 32 * 128;                   // one staged fragment: 32 rows of 64 channels
+constexpr int kScStage = kScRound * kScFrag;        // 64 KB
+constexpr int kScBias = 64 * 4;                     // the workgroup's 64 biases, fp32
 
 // bytes between two output channels' weights: KH kwp 8, plus 16 where that is an even number
 // of 16-byte chunks, so that the 32 lanes' fragment reads (one channel each) fall in distinct
@@ -31,9 +48,118 @@ __host__ __device__ inline int smallc_wstride(int kh, int kwp) {
     return (b / 16) % 2 == 0 ? b + 16 : b;
 }
 
-template <int ACT, bool RES>
-__global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmallLds + 4 * kSmallStage];
+// s_waitcnt lgkmcnt(0), then s_barrier: this wave's LDS reads and writes are done before the
+// other waves pass.  Outstanding global stores are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier();
+}
+
+// a / b for 0 <= a < 2^22 and b >= 1 given inv = 1 / b: (a + 1/2) / b lies at least 1 / (2b)
+// from an integer, and the two float roundings move it by at most (a + 1/2) / b * 2^-23
+__device__ __forceinline__ int small_div(int a, float inv) {
+    return static_cast<int>((static_cast<float>(a) + 0.5f) * inv);
+}
+
+// CIN consecutive dwords of buffer r at byte offset off (zeros past the buffer)
+template <int CIN>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* d) {
+    if constexpr (CIN == 1) {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (CIN == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        d[0] = v[0]; d[1] = v[1];
+    } else if constexpr (CIN == 3) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+        d[0] = v[0]; d[1] = v[1]; d[2] = v[2];
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    }
+}
+
+// two input pixels of CIN bf16 channels each (CIN dwords) as two 8-byte pixels of 4 channels
+template <int CIN>
+__device__ __forceinline__ u32x4_t widen_pair(const uint32_t* d) {
+    if constexpr (CIN == 1) return u32x4_t{d[0] & 0xFFFFu, 0u, d[0] >> 16, 0u};
+    else if constexpr (CIN == 2) return u32x4_t{d[0], 0u, d[1], 0u};
+    else if constexpr (CIN == 3) return u32x4_t{d[0], d[1] & 0xFFFFu, (d[1] >> 16) | (d[2] << 16), d[2] >> 16};
+    else return u32x4_t{d[0], d[1], d[2], d[3]};
+}
+
+// Weights of channels co0 .. co0+nco-1 and the input patch (rows hi0 .. hi0+prows-1 of image
+// img) into their LDS layouts, every position written once.
+template <int CIN>
+__device__ void smallc_fill(const SmallCArgs& p, uint8_t* sw, uint8_t* sx, int wstride, int img, int co0,
+                            int nco, int hi0, int prows, int tid) {
+    // weights: chunk (co, r, tp) holds taps t = 2 tp and 2 tp + 1 of kernel row r
+    {
+        const int kp2 = p.kwp / 2, per_co = p.KH * kp2;
+        const float inv_co = 1.0f / static_cast<float>(per_co), inv_kp2 = 1.0f / static_cast<float>(kp2);
+        const int kvals = p.KH * p.KW * CIN;
+        const __amdgpu_buffer_rsrc_t wr =
+            buffer_rsrc(p.w + static_cast<int64_t>(co0) * kvals, static_cast<uint32_t>(nco * kvals * 2));
+        for (int c = tid; c < nco * per_co; c += kScThreads) {
+            const int co = small_div(c, inv_co), rem = c - co * per_co;
+            const int r = small_div(rem, inv_kp2), tp = rem - r * kp2;
+            uint32_t v[2][CIN];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int s = 2 * tp + h - p.toff;
+                const bool ok = s >= 0 && s < p.KW;
+                const uint32_t base = static_cast<uint32_t>(((co * p.KH + r) * p.KW + s) * CIN * 2);
+#pragma unroll
+                for (int ci = 0; ci < CIN; ++ci)
+                    v[h][ci] = __builtin_amdgcn_raw_buffer_load_b16(wr, ok ? base + 2 * ci : kOutOfRange, 0, 0);
+            }
+            uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int ci = 0; ci < CIN; ++ci) o[2 * h + (ci >> 1)] |= v[h][ci] << (16 * (ci & 1));
+            *reinterpret_cast<u32x4_t*>(sw + co * wstride + (r * p.kwp + 2 * tp) * 8) = u32x4_t{o[0], o[1], o[2], o[3]};
+        }
+    }
+    // patch: pair (pr, cp) is patch columns 2 cp, 2 cp + 1 = image columns 2 cp - pwl (even)
+    // and the next one, of image row hi0 + pr.  Four pairs a thread per pass, their loads
+    // in flight together; the pair index steps by kScThreads without a division.
+    {
+        const int pairs = p.pw / 2;
+        const int64_t img_bytes = static_cast<int64_t>(p.H) * p.W * CIN * 2;
+        const __amdgpu_buffer_rsrc_t xr =
+            buffer_rsrc(reinterpret_cast<const uint8_t*>(p.x) + img * img_bytes, static_cast<uint32_t>(img_bytes));
+        const float inv_pairs = 1.0f / static_cast<float>(pairs);
+        int pr = small_div(tid, inv_pairs), cp = tid - pr * pairs;
+        const int dpr = small_div(kScThreads, inv_pairs), dcp = kScThreads - dpr * pairs;
+        while (pr < prows) {
+            uint32_t d[4][CIN];
+            int dst[4];
+            bool live[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                live[u] = pr < prows;
+                const int hi = hi0 + pr, w = 2 * cp - p.pwl;
+                const bool in = live[u] && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                                static_cast<unsigned>(w) < static_cast<unsigned>(p.W);
+                load_dwords<CIN>(xr, in ? static_cast<uint32_t>((hi * p.W + w) * CIN * 2) : kOutOfRange, d[u]);
+                dst[u] = (pr * p.pw + 2 * cp) * 8;
+                cp += dcp;
+                pr += dpr;
+                if (cp >= pairs) {
+                    cp -= pairs;
+                    ++pr;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (live[u]) *reinterpret_cast<u32x4_t*>(sx + dst[u]) = widen_pair<CIN>(d[u]);
+        }
+    }
+}
+
+template <int ACT, bool RES, bool A16>
+__global__ __launch_bounds__(kScThreads, 1) void conv_smallc_kernel(const SmallCArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kScLds];
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     int bid = static_cast<int>(blockIdx.x);
@@ -46,220 +172,199 @@ __global__ __launch_bounds__(256, 2) void conv_smallc_kernel(const SmallCArgs p)
     const int ho0 = rt * p.th;
     const int rows = min(p.th, p.Ho - ho0);
     const int wstride = smallc_wstride(p.KH, p.kwp);
-    uint8_t* const sw = smem;
-    uint8_t* const sx = smem + 64 * wstride;
+    uint8_t* const stage = smem;
+    float* const sbias = reinterpret_cast<float*>(smem + kScStage);
+    uint8_t* const sw = smem + kScStage + kScBias;
+    uint8_t* const sx = sw + 64 * wstride;
 
-    // ---- zero both regions (padding taps, the fourth channel, rows and columns outside) ----
-    for (int i = tid; i < kSmallLds / 16; i += 256)
-        *reinterpret_cast<u32x4_t*>(smem + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
-    __syncthreads();
-
-    // ---- weights of channels co0 .. co0+nco-1: one contiguous block of nco*K values.  Four
-    //      16-byte loads per lane go out before their values are scattered; the (co, r, s, ci)
-    //      position of a chunk's first value is divided out once, the next seven step on. ----
-    const int K = p.KH * p.KW * p.Cin;
-    {
-        const uint8_t* const src = reinterpret_cast<const uint8_t*>(p.w) + static_cast<int64_t>(co0) * K * 2;
-        const int chunks = nco * K / 8;                     // whole: nco % 8 == 0
-        for (int c0 = tid; c0 < chunks; c0 += 4 * 256) {
-            u32x4_t v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (c0 + 256 * u < chunks) v[u] = *reinterpret_cast<const u32x4_t*>(src + 16 * (c0 + 256 * u));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + 256 * u;
-                if (c >= chunks) break;
-                const int idx = 8 * c;
-                int co = idx / K, k = idx - co * K;
-                int r = k / (p.KW * p.Cin), rem = k - r * p.KW * p.Cin;
-                int sx_ = rem / p.Cin, ci = rem - sx_ * p.Cin;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t word = v[u][e >> 1];
-                    const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-                    *reinterpret_cast<uint16_t*>(sw + co * wstride + ((r * p.kwp + sx_) * 4 + ci) * 2) = val;
-                    if (++ci == p.Cin) {
-                        ci = 0;
-                        if (++sx_ == p.KW) {
-                            sx_ = 0;
-                            if (++r == p.KH) {
-                                r = 0;
-                                ++co;
-                            }
-                        }
-                    }
-                }
-            }
-        }
+    // ---- fill: biases, weights, patch ----
+    if (tid < 16) {
+        f32x4_t b = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.bias && 4 * tid < nco) b = *reinterpret_cast<const f32x4_t*>(p.bias + co0 + 4 * tid);
+        *reinterpret_cast<f32x4_t*>(sbias + 4 * tid) = b;
     }
-    // ---- input rows hi0 .. hi0+prows-1 of this image, whole rows (W*Cin values each), four
-    //      loads per lane in flight as above ----
     const int hi0 = ho0 * p.SH - p.PH;
     const int prows = (rows - 1) * p.SH + p.KH;
-    const int row_vals = p.W * p.Cin;
-    const int row_chunks = row_vals / 8;                   // whole: the host checks W*Cin % 8 == 0
-    {
-        const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x) + static_cast<int64_t>(img) * p.H * row_vals * 2;
-        const int total = prows * row_chunks;
-        for (int c0 = tid; c0 < total; c0 += 4 * 256) {
-            u32x4_t v[4];
-            int pr[4], rc[4];
-            bool ok[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + 256 * u;
-                pr[u] = c / row_chunks;
-                rc[u] = c - pr[u] * row_chunks;
-                const int hi = hi0 + pr[u];
-                ok[u] = c < total && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H);   // else stays zero
-                if (ok[u]) v[u] = *reinterpret_cast<const u32x4_t*>(xb + (static_cast<int64_t>(hi) * row_vals + 8 * rc[u]) * 2);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (!ok[u]) continue;
-                const int idx = 8 * rc[u];
-                int wi = idx / p.Cin, ci = idx - wi * p.Cin;
-                uint8_t* const rowp = sx + (pr[u] * p.pw + p.PW) * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t word = v[u][e >> 1];
-                    const uint16_t val = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-                    *reinterpret_cast<uint16_t*>(rowp + (wi * 4 + ci) * 2) = val;
-                    if (++ci == p.Cin) {
-                        ci = 0;
-                        ++wi;
-                    }
-                }
-            }
-        }
+    switch (p.Cin) {
+        case 1: smallc_fill<1>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
+        case 2: smallc_fill<2>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
+        case 3: smallc_fill<3>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
+        default: smallc_fill<4>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 32-pixel fragments, two at a time per wave (fragments f and f + 4), so that four
-    //      accumulator chains interleave on the matrix pipe ----
-    const int npx = rows * p.Wo;
-    const int nfrag = (npx + 31) / 32;
-    const int ksteps = p.kwp / 4;                           // 1 .. 4 (the host bounds KH * kwp)
-    const int nj = nco / 32;
-    uint8_t* const yb = reinterpret_cast<uint8_t*>(p.y);
-    const uint8_t* const bbase = sw + (lane & 31) * wstride + 2 * half * 8;
-    const int bstep_j = 32 * wstride;
-    uint8_t* const stg = smem + kSmallLds + wave * kSmallStage;
-    const int cpr = nco / 8;                                // 16-byte chunks of a staged row
-    for (int f0 = wave; f0 < nfrag; f0 += 8) {
-        int hl[2], wo[2];
-        bool pv[2];
-        const uint8_t* abase[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int pl = (f0 + 4 * u) * 32 + (lane & 31);
-            pv[u] = pl < npx;
-            const int plc = pv[u] ? pl : 0;
-            hl[u] = plc / p.Wo;
-            wo[u] = plc - hl[u] * p.Wo;
-            abase[u] = sx + ((hl[u] * p.SH) * p.pw + wo[u] * p.SW + 2 * half) * 8;
-        }
-        f32x16_t acc[2][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[u][j][e] = 0.0f;
-        for (int r = 0; r < p.KH; ++r) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks >= ksteps) break;
-                bf16x8_t av[2];
+    const int npx = rows * p.Wo;                            // the tile's pixels: whole output rows,
+    const int nfrag = (npx + 31) / 32;                      // contiguous in y
+    const int nrounds = (nfrag + kScRound - 1) / kScRound;
+    const int64_t pix0 = (static_cast<int64_t>(img) * p.Ho + ho0) * p.Wo;
+    const int cpr = nco / 8;                                // 16-byte chunks of a pixel's channels
+
+    if (wave < kScCompute) {
+        // ---- compute waves: fragments f0 and f0 + 8 of each round, four accumulator chains
+        //      (2 fragments x 2 channel halves) interleaved on the matrix pipe ----
+        const int ksteps = p.kwp / 4;                       // 1 .. 4
+        const int nj = nco / 32;
+        const uint8_t* const bbase = sw + (lane & 31) * wstride + 2 * half * 8;
+        const int bstep_j = 32 * wstride;
+        const int m = lane & 31, swz = (m >> 1) & 7;
+        const float inv_wo = 1.0f / static_cast<float>(p.Wo);
+        for (int rd = 0; rd < nrounds; ++rd) {
+            const int f0 = rd * kScRound + wave;
+            const bool any = f0 < nfrag;
+            f32x16_t acc[2][2];
+            int pl[2];
+            bool pv[2];
+            if (any) {
+                const uint8_t* abase[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const uint8_t* const a = abase[u] + (r * p.pw + 4 * ks) * 8;
-                    const uint2 a0 = *reinterpret_cast<const uint2*>(a);
-                    const uint2 a1 = *reinterpret_cast<const uint2*>(a + 8);
-                    av[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
+                    const int q = (f0 + 8 * u) * 32 + m;
+                    pv[u] = q < npx;
+                    pl[u] = pv[u] ? q : 0;
+                    const int hl = small_div(pl[u], inv_wo), wo = pl[u] - hl * p.Wo;
+                    abase[u] = sx + ((hl * p.SH) * p.pw + wo * p.SW + 2 * half) * 8;
                 }
-                const uint8_t* const b = bbase + (r * p.kwp + 4 * ks) * 8;
-                const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(b);
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[0], acc[0][0], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[1], acc[1][0], 0, 0, 0);
-                if (nj > 1) {
-                    const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b + bstep_j);
-                    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[0], acc[0][1], 0, 0, 0);
-                    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[1], acc[1][1], 0, 0, 0);
-                }
-            }
-        }
-        // lane: pixel of fragment f0 + 4u; register group g of channel fragment j holds
-        // channels 32 j + 8 g + 4 half .. +3.  The finished fragment goes through this wave's
-        // staging area, 32 rows of 128 bytes with chunk c of row m at c ^ ((m >> 1) & 7), and
-        // out as whole rows of 16-byte stores.
-        const int m = lane & 31, swz = (m >> 1) & 7;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int f = f0 + 4 * u;
-            if (f >= nfrag) break;
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (j >= nj) break;
+                    for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int co = co0 + 32 * j + 8 * g + 4 * half;
-                    float v[4];
+                        for (int e = 0; e < 16; ++e) acc[u][j][e] = 0.0f;
+                for (int r = 0; r < p.KH; ++r) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = acc[u][j][4 * g + e];
-                    if (p.bias) {
-                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(p.bias + co);
+                    for (int ks = 0; ks < 4; ++ks) {
+                        if (ks >= ksteps) break;
+                        bf16x8_t av[2];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] += bv[e];
-                    }
-                    if constexpr (RES) {
-                        if (pv[u]) {
-                            const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hl[u]) * p.Wo + wo[u];
-                            const uint2 rv = *reinterpret_cast<const uint2*>(p.res + pix * p.Cout + co);
-                            v[0] += __uint_as_float(rv.x << 16);
-                            v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
-                            v[2] += __uint_as_float(rv.y << 16);
-                            v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
+                        for (int u = 0; u < 2; ++u) {
+                            const uint8_t* const a = abase[u] + (r * p.pw + 4 * ks) * 8;
+                            if constexpr (A16) {
+                                av[u] = *reinterpret_cast<const bf16x8_t*>(a);
+                            } else {
+                                const uint2 a0 = *reinterpret_cast<const uint2*>(a);
+                                const uint2 a1 = *reinterpret_cast<const uint2*>(a + 8);
+                                av[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
+                            }
+                        }
+                        const uint8_t* const b = bbase + (r * p.kwp + 4 * ks) * 8;
+                        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(b);
+                        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[0], acc[0][0], 0, 0, 0);
+                        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[1], acc[1][0], 0, 0, 0);
+                        if (nj > 1) {
+                            const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b + bstep_j);
+                            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[0], acc[0][1], 0, 0, 0);
+                            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[1], acc[1][1], 0, 0, 0);
                         }
                     }
-                    if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
-                    }
-                    uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-                    if constexpr (ACT == kActRelu) {
-                        lo = relu_bf16x2(lo);
-                        hi = relu_bf16x2(hi);
-                    }
-                    *reinterpret_cast<uint2*>(stg + m * 128 + (((4 * j + g) ^ swz) << 4) + 8 * half) = make_uint2(lo, hi);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's staging writes are done
-            __builtin_amdgcn_wave_barrier();
-            // rows of the fragment: pixel f 32 + r of the tile, cpr chunks each
-            for (int q = lane; q < 32 * cpr; q += 64) {
-                const int r = q / cpr, c = q - r * cpr;
-                const int pl = f * 32 + r;
-                if (pl >= npx) continue;
-                const int hr = pl / p.Wo, wr = pl - hr * p.Wo;
-                const int64_t pix = (static_cast<int64_t>(img) * p.Ho + ho0 + hr) * p.Wo + wr;
-                const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-                *reinterpret_cast<u32x4_t*>(yb + (pix * p.Cout + co0 + 8 * c) * 2) = val;
+            lds_barrier();   // B1: the store waves hold the previous round's fragments
+            if (any) {
+                // lane: pixel m of its fragment; register group g of channel half j holds
+                // channels 32 j + 8 g + 4 half .. +3.  Staged as 32 rows of 128 bytes with
+                // chunk c of row m at c ^ ((m >> 1) & 7).
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (f0 + 8 * u >= nfrag) break;
+                    uint8_t* const stg = stage + (2 * wave + u) * kScFrag;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (j >= nj) break;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int col = 32 * j + 8 * g + 4 * half;
+                            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(sbias + col);
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = acc[u][j][4 * g + e] + bv[e];
+                            if constexpr (RES) {
+                                if (pv[u]) {
+                                    const uint2 rv = *reinterpret_cast<const uint2*>(
+                                        p.res + (pix0 + pl[u]) * p.Cout + co0 + col);
+                                    v[0] += __uint_as_float(rv.x << 16);
+                                    v[1] += __uint_as_float(rv.x & 0xFFFF0000u);
+                                    v[2] += __uint_as_float(rv.y << 16);
+                                    v[3] += __uint_as_float(rv.y & 0xFFFF0000u);
+                                }
+                            }
+                            if constexpr (ACT == kActGelu || ACT == kActGeluErf) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) v[e] = activate<ACT>(v[e]);
+                            }
+                            uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                            if constexpr (ACT == kActRelu) {
+                                lo = relu_bf16x2(lo);
+                                hi = relu_bf16x2(hi);
+                            }
+                            *reinterpret_cast<uint2*>(stg + m * 128 + (((4 * j + g) ^ swz) << 4) + 8 * half) =
+                                make_uint2(lo, hi);
+                        }
+                    }
+                }
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // the staging reads are done before the next writes
-            __builtin_amdgcn_wave_barrier();
+            lds_barrier();   // B2: this round's fragments are staged
         }
+    } else {
+        // ---- store waves: wave 8 + s copies the fragments of compute wave s (staging slots
+        //      2 s and 2 s + 1), 16 bytes a lane per row chunk, into registers after B2 and
+        //      out to y during the next round.  Stores write through to device scope: every
+        //      store instruction covers whole 128-byte lines, and no dirty lines are left for
+        //      the end of the kernel. ----
+        const int s = wave - kScCompute;
+        const int shift = cpr == 8 ? 3 : 2;
+        const __amdgpu_buffer_rsrc_t yr = buffer_rsrc(reinterpret_cast<uint8_t*>(p.y) + (pix0 * p.Cout + co0) * 2,
+                                                      static_cast<uint32_t>(npx * p.Cout * 2));
+        u32x4_t held[2][4];
+        auto store_round = [&](int rd) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int f = rd * kScRound + s + 8 * u;
+                if (f >= nfrag) break;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (2 * i >= cpr) break;
+                    const int q = lane + 64 * i, row = q >> shift, c = q & (cpr - 1);
+                    const int px = f * 32 + row;
+                    if (px < npx)
+                        __builtin_amdgcn_raw_buffer_store_b128(held[u][i], yr,
+                                                               static_cast<uint32_t>((px * p.Cout + 8 * c) * 2), 0,
+                                                               kStoreDevice);
+                }
+            }
+        };
+        for (int rd = 0; rd < nrounds; ++rd) {
+            if (rd > 0) store_round(rd - 1);
+            lds_barrier();   // B1
+            lds_barrier();   // B2
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int f = rd * kScRound + s + 8 * u;
+                if (f >= nfrag) break;
+                const uint8_t* const stg = stage + (2 * s + u) * kScFrag;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (2 * i >= cpr) break;
+                    const int q = lane + 64 * i, row = q >> shift, c = q & (cpr - 1);
+                    held[u][i] = *reinterpret_cast<const u32x4_t*>(stg + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+                }
+            }
+        }
+        store_round(nrounds - 1);
     }
+}
+
+template <int ACT, bool RES>
+hipError_t launch_res(const SmallCArgs& a, dim3 grid, hipStream_t s) {
+    if (a.SW % 2 == 0)
+        hipLaunchKernelGGL((conv_smallc_kernel<ACT, RES, true>), grid, dim3(kScThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((conv_smallc_kernel<ACT, RES, false>), grid, dim3(kScThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int ACT>
 hipError_t launch_act(const SmallCArgs& a, dim3 grid, hipStream_t s) {
-    if (a.res)
-        hipLaunchKernelGGL((conv_smallc_kernel<ACT, true>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((conv_smallc_kernel<ACT, false>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    return a.res ? launch_res<ACT, true>(a, grid, s) : launch_res<ACT, false>(a, grid, s);
 }
 
 }  // namespace
@@ -268,28 +373,39 @@ bool conv_smallc_plan(int N, int H, int W, int Cin, int Cout, int KH, int KW, in
                       int Ho, int Wo, SmallCArgs* a) {
     if (Cin < 1 || Cin > 4 || Cout < 32 || Cout % 32 != 0 || N < 1 || H < 1 || W < 1 || Ho < 1 || Wo < 1)
         return false;
-    if ((W * Cin) % 8 != 0) return false;                 // whole 16-byte chunks per input row
-    const int kwp = (KW + 3) / 4 * 4;
+    if ((W * Cin) % 8 != 0) return false;                 // W even: a pixel pair never straddles a row
+    if (static_cast<int64_t>(H) * W * Cin * 2 >= (int64_t(1) << 31)) return false;   // 32-bit offsets in an image
+    const int pwl = PW + (PW & 1), toff = pwl - PW;
+    const int kwp = (KW + toff + 3) / 4 * 4;
     if (kwp > 16) return false;                            // at most four MFMA steps per kernel row
     const int wbytes = 64 * smallc_wstride(KH, kwp);
-    if (wbytes > kSmallLds / 2) return false;
-    // patch columns: every input column (filled) and every column a fragment reads, padded
-    // taps included
-    int pw = W + PW > (Wo - 1) * SW + kwp ? W + PW : (Wo - 1) * SW + kwp;
-    pw = (pw + 1) / 2 * 2;
-    const int rows_fit = (kSmallLds - wbytes) / (pw * 8);
+    // patch columns: every column a fragment reads, wo SW + t for t < kwp
+    const int pw = ((Wo - 1) * SW + kwp + 1) / 2 * 2;
+    const int budget = kScLds - kScStage - kScBias - wbytes;
+    if (budget <= 0 || pw > 4096) return false;
+    const int rows_fit = budget / (pw * 8);
     if (rows_fit < KH) return false;
-    int th = (rows_fit - KH) / SH + 1;                     // th rows read (th - 1) SH + KH input rows
-    th = th > 16 ? 16 : th;
-    th = th > Ho ? Ho : th;
+    const int th_max = (rows_fit - KH) / SH + 1;           // th rows read (th - 1) SH + KH input rows
+    const int co_blocks = (Cout + 63) / 64;
+    // as few row tiles as the LDS allows, but at least one workgroup per CU where the rows
+    // allow it, and the rows shared out evenly
+    int row_tiles = (Ho + th_max - 1) / th_max;
+    const int64_t per_img = static_cast<int64_t>(N) * co_blocks;
+    const int64_t want = (256 + per_img - 1) / per_img;
+    if (row_tiles < want) row_tiles = static_cast<int>(want < Ho ? want : Ho);
+    const int th = (Ho + row_tiles - 1) / row_tiles;
+    if (static_cast<int64_t>(th) * Wo * Cout * 2 >= (int64_t(1) << 31)) return false;   // 32-bit store offsets
+    if (static_cast<int64_t>(N) * ((Ho + th - 1) / th) * co_blocks > 0x7FFFFFFF) return false;
     a->N = N; a->H = H; a->W = W; a->Cin = Cin; a->Cout = Cout;
     a->KH = KH; a->KW = KW; a->SH = SH; a->SW = SW; a->PH = PH; a->PW = PW;
     a->Ho = Ho; a->Wo = Wo;
     a->kwp = kwp;
     a->pw = pw;
+    a->pwl = pwl;
+    a->toff = toff;
     a->th = th;
     a->row_tiles = (Ho + th - 1) / th;
-    a->co_blocks = (Cout + 63) / 64;
+    a->co_blocks = co_blocks;
     return true;
 }
 

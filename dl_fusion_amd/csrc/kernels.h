@@ -118,7 +118,8 @@ bool conv_halo_plan(int N, int H, int W, int Cin, int Cout, bool resident_ok, Ha
 hipError_t launch_conv_halo(const HaloArgs& args, const HaloPlan& plan, int act, hipStream_t stream);
 
 // bf16 convolution for inputs with few channels (c_in <= 4, e.g. a ResNet stem): weights and
-// the input patch of `th` output rows re-laid in LDS with 4-channel pixels.
+// the input patch of `th` output rows re-laid in LDS with 4-channel pixels, one workgroup
+// per CU with compute and store waves.
 struct SmallCArgs {
     const uint16_t* x;      // [N][H][W][Cin]
     const uint16_t* w;      // [Cout][KH][KW][Cin]
@@ -126,15 +127,17 @@ struct SmallCArgs {
     const uint16_t* res;    // [N][Ho][Wo][Cout] or nullptr
     uint16_t* y;            // [N][Ho][Wo][Cout]
     int N, H, W, Cin, Cout, KH, KW, SH, SW, PH, PW, Ho, Wo;
-    int kwp;                // KW rounded up to a multiple of 4
+    int kwp;                // KW + toff rounded up to a multiple of 4
     int pw;                 // patch width in pixels (even)
+    int pwl;                // patch column of image column 0: PW rounded up to even
+    int toff;               // pwl - PW: kernel column s is tap s + toff
     int th;                 // output rows per workgroup
     int row_tiles;          // ceil(Ho / th)
     int co_blocks;          // ceil(Cout / 64)
 };
 // False when the shape does not qualify (Cin <= 4, Cout a multiple of 32, W*Cin a multiple
-// of 8, KW <= 16, the weights of 64 channels within 32 KB and the patch of one output row
-// within the rest of 64 KB); fills everything but the pointers.
+// of 8, KW + toff <= 16, and the weights of 64 channels, 64 KB of staged output and the
+// patch of one output row within 160 KB of LDS); fills everything but the pointers.
 bool conv_smallc_plan(int N, int H, int W, int Cin, int Cout, int KH, int KW, int SH, int SW, int PH, int PW,
                       int Ho, int Wo, SmallCArgs* args);
 hipError_t launch_conv_smallc(const SmallCArgs& args, int act, hipStream_t stream);

@@ -69,6 +69,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // Offset that lies outside every buffer: the load returns zeros.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// Cache-policy operand of a buffer store that writes through to device scope (sc1): the line
+// goes on towards memory when stored, instead of staying dirty in the XCD's L2 until the
+// release at the end of the kernel writes it back.  Worth it where every store instruction
+// writes whole 128-byte lines; stores of partial lines were slower this way.
+constexpr int kStoreDevice = 16;
+
 // One 16-byte load per lane from buffer r at byte offset voff into LDS (lane i's data lands at
 // lds_wave_base + 16 i; the base must be uniform across the wave).  Offsets past the buffer
 // read as zero.  Unlike the global form it is not a FLAT instruction, so the compiler does not
