@@ -12,10 +12,13 @@
 //     the image's column 0 at the even column pwl, zero outside the image,
 // so that one lane's 8 k-values of a 32x32x16 MFMA (two neighbouring taps t, t+1 of one
 // kernel row, four channels each) are 16 contiguous bytes in both, 16-byte aligned in the
-// patch when the column stride is even.  Both are built in one pass without a separate
-// zero fill: a thread loads whole input pixel pairs (c_in dwords, dword-aligned because
-// pairs start at even image columns) and writes them out widened to four channels, and
-// positions outside the image or the kernel come from loads past the buffer, which read 0.
+// patch when the column stride is even.  Both are written once, without a zero fill: a
+// thread loads whole input pixel pairs (c_in dwords, dword-aligned because pairs start at
+// even image columns) and writes them out widened to four channels, each weight tap comes
+// from one 8-byte load shifted into place, and positions outside the image or the kernel
+// come from loads past the buffer, which read 0.  Before the first K loop only the weights
+// and the patch rows of the first round are filled; the store waves, which have nothing to
+// store in the first round, fill the other rows meanwhile.
 //
 // What bounds this layer is its output: 64 output channels from 3 input channels make
 // 51 MB written against 10 MB read for a batch of 32 224x224 images.  The workgroup
@@ -61,6 +64,19 @@ __device__ __forceinline__ int small_div(int a, float inv) {
     return static_cast<int>((static_cast<float>(a) + 0.5f) * inv);
 }
 
+// One lane's 8 k-values of a pixel fragment: 16 bytes of the patch, 16-byte aligned when the
+// column stride is even (A16), else 8-byte aligned.
+template <bool A16>
+__device__ __forceinline__ bf16x8_t read_a(const uint8_t* a) {
+    if constexpr (A16) {
+        return *reinterpret_cast<const bf16x8_t*>(a);
+    } else {
+        const uint2 a0 = *reinterpret_cast<const uint2*>(a);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(a + 8);
+        return __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
+    }
+}
+
 // CIN consecutive dwords of buffer r at byte offset off (zeros past the buffer)
 template <int CIN>
 __device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* d) {
@@ -87,73 +103,126 @@ __device__ __forceinline__ u32x4_t widen_pair(const uint32_t* d) {
     else return u32x4_t{d[0], d[1], d[2], d[3]};
 }
 
-// Weights of channels co0 .. co0+nco-1 and the input patch (rows hi0 .. hi0+prows-1 of image
-// img) into their LDS layouts, every position written once.
+// Weights of channels co0 .. co0+nco-1 re-laid as [co][r][t][4 channels] and the first
+// rows of the input patch, every position written once.  Weight chunk (co, r, tp) holds taps
+// t = 2 tp and 2 tp + 1 of kernel row r: each tap's CIN channels come from one 8-byte load
+// that lies wholly inside the block (from the dword below them, or from the block's last
+// 8 bytes), shifted down to them; a tap outside the kernel reads past the buffer: zero.  Each
+// pass issues the loads of two weight chunks and four pixel pairs a thread before any LDS
+// write.
 template <int CIN>
-__device__ void smallc_fill(const SmallCArgs& p, uint8_t* sw, uint8_t* sx, int wstride, int img, int co0,
-                            int nco, int hi0, int prows, int tid) {
-    // weights: chunk (co, r, tp) holds taps t = 2 tp and 2 tp + 1 of kernel row r
-    {
-        const int kp2 = p.kwp / 2, per_co = p.KH * kp2;
-        const float inv_co = 1.0f / static_cast<float>(per_co), inv_kp2 = 1.0f / static_cast<float>(kp2);
-        const int kvals = p.KH * p.KW * CIN;
-        const __amdgpu_buffer_rsrc_t wr =
-            buffer_rsrc(p.w + static_cast<int64_t>(co0) * kvals, static_cast<uint32_t>(nco * kvals * 2));
-        for (int c = tid; c < nco * per_co; c += kScThreads) {
+__device__ void smallc_fill(const SmallCArgs& p, uint8_t* sw, uint8_t* sx, int wstride, int img, int co0, int nco,
+                            int hi0, int prows0, int tid) {
+    const int kp2 = p.kwp / 2, per_co = p.KH * kp2, wchunks = nco * per_co;
+    const float inv_co = 1.0f / static_cast<float>(per_co), inv_kp2 = 1.0f / static_cast<float>(kp2);
+    const int kvals = p.KH * p.KW * CIN;
+    const uint32_t wbytes = static_cast<uint32_t>(nco * kvals * 2);   // a multiple of 64
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w + static_cast<int64_t>(co0) * kvals, wbytes);
+    const int pairs = p.pw / 2;
+    const int64_t img_bytes = static_cast<int64_t>(p.H) * p.W * CIN * 2;
+    const __amdgpu_buffer_rsrc_t xr =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(p.x) + img * img_bytes, static_cast<uint32_t>(img_bytes));
+    const float inv_pairs = 1.0f / static_cast<float>(pairs);
+    int pr = small_div(tid, inv_pairs), cp = tid - pr * pairs;
+    const int dpr = small_div(kScThreads, inv_pairs), dcp = kScThreads - dpr * pairs;
+    for (int c0 = tid; c0 < wchunks || pr < prows0; c0 += 2 * kScThreads) {
+        uint64_t wv[2][2];
+        uint32_t wsh[2][2];
+        int wdst[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = c0 + k * kScThreads;
             const int co = small_div(c, inv_co), rem = c - co * per_co;
             const int r = small_div(rem, inv_kp2), tp = rem - r * kp2;
-            uint32_t v[2][CIN];
+            wdst[k] = c < wchunks ? co * wstride + (r * p.kwp + 2 * tp) * 8 : -1;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int s = 2 * tp + h - p.toff;
-                const bool ok = s >= 0 && s < p.KW;
-                const uint32_t base = static_cast<uint32_t>(((co * p.KH + r) * p.KW + s) * CIN * 2);
-#pragma unroll
-                for (int ci = 0; ci < CIN; ++ci)
-                    v[h][ci] = __builtin_amdgcn_raw_buffer_load_b16(wr, ok ? base + 2 * ci : kOutOfRange, 0, 0);
+                const bool ok = c < wchunks && s >= 0 && s < p.KW;
+                const uint32_t off = static_cast<uint32_t>(((co * p.KH + r) * p.KW + s) * CIN * 2);
+                const uint32_t base = min(off & ~3u, wbytes - 8u);
+                wsh[k][h] = (off - base) * 8u;
+                const auto d = __builtin_amdgcn_raw_buffer_load_b64(wr, ok ? base : kOutOfRange, 0, 0);
+                wv[k][h] = static_cast<uint64_t>(d[0]) | (static_cast<uint64_t>(d[1]) << 32);
             }
-            uint32_t o[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int ci = 0; ci < CIN; ++ci) o[2 * h + (ci >> 1)] |= v[h][ci] << (16 * (ci & 1));
-            *reinterpret_cast<u32x4_t*>(sw + co * wstride + (r * p.kwp + 2 * tp) * 8) = u32x4_t{o[0], o[1], o[2], o[3]};
         }
+        uint32_t d[4][CIN];
+        int dst[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool live = pr < prows0;
+            const int hi = hi0 + pr, w = 2 * cp - p.pwl;
+            const bool in = live && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                            static_cast<unsigned>(w) < static_cast<unsigned>(p.W);
+            load_dwords<CIN>(xr, in ? static_cast<uint32_t>((hi * p.W + w) * CIN * 2) : kOutOfRange, d[u]);
+            dst[u] = live ? (pr * p.pw + 2 * cp) * 8 : -1;
+            cp += dcp;
+            pr += dpr;
+            if (cp >= pairs) {
+                cp -= pairs;
+                ++pr;
+            }
+        }
+        constexpr uint64_t kMask = CIN == 4 ? ~uint64_t(0) : (uint64_t(1) << (16 * CIN)) - 1;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (wdst[k] < 0) continue;
+            const uint64_t t0 = (wv[k][0] >> wsh[k][0]) & kMask, t1 = (wv[k][1] >> wsh[k][1]) & kMask;
+            *reinterpret_cast<u32x4_t*>(sw + wdst[k]) = u32x4_t{static_cast<uint32_t>(t0), static_cast<uint32_t>(t0 >> 32),
+                                                                static_cast<uint32_t>(t1), static_cast<uint32_t>(t1 >> 32)};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (dst[u] >= 0) *reinterpret_cast<u32x4_t*>(sx + dst[u]) = widen_pair<CIN>(d[u]);
     }
-    // patch: pair (pr, cp) is patch columns 2 cp, 2 cp + 1 = image columns 2 cp - pwl (even)
-    // and the next one, of image row hi0 + pr.  Four pairs a thread per pass, their loads
-    // in flight together; the pair index steps by kScThreads without a division.
-    {
-        const int pairs = p.pw / 2;
-        const int64_t img_bytes = static_cast<int64_t>(p.H) * p.W * CIN * 2;
-        const __amdgpu_buffer_rsrc_t xr =
-            buffer_rsrc(reinterpret_cast<const uint8_t*>(p.x) + img * img_bytes, static_cast<uint32_t>(img_bytes));
-        const float inv_pairs = 1.0f / static_cast<float>(pairs);
-        int pr = small_div(tid, inv_pairs), cp = tid - pr * pairs;
-        const int dpr = small_div(kScThreads, inv_pairs), dcp = kScThreads - dpr * pairs;
-        while (pr < prows) {
-            uint32_t d[4][CIN];
-            int dst[4];
-            bool live[4];
+}
+
+// Patch rows pr_begin .. pr_end-1 (image rows hi0 + pr) into their LDS layout, by threads
+// t = 0 .. nthr-1.  Pair (pr, cp) is patch columns 2 cp, 2 cp + 1 = image columns
+// 2 cp - pwl (even) and the next one.  Four pairs a thread per pass, their loads in flight
+// together; the pair index steps by nthr without a division.
+template <int CIN>
+__device__ void smallc_fill_patch(const SmallCArgs& p, uint8_t* sx, int img, int hi0, int pr_begin, int pr_end,
+                                  int t, int nthr) {
+    const int pairs = p.pw / 2;
+    const int64_t img_bytes = static_cast<int64_t>(p.H) * p.W * CIN * 2;
+    const __amdgpu_buffer_rsrc_t xr =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(p.x) + img * img_bytes, static_cast<uint32_t>(img_bytes));
+    const float inv_pairs = 1.0f / static_cast<float>(pairs);
+    int pr = small_div(t, inv_pairs), cp = t - pr * pairs;
+    pr += pr_begin;
+    const int dpr = small_div(nthr, inv_pairs), dcp = nthr - dpr * pairs;
+    while (pr < pr_end) {
+        uint32_t d[4][CIN];
+        int dst[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                live[u] = pr < prows;
-                const int hi = hi0 + pr, w = 2 * cp - p.pwl;
-                const bool in = live[u] && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
-                                static_cast<unsigned>(w) < static_cast<unsigned>(p.W);
-                load_dwords<CIN>(xr, in ? static_cast<uint32_t>((hi * p.W + w) * CIN * 2) : kOutOfRange, d[u]);
-                dst[u] = (pr * p.pw + 2 * cp) * 8;
-                cp += dcp;
-                pr += dpr;
-                if (cp >= pairs) {
-                    cp -= pairs;
-                    ++pr;
-                }
+        for (int u = 0; u < 4; ++u) {
+            const bool live = pr < pr_end;
+            const int hi = hi0 + pr, w = 2 * cp - p.pwl;
+            const bool in = live && static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
+                            static_cast<unsigned>(w) < static_cast<unsigned>(p.W);
+            load_dwords<CIN>(xr, in ? static_cast<uint32_t>((hi * p.W + w) * CIN * 2) : kOutOfRange, d[u]);
+            dst[u] = live ? (pr * p.pw + 2 * cp) * 8 : -1;
+            cp += dcp;
+            pr += dpr;
+            if (cp >= pairs) {
+                cp -= pairs;
+                ++pr;
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (live[u]) *reinterpret_cast<u32x4_t*>(sx + dst[u]) = widen_pair<CIN>(d[u]);
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (dst[u] >= 0) *reinterpret_cast<u32x4_t*>(sx + dst[u]) = widen_pair<CIN>(d[u]);
+    }
+}
+
+__device__ __forceinline__ void smallc_fill_patch_any(const SmallCArgs& p, uint8_t* sx, int img, int hi0,
+                                                      int pr_begin, int pr_end, int t, int nthr) {
+    switch (p.Cin) {
+        case 1: smallc_fill_patch<1>(p, sx, img, hi0, pr_begin, pr_end, t, nthr); break;
+        case 2: smallc_fill_patch<2>(p, sx, img, hi0, pr_begin, pr_end, t, nthr); break;
+        case 3: smallc_fill_patch<3>(p, sx, img, hi0, pr_begin, pr_end, t, nthr); break;
+        default: smallc_fill_patch<4>(p, sx, img, hi0, pr_begin, pr_end, t, nthr); break;
     }
 }
 
@@ -177,25 +246,27 @@ __global__ __launch_bounds__(kScThreads, 1) void conv_smallc_kernel(const SmallC
     uint8_t* const sw = smem + kScStage + kScBias;
     uint8_t* const sx = sw + 64 * wstride;
 
-    // ---- fill: biases, weights, patch ----
-    if (tid < 16) {
-        f32x4_t b = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.bias && 4 * tid < nco) b = *reinterpret_cast<const f32x4_t*>(p.bias + co0 + 4 * tid);
-        *reinterpret_cast<f32x4_t*>(sbias + 4 * tid) = b;
-    }
-    const int hi0 = ho0 * p.SH - p.PH;
-    const int prows = (rows - 1) * p.SH + p.KH;
-    switch (p.Cin) {
-        case 1: smallc_fill<1>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
-        case 2: smallc_fill<2>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
-        case 3: smallc_fill<3>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
-        default: smallc_fill<4>(p, sw, sx, wstride, img, co0, nco, hi0, prows, tid); break;
-    }
-    lds_barrier();
-
+    // ---- fill: biases, weights, the first round's patch rows.  The bias load goes out first
+    //      and lands in LDS after the fill, so that its latency hides behind the fill's. ----
+    f32x4_t bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (tid < 16 && p.bias && 4 * tid < nco) bias4 = *reinterpret_cast<const f32x4_t*>(p.bias + co0 + 4 * tid);
     const int npx = rows * p.Wo;                            // the tile's pixels: whole output rows,
     const int nfrag = (npx + 31) / 32;                      // contiguous in y
     const int nrounds = (nfrag + kScRound - 1) / kScRound;
+    // patch rows: the first round's fragments read rows 0 .. prows0-1, filled now; the store
+    // waves fill the rest during the first round, in which they have nothing to store
+    const int hi0 = ho0 * p.SH - p.PH;
+    const int prows = (rows - 1) * p.SH + p.KH;
+    const int prows0 = min(prows, ((min(npx, kScRound * 32) - 1) / p.Wo) * p.SH + p.KH);
+    switch (p.Cin) {
+        case 1: smallc_fill<1>(p, sw, sx, wstride, img, co0, nco, hi0, prows0, tid); break;
+        case 2: smallc_fill<2>(p, sw, sx, wstride, img, co0, nco, hi0, prows0, tid); break;
+        case 3: smallc_fill<3>(p, sw, sx, wstride, img, co0, nco, hi0, prows0, tid); break;
+        default: smallc_fill<4>(p, sw, sx, wstride, img, co0, nco, hi0, prows0, tid); break;
+    }
+    if (tid < 16) *reinterpret_cast<f32x4_t*>(sbias + 4 * tid) = bias4;
+    lds_barrier();   // weights, biases and the first round's patch rows are in place
+
     const int64_t pix0 = (static_cast<int64_t>(img) * p.Ho + ho0) * p.Wo;
     const int cpr = nco / 8;                                // 16-byte chunks of a pixel's channels
 
@@ -203,7 +274,7 @@ __global__ __launch_bounds__(kScThreads, 1) void conv_smallc_kernel(const SmallC
         // ---- compute waves: fragments f0 and f0 + 8 of each round, four accumulator chains
         //      (2 fragments x 2 channel halves) interleaved on the matrix pipe ----
         const int ksteps = p.kwp / 4;                       // 1 .. 4
-        const int nj = nco / 32;
+        const int nj = nco / 32;                            // channel halves staged
         const uint8_t* const bbase = sw + (lane & 31) * wstride + 2 * half * 8;
         const int bstep_j = 32 * wstride;
         const int m = lane & 31, swz = (m >> 1) & 7;
@@ -224,38 +295,51 @@ __global__ __launch_bounds__(kScThreads, 1) void conv_smallc_kernel(const SmallC
                     const int hl = small_div(pl[u], inv_wo), wo = pl[u] - hl * p.Wo;
                     abase[u] = sx + ((hl * p.SH) * p.pw + wo * p.SW + 2 * half) * 8;
                 }
+                // the accumulators start at the bias: the epilogue then reads nothing from LDS
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(sbias + 32 * j + 8 * g + 4 * half);
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[u][j][e] = 0.0f;
-                for (int r = 0; r < p.KH; ++r) {
+                        for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        if (ks >= ksteps) break;
-                        bf16x8_t av[2];
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const uint8_t* const a = abase[u] + (r * p.pw + 4 * ks) * 8;
-                            if constexpr (A16) {
-                                av[u] = *reinterpret_cast<const bf16x8_t*>(a);
-                            } else {
-                                const uint2 a0 = *reinterpret_cast<const uint2*>(a);
-                                const uint2 a1 = *reinterpret_cast<const uint2*>(a + 8);
-                                av[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
-                            }
-                        }
-                        const uint8_t* const b = bbase + (r * p.kwp + 4 * ks) * 8;
-                        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(b);
-                        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[0], acc[0][0], 0, 0, 0);
-                        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[1], acc[1][0], 0, 0, 0);
-                        if (nj > 1) {
-                            const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b + bstep_j);
-                            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[0], acc[0][1], 0, 0, 0);
-                            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[1], acc[1][1], 0, 0, 0);
-                        }
+                            for (int e = 0; e < 4; ++e) acc[u][j][4 * g + e] = bv[e];
                     }
+                // k-step i reads kernel row i / ksteps, taps 4 (i % ksteps) .. +3: 32 bytes on
+                // within a row, to the next row's start after its last step.  The next step's
+                // operands are read before this step's four MFMAs.  Both channel halves are
+                // computed; with 32 channels the second is never staged.
+                const int nk = p.KH * ksteps;
+                const int a_row = (p.pw - 4 * (ksteps - 1)) * 8, b_row = (p.kwp - 4 * (ksteps - 1)) * 8;
+                const uint8_t* pa0 = abase[0];
+                const uint8_t* pa1 = abase[1];
+                const uint8_t* pb = bbase;
+                bf16x8_t a0 = read_a<A16>(pa0), a1 = read_a<A16>(pa1);
+                bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(pb), b1 = *reinterpret_cast<const bf16x8_t*>(pb + bstep_j);
+                int ks = 0;
+                for (int i = 0; i < nk; ++i) {
+                    bf16x8_t na0 = a0, na1 = a1, nb0 = b0, nb1 = b1;
+                    if (i + 1 < nk) {
+                        const bool row_end = ++ks == ksteps;
+                        if (row_end) ks = 0;
+                        const int da = row_end ? a_row : 32, db = row_end ? b_row : 32;
+                        pa0 += da;
+                        pa1 += da;
+                        pb += db;
+                        na0 = read_a<A16>(pa0);
+                        na1 = read_a<A16>(pa1);
+                        nb0 = *reinterpret_cast<const bf16x8_t*>(pb);
+                        nb1 = *reinterpret_cast<const bf16x8_t*>(pb + bstep_j);
+                    }
+                    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, a0, acc[0][0], 0, 0, 0);
+                    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, a1, acc[1][0], 0, 0, 0);
+                    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, a0, acc[0][1], 0, 0, 0);
+                    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, a1, acc[1][1], 0, 0, 0);
+                    a0 = na0;
+                    a1 = na1;
+                    b0 = nb0;
+                    b1 = nb1;
                 }
             }
             lds_barrier();   // B1: the store waves hold the previous round's fragments
@@ -273,10 +357,9 @@ __global__ __launch_bounds__(kScThreads, 1) void conv_smallc_kernel(const SmallC
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
                             const int col = 32 * j + 8 * g + 4 * half;
-                            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(sbias + col);
                             float v[4];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] = acc[u][j][4 * g + e] + bv[e];
+                            for (int e = 0; e < 4; ++e) v[e] = acc[u][j][4 * g + e];
                             if constexpr (RES) {
                                 if (pv[u]) {
                                     const uint2 rv = *reinterpret_cast<const uint2*>(
@@ -332,6 +415,7 @@ __global__ __launch_bounds__(kScThreads, 1) void conv_smallc_kernel(const SmallC
                 }
             }
         };
+        smallc_fill_patch_any(p, sx, img, hi0, prows0, prows, tid - kScCompute * 64, kScThreads - kScCompute * 64);
         for (int rd = 0; rd < nrounds; ++rd) {
             if (rd > 0) store_round(rd - 1);
             lds_barrier();   // B1

@@ -72,11 +72,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-// ReLU of two packed bf16 values: a value with the sign bit set becomes +0.  Rounding
-// to nearest keeps the sign, so ReLU after the rounding equals the rounding of ReLU.
+// ReLU of two packed bf16 values: a value with the sign bit set becomes +0 (as a signed
+// 16-bit integer it is negative, so one packed integer max with 0 does both halves).
+// Rounding to nearest keeps the sign, so ReLU after the rounding equals the rounding of ReLU.
 __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t u) {
     const i16x2_t s = __builtin_bit_cast(i16x2_t, u);
-    return __builtin_bit_cast(uint32_t, s & ~(s >> 15));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(s, i16x2_t{0, 0}));
 }
 
 // SiLU, v / (1 + e^-v), with the hardware exp2 and reciprocal.
