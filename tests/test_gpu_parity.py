@@ -237,13 +237,22 @@ def test_bf16_conv_any_cin_every_tile(i):
 # Up to four input channels with whole 16-byte input rows: the small-channel kernel (weights
 # and the input patch re-laid in LDS with 4-channel pixels) by default, the value-by-value
 # implicit GEMM on the forced generic route.  Ragged row tiles, a half channel block
-# (Cout % 64 = 32), residuals, one and two channels, a tall image with many row tiles.
+# (Cout % 64 = 32), residuals, one and two channels, a tall image with many row tiles, and
+# workgroups that run several rounds of compute and store waves.
 SMALLC_BF16 = [
     dict(n=2, h=24, w=16, cin=3, cout=64, kh=7, kw=7, stride=2, pad=3, act="relu", residual=False),
     dict(n=3, h=10, w=8, cin=4, cout=96, kh=3, kw=3, stride=1, pad=1, act="gelu_erf", residual=True),
     dict(n=1, h=9, w=16, cin=2, cout=32, kh=5, kw=5, stride=2, pad=2, act="none", residual=True),
     dict(n=2, h=40, w=40, cin=1, cout=64, kh=3, kw=3, stride=1, pad=0, act="gelu_tanh", residual=False),
     dict(n=1, h=200, w=64, cin=3, cout=128, kh=7, kw=7, stride=2, pad=3, act="relu", residual=False),
+    # several rounds of 16 fragments per workgroup (the shapes above plan one output row per
+    # workgroup): two rounds with a residual at stride 1 (odd left padding, 8-byte patch
+    # reads); two rounds with a 32-channel block at stride 2; five rounds with a shorter last
+    # row tile; a 32-channel layer of two rounds
+    dict(n=64, h=64, w=64, cin=3, cout=64, kh=3, kw=3, stride=1, pad=1, act="relu", residual=True),
+    dict(n=64, h=64, w=72, cin=4, cout=96, kh=5, kw=5, stride=2, pad=2, act="gelu_tanh", residual=False),
+    dict(n=64, h=96, w=96, cin=1, cout=64, kh=3, kw=3, stride=1, pad=0, act="gelu_erf", residual=True),
+    dict(n=64, h=64, w=64, cin=2, cout=32, kh=3, kw=3, stride=1, pad=1, act="none", residual=False),
 ]
 
 
