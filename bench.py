@@ -355,11 +355,11 @@ def cpu_baseline(inp, budget_s: float):
             sub["residual"] = inp["residual"][:imgs]
         sub["workload"] = dataclasses.replace(wl, n=imgs)
         # the whole workload can take well under the budget: then repeat it until the budget is
-        # spent (at most 50 passes), so that the figure is not one short, noisy pass
+        # spent (at most 500 passes), so that the figure is not one short, noisy pass
         t0 = time.perf_counter()
         oracle.conv_bn_act(sub)
         first = time.perf_counter() - t0
-        passes = 1 + int(max(0, min(49, (budget_s - t1 - first) / max(first, 1e-6))))
+        passes = 1 + int(max(0, min(499, (budget_s - t1 - first) / max(first, 1e-6))))
         for _ in range(passes - 1):
             oracle.conv_bn_act(sub)
         total_s = time.perf_counter() - t0
