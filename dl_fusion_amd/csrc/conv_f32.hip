@@ -8,7 +8,7 @@
 // conv_f32_regw_kernel (K <= 256, Cin a multiple of 4): one pass, 32 x PPB lanes.  The workgroup
 // copies its 32 channels' K weights into LDS once (16-byte loads of one contiguous block) while
 // it gathers the receptive fields of its pixels (one 16-byte load per tap and 4 channels, zero
-// outside the image); after one barrier a lane reads 4 weights of its channel and 4 input values
+// outside the image), every load of both issued before the first LDS store; after one barrier a lane reads 4 weights of its channel and 4 input values
 // of its pixel per pair of LDS reads (the lanes of a pixel read the same input address) for 4
 // FMAs.
 //
@@ -95,20 +95,27 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
     const int k4n = p.K >> 2;
     // the workgroup's weight rows c0 .. c0 + 31 are one block of 32 K values (K % 4 == 0, w 16-byte
     // aligned); rows past Cout are left unread and their results never stored
+    // Every global load of both copies is issued before the first LDS store, so the staging costs
+    // one memory round trip instead of one per loop trip.
     const int rows = min(TC, p.Cout - c0);
     const f32x4_t* const wblk = reinterpret_cast<const f32x4_t*>(p.w + static_cast<int64_t>(c0) * p.K);
-    for (int e = tid; e < rows * k4n; e += NT) {
-        const int r = e / k4n, q = e - r * k4n;
-        ws[r * (WS / 4) + q] = wblk[e];
+    constexpr int WIT = (TC * K4 + NT - 1) / NT, XIT = (PPB * K4 + NT - 1) / NT;
+    f32x4_t wstage[WIT], xstage[XIT];
+#pragma unroll
+    for (int i = 0; i < WIT; ++i) {
+        const int e = tid + i * NT;
+        if (e < rows * k4n) wstage[i] = wblk[e];
     }
     // receptive fields of the workgroup's pixels: item e = (pixel, 4 consecutive k), one tap each
     const int hw = p.Ho * p.Wo;
     const int c4 = p.Cin >> 2;
-    for (int e = tid; e < PPB * k4n; e += NT) {
+#pragma unroll
+    for (int i = 0; i < XIT; ++i) {
+        const int e = tid + i * NT;
+        xstage[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         const int q = e / k4n, kk4 = e - q * k4n;
         const int m = m0 + q;
-        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (m < p.M) {
+        if (e < PPB * k4n && m < p.M) {
             const int img = m / hw, rem = m - img * hw;
             const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
             const int tap = kk4 / c4, ci = (kk4 - tap * c4) * 4;
@@ -116,9 +123,25 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
             const int hi = ho * p.SH - p.PH + r, wi = wo * p.SW - p.PW + sx;
             if (static_cast<unsigned>(hi) < static_cast<unsigned>(p.H) &&
                 static_cast<unsigned>(wi) < static_cast<unsigned>(p.W))
-                v = *reinterpret_cast<const f32x4_t*>(p.x + ((static_cast<int64_t>(img) * p.H + hi) * p.W + wi) * p.Cin + ci);
+                xstage[i] = *reinterpret_cast<const f32x4_t*>(
+                    p.x + ((static_cast<int64_t>(img) * p.H + hi) * p.W + wi) * p.Cin + ci);
         }
-        xs[q][kk4] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < WIT; ++i) {
+        const int e = tid + i * NT;
+        if (e < rows * k4n) {
+            const int r = e / k4n, q = e - r * k4n;
+            ws[r * (WS / 4) + q] = wstage[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < XIT; ++i) {
+        const int e = tid + i * NT;
+        if (e < PPB * k4n) {
+            const int q = e / k4n, kk4 = e - q * k4n;
+            xs[q][kk4] = xstage[i];
+        }
     }
     __syncthreads();
     const int m = m0 + pl;
@@ -162,9 +185,10 @@ hipError_t launch_regw_ppb(const ConvF32Args& a, int act, hipStream_t s) {
 }
 
 // The weights are staged once per workgroup, so larger pixel blocks cut the weight traffic: 16
-// pixels a workgroup measured best on a 1x32x32 16->32 layer (64 workgroups, 4.45 us a launch in
-// a graph, against 4.7 us with 8, 5.1 us with 4 and 5.4 us with 32).  Smaller blocks only where
-// 16 would leave fewer than 64 workgroups.
+// pixels a workgroup measured best on a 1x32x32 16->32 layer (64 workgroups, 4.29 us a launch in
+// a graph, against 5.2 us with 8; before the staging loads were all issued up front, 4.45 us with
+// 16, 4.7 us with 8, 5.1 us with 4 and 5.4 us with 32).  Smaller blocks only where 16 would leave
+// fewer than 64 workgroups.
 template <int KMAX>
 hipError_t launch_regw(const ConvF32Args& a, int act, hipStream_t s) {
     const int64_t cb = (a.Cout + 31) / 32;
