@@ -10,7 +10,7 @@
 // it gathers the receptive fields of its pixels (one 16-byte load per tap and 4 channels, zero
 // outside the image), every load of both issued before the first LDS store; after one barrier a lane reads 4 weights of its channel and 4 input values
 // of its pixel per pair of LDS reads (the lanes of a pixel read the same input address) for 4
-// FMAs.
+// FMAs, sixteen pairs of reads in flight at a time (the rows are zero-padded to whole groups).
 //
 // conv_f32_kernel (any other shape): weights staged in LDS transposed to [k][channel] in
 // slices of 4096 values, together with the im2col rows of its pixels, each gathered by
@@ -143,20 +143,41 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
             xs[q][kk4] = xstage[i];
         }
     }
+    // zeros past K in every weight and pixel row: the contraction below then runs whole groups
+    // of chunks, with one guard per group instead of one per chunk
+    const int kt4 = K4 - k4n;
+    for (int e = tid; e < (TC + PPB) * kt4; e += NT) {
+        const int r = e / kt4, q = k4n + (e - r * kt4);
+        if (r < TC)
+            ws[r * (WS / 4) + q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        else
+            xs[r - TC][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     __syncthreads();
     const int m = m0 + pl;
     if (m >= p.M || co >= p.Cout) return;
     const f32x4_t* const wrow = ws + co_l * (WS / 4);
     float acc0 = 0.0f, acc1 = 0.0f;    // two chains: even and odd k
+    // groups of 16 chunks, each its own basic block: a group's 32 LDS reads go out together, then
+    // its 64 FMAs.  With a guard per chunk every pair of reads waited out its own LDS round trip;
+    // with no guard at all the compiler kept the whole row's reads in registers and spilled.
+    constexpr int GQ = 16;
 #pragma unroll
-    for (int q = 0; q < K4; ++q) {
-        if (q < k4n) {
-            const f32x4_t xv = xs[pl][q];
-            const f32x4_t wv = wrow[q];
-            acc0 = fmaf(xv[0], wv[0], acc0);
-            acc1 = fmaf(xv[1], wv[1], acc1);
-            acc0 = fmaf(xv[2], wv[2], acc0);
-            acc1 = fmaf(xv[3], wv[3], acc1);
+    for (int q0 = 0; q0 < K4; q0 += GQ) {
+        if (q0 < k4n) {
+            f32x4_t xq[GQ], wq[GQ];
+#pragma unroll
+            for (int u = 0; u < GQ && q0 + u < K4; ++u) {
+                xq[u] = xs[pl][q0 + u];
+                wq[u] = wrow[q0 + u];
+            }
+#pragma unroll
+            for (int u = 0; u < GQ && q0 + u < K4; ++u) {
+                acc0 = fmaf(xq[u][0], wq[u][0], acc0);
+                acc1 = fmaf(xq[u][1], wq[u][1], acc1);
+                acc0 = fmaf(xq[u][2], wq[u][2], acc0);
+                acc1 = fmaf(xq[u][3], wq[u][3], acc1);
+            }
         }
     }
     const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
@@ -185,9 +206,10 @@ hipError_t launch_regw_ppb(const ConvF32Args& a, int act, hipStream_t s) {
 }
 
 // The weights are staged once per workgroup, so larger pixel blocks cut the weight traffic: 16
-// pixels a workgroup measured best on a 1x32x32 16->32 layer (64 workgroups, 4.29 us a launch in
-// a graph, against 5.2 us with 8; before the staging loads were all issued up front, 4.45 us with
-// 16, 4.7 us with 8, 5.1 us with 4 and 5.4 us with 32).  Smaller blocks only where 16 would leave
+// pixels a workgroup measured best on a 1x32x32 16->32 layer (64 workgroups, 4.0 us a launch in
+// a graph; 4.29 us against 5.2 us with 8 before the contraction read its operands in groups; before
+// the staging loads were all issued up front, 4.45 us with 16, 4.7 us with 8, 5.1 us with 4 and
+// 5.4 us with 32).  Smaller blocks only where 16 would leave
 // fewer than 64 workgroups.
 template <int KMAX>
 hipError_t launch_regw(const ConvF32Args& a, int act, hipStream_t s) {
