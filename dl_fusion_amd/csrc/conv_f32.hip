@@ -93,10 +93,10 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
     const int c0 = static_cast<int>(blockIdx.y) * TC;
     const int co = c0 + co_l;
     const int k4n = p.K >> 2;
-    // the workgroup's weight rows c0 .. c0 + 31 are one block of 32 K values (K % 4 == 0, w 16-byte
-    // aligned); rows past Cout are left unread and their results never stored
-    // Every global load of both copies is issued before the first LDS store, so the staging costs
-    // one memory round trip instead of one per loop trip.
+    // Every global load of both copies below is issued before the first LDS store, so the staging
+    // costs one memory round trip instead of one per loop trip.  The workgroup's weight rows
+    // c0 .. c0 + 31 are one block of 32 K values (K % 4 == 0, w 16-byte aligned); rows past Cout
+    // are left unread and their results never stored.
     const int rows = min(TC, p.Cout - c0);
     const f32x4_t* const wblk = reinterpret_cast<const f32x4_t*>(p.w + static_cast<int64_t>(c0) * p.K);
     constexpr int WIT = (TC * K4 + NT - 1) / NT, XIT = (PPB * K4 + NT - 1) / NT;
