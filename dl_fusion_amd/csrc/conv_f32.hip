@@ -37,6 +37,12 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
     const int co = c0 + co_l;
     const int hw = p.Ho * p.Wo;
 
+    // the epilogue's bias and residual are loaded before the K loop, not after it
+    const int m = m0 + pl;
+    const bool live = m < p.M && co < p.Cout;
+    const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
+    const float bco = p.bias && co < p.Cout ? p.bias[co] : 0.0f;
+    const float rv = p.res && live ? p.res[idx] : 0.0f;
     float acc = 0.0f;
     for (int k0 = 0; k0 < p.K; k0 += KS) {
         // weights slice -> ws[k][channel]; consecutive lanes read consecutive k
@@ -48,10 +54,10 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
         // im2col rows of this workgroup's pixels -> xs[pixel][k]; every load is independent
         for (int e = tid; e < PPB * KS; e += 256) {
             const int q = e / KS, kk = e - q * KS;
-            const int m = m0 + q, gk = k0 + kk;
+            const int mq = m0 + q, gk = k0 + kk;
             float v = 0.0f;
-            if (m < p.M && gk < p.K) {
-                const int img = m / hw, rem = m - img * hw;
+            if (mq < p.M && gk < p.K) {
+                const int img = mq / hw, rem = mq - img * hw;
                 const int ho = rem / p.Wo, wo = rem - ho * p.Wo;
                 const int tap = gk / p.Cin, ci = gk - tap * p.Cin;
                 const int r = tap / p.KW, s = tap - r * p.KW;
@@ -69,11 +75,9 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(const ConvF32Args p) {
         __syncthreads();
     }
 
-    const int m = m0 + pl;
-    if (m >= p.M || co >= p.Cout) return;
-    const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
-    float v = acc + (p.bias ? p.bias[co] : 0.0f);
-    if (p.res) v += p.res[idx];
+    if (!live) return;
+    float v = acc + bco;
+    if (p.res) v += rv;
     p.y[idx] = activate<ACT>(v);
 }
 
@@ -127,6 +131,13 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
                     p.x + ((static_cast<int64_t>(img) * p.H + hi) * p.W + wi) * p.Cin + ci);
         }
     }
+    // the epilogue's bias and residual go out with the staging loads: loaded after the
+    // contraction, they would add a memory round trip to the end of the kernel
+    const int m = m0 + pl;
+    const bool live = m < p.M && co < p.Cout;
+    const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
+    const float bco = p.bias && co < p.Cout ? p.bias[co] : 0.0f;
+    const float rv = p.res && live ? p.res[idx] : 0.0f;
 #pragma unroll
     for (int i = 0; i < WIT; ++i) {
         const int e = tid + i * NT;
@@ -154,8 +165,7 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
             xs[r - TC][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     __syncthreads();
-    const int m = m0 + pl;
-    if (m >= p.M || co >= p.Cout) return;
+    if (!live) return;
     const f32x4_t* const wrow = ws + co_l * (WS / 4);
     float acc0 = 0.0f, acc1 = 0.0f;    // two chains: even and odd k
     // groups of 16 chunks, each its own basic block: a group's 32 LDS reads go out together, then
@@ -180,9 +190,8 @@ __global__ __launch_bounds__(32 * PPB) void conv_f32_regw_kernel(const ConvF32Ar
             }
         }
     }
-    const int64_t idx = static_cast<int64_t>(m) * p.Cout + co;
-    float v = (acc0 + acc1) + (p.bias ? p.bias[co] : 0.0f);
-    if (p.res) v += p.res[idx];
+    float v = (acc0 + acc1) + bco;
+    if (p.res) v += rv;
     p.y[idx] = activate<ACT>(v);
 }
 
