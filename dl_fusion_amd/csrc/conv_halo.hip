@@ -679,6 +679,20 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
         for (int e = 0; e < 4; ++e) biasv[4 * g + e] = b4[e];
     }
 
+    // the residual of this wave's outputs, loaded before anything else: the oldest loads, they
+    // are complete by the prologue's wait for the first slices (loads return in issue order), so
+    // none of the waits below counts them, and their latency hides behind the halo's
+    uint2 rv[2][4];
+    if (kh == 0 && p.res) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pix = (2 * pg + i) * 32 + (lane & 31);
+            const int64_t e0 = (static_cast<int64_t>(img) * HW + (pix < HW ? pix : 0)) * p.Cout + c0 + 4 * half;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) rv[i][g] = *reinterpret_cast<const uint2*>(p.res + e0 + 8 * g);
+        }
+    }
+
     // ---- prologue: groups 0 and 1, weight slices 0 .. kIS-2; slices 0 .. kILook visible ----
     load_group(0);
     if (Q > 1) load_group(1);
@@ -767,18 +781,6 @@ __global__ __launch_bounds__(512, 1) void conv_halo_img_kernel(const HaloArgs p)
         });
     }
     wait_vmcnt<0>();
-
-    // the residual of this wave's outputs is fetched before the two k halves meet
-    uint2 rv[2][4];
-    if (kh == 0 && p.res) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int pix = (2 * pg + i) * 32 + (lane & 31);
-            const int64_t e0 = (static_cast<int64_t>(img) * HW + (pix < HW ? pix : 0)) * p.Cout + c0 + 4 * half;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) rv[i][g] = *reinterpret_cast<const uint2*>(p.res + e0 + 8 * g);
-        }
-    }
 
     // ---- the two k halves meet: waves 4-7 hand their partial sums to waves 0-3 through LDS ----
     barrier();   // every wave is done with the halo buffers
